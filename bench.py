@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Decode-step throughput of the TokenSelect hot path on one MI355X.
+
+Headline workload: one request at N = 1,048,576 cached tokens, Llama-3-8B layer
+shapes (32 query / 8 KV heads, d = 128), bf16 paged pool (page 16, shuffled),
+TopK 2048 united with 512 local tokens, 32 independent layers (seeds 2000 + l).
+A step is one full decode step of one layer through tokenselect_decode_step:
+cache check, paged scoring, per-head softmax, soft vote, radix TopK, sparse
+attention. Every timed step reselects (theta = 2 forces a cache miss), and the
+steps cycle through the 32 layers, so each step streams a different 2 GiB K pool.
+
+Prints one JSON line: decode steps/s (value), the scoring kernel's achieved HBM
+bandwidth against the 8 TB/s peak (roofline), the same metric at N = 131072
+(secondary), and the fp64 oracle timed on host cores (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def score_bytes_per_token(geo) -> float:
+    """Algorithmic bytes the scoring kernel moves per cached token.
+
+    K rows of every KV head (H_kv * d * element size), the fp32 logits of every
+    query head (H * 4) and the block-table entry shared by a page (4 / P).
+    """
+    esize = 4 if geo.dtype == "f32" else 2
+    return geo.num_kv_heads * geo.head_dim * esize + geo.num_q_heads * 4 + 4.0 / geo.page_size
+
+
+class Layer:
+    """Device buffers of one layer's request: paged pool, query, cache state."""
+
+    def __init__(self, geo, layer, dev, keep_host=False):
+        import torch
+        import token_level_sparse_amd as ts
+        from synth import workloads as wl
+        b = wl.make_batch(geo, device=dev, layer=layer)
+        self.q, self.k_pool, self.v_pool = b.q, b.k_pool, b.v_pool
+        self.block_table, self.seq_lens = b.block_table, b.seq_lens
+        self.total = b.total_tokens
+        self.host = None
+        if keep_host:
+            r = b.requests[0]
+            self.host = tuple(x.float().cpu().numpy() for x in (r.q, r.k, r.v))
+        del b
+        H, d = geo.num_q_heads, geo.head_dim
+        self.cache = ts.CacheState.allocate(1, H, d, geo.top_k, geo.torch_dtype, dev)
+        self.hit = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.out = torch.empty(1, H, d, dtype=geo.torch_dtype, device=dev)
+
+
+def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False):
+    import torch
+    import token_level_sparse_amd as ts
+    t0 = time.time()
+    layers = [Layer(geo, l, dev, keep_host and l == 0) for l in range(n_layers)]
+    torch.cuda.synchronize()
+    log(f"[{geo.name}] generated {n_layers} layers in {time.time() - t0:.1f}s")
+    L0 = layers[0]
+    shape = ts.make_shape(geo.num_q_heads, geo.num_kv_heads, 1, L0.block_table.shape[1], L0.total,
+                          geo.torch_dtype)
+    # theta = 2 > any cosine: every step reselects (a full miss step)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, 2.0)
+    ws = ts.alloc_workspace(shape, sel, dev)
+
+    def step(s):
+        L = layers[s % n_layers]
+        ts.decode_step(shape, sel, L.q, L.k_pool, L.v_pool, L.block_table, L.seq_lens, L.cache,
+                       L.hit, L.out, ws)
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for s in range(steps):
+        step(s)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / steps
+    log(f"[{geo.name}] decode step {ms_step:.4f} ms (wall {wall / steps * 1e3:.4f} ms)")
+
+    # the scoring launch alone (tokenselect_score: the scoring kernel plus the small
+    # kernel folding per-unit softmax pairs), timed per launch on the same stream
+    H = geo.num_q_heads
+    logits = torch.empty(H * L0.total, dtype=torch.float32, device=dev)
+    stats = torch.empty(H * 2, dtype=torch.float32, device=dev)
+    for s in range(min(warmup, 4)):
+        L = layers[s % n_layers]
+        ts.score(shape, sel, L.q, L.k_pool, L.block_table, L.seq_lens, logits, stats, ws)
+    torch.cuda.synchronize()
+    evs = []
+    for s in range(steps):
+        L = layers[s % n_layers]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ts.score(shape, sel, L.q, L.k_pool, L.block_table, L.seq_lens, logits, stats, ws)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    score_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    algo = score_bytes_per_token(geo) * L0.total
+    kbytes = geo.num_kv_heads * geo.head_dim * (2 if geo.dtype == "bf16" else 4) * L0.total
+    res = dict(ms_per_step=ms_step, wall_ms_per_step=wall / steps * 1e3, score_ms=score_ms,
+               score_gbps=algo / (score_ms * 1e-3) / 1e9, k_gbps=kbytes / (score_ms * 1e-3) / 1e9,
+               score_bytes=algo, tokens=L0.total)
+    log(f"[{geo.name}] score launch {score_ms:.4f} ms -> {res['score_gbps']:.0f} GB/s "
+        f"(K stream {res['k_gbps']:.0f} GB/s)")
+    host = L0.host
+    del layers, ws, logits
+    torch.cuda.empty_cache()
+    return res, host
+
+
+def cpu_baseline(geo, host):
+    """The fp64 oracle, as it stands, on one decode step of layer 0."""
+    from oracle import tokenselect_oracle as ora
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        threads = 1
+    q, K, V = host
+    t0 = time.perf_counter()
+    ora.decode_step(q, K, V, geo.top_k, geo.n_local, 1.0, geo.attn_scale)
+    dt = time.perf_counter() - t0
+    log(f"[cpu oracle] one decode step in {dt:.2f}s with {threads} threads")
+    return {"value": 1.0 / dt, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"one decode step of layer 0 of {geo.name} (N={K.shape[1]}): select + "
+                      f"attention, numpy fp64, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import workloads as wl
+    import token_level_sparse_amd as ts
+    ts.load_library()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    geo = wl.workload("llama3-8b-1m")
+    main_res, host = time_workload(geo, args.layers, args.steps, args.warmup, dev,
+                                   keep_host=not args.no_cpu_baseline)
+    secondary = None
+    if not args.no_secondary:
+        g1 = wl.workload("llama3-8b-128k")
+        # 8 rotating layers: 8 x 256 MiB of K, so no step finds its pool in the 256 MB MALL
+        r1, _ = time_workload(g1, 8, max(args.steps, 32), args.warmup, dev)
+        secondary = {"workload": g1.name, "N": g1.seq_len, "decode_steps_per_s": 1e3 / r1["ms_per_step"],
+                     "ms_per_step": r1["ms_per_step"], "score_ms": r1["score_ms"],
+                     "score_gbps": r1["score_gbps"], "k_gbps": r1["k_gbps"], "rotating_layers": 8}
+    cpu = cpu_baseline(geo, host) if host is not None else None
+
+    ms = main_res["ms_per_step"]
+    line = {
+        "metric": "decode steps/s and K-scoring HBM GB/s (% peak) at N=128K and 1M, 1 GPU",
+        "value": 1e3 / ms,
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": geo.name, "N": geo.seq_len, "batch": 1,
+                   "heads": f"{geo.num_q_heads}/{geo.num_kv_heads}/{geo.head_dim}",
+                   "top_k": geo.top_k, "n_local": geo.n_local, "page_size": geo.page_size,
+                   "layers": args.layers, "cache": "every step reselects"},
+        "roofline": {"bound": "hbm", "achieved": main_res["score_gbps"], "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": main_res["score_gbps"] / PEAK_HBM_GBPS, "traffic": None,
+                     "kernel": "score (tokenselect_score launch)",
+                     "bytes_per_launch": main_res["score_bytes"], "launch_ms": main_res["score_ms"]},
+        "k_stream_gbps": main_res["k_gbps"],
+        "scored_tokens_per_s": main_res["tokens"] * 1e3 / ms,
+        "secondary": secondary,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

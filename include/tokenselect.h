@@ -1,0 +1,171 @@
+/*
+ * tokenselect.h - C ABI of the MI355X (gfx950) decode-step hot path of
+ * TokenSelect-style dynamic token-level KV-cache selection.
+ *
+ * Per layer and per request a decode step
+ *   0. checks the Selection Cache (cosine of the concatenated query against the
+ *      query stored at the last reselection),
+ *   1. scores the current query against every cached key of its KV head
+ *      (paged pool, GQA: query head h reads KV head h / (H / H_kv)),
+ *   2. normalises each head's scores by a softmax over all N cached tokens,
+ *   3. sums the normalised scores over the H query heads (head soft vote),
+ *   4. keeps the top_k positions of the vote, united with the n_local most
+ *      recent positions,
+ *   5. runs scaled-dot-product attention over only those positions.
+ *
+ * Sources: "TokenSelect: Efficient Long-Context Inference and Length
+ * Extrapolation for LLMs via Dynamic Token-Level KV Cache Selection"
+ * (deepnotes page): selective sparse attention formalisation (SDPA over the
+ * selected keys plus the current one), head soft vote equation, Selection Cache
+ * (appendix Algorithm 1), Paged Dot Product Kernel (appendix Algorithm 2).
+ * Blog review of the same paper: section 3 (Fig. 4 data flow: only indices move,
+ * the paged KV stays in place), section 3.2 (Algorithm 1), section 4.2 (budget of
+ * selected plus local tokens).
+ *
+ * Conventions shared by every entry point
+ *   - Array arguments are DEVICE pointers unless stated; the structs are host
+ *     memory read during the call only. The library keeps no pointer after a
+ *     call returns and allocates no memory: the caller owns every buffer,
+ *     including the workspace.
+ *   - Work is enqueued on `stream` in order; no call synchronises the host with
+ *     the device. Calls are reentrant; calls that share a workspace must be
+ *     ordered on one stream.
+ *   - Host-side validation runs before any launch. On failure nothing is
+ *     launched and a non-zero ts_status is returned; tokenselect_last_error()
+ *     gives a message (thread-local). A failed launch returns TS_ERR_DEVICE.
+ *   - Device-side contract (not checked): every block-table entry a request
+ *     reaches (pages [0, ceil(N_r / page_size))) is a valid pool page;
+ *     1 <= N_r <= block_table_stride * page_size; sum of N_r <=
+ *     shape.max_total_tokens; every selected index lies in [0, N_r).
+ *
+ * Layouts
+ *   q          [batch][H][d]                      element type `dtype`
+ *   k_pool     [num_pages][H_kv][page_size][d]    element type `dtype`
+ *   v_pool     same as k_pool
+ *   block_table int32 [batch][block_table_stride]: logical page p of request r
+ *              is pool page block_table[r * stride + p]; token i of request r
+ *              is slot i % page_size of logical page i / page_size.
+ *   seq_lens   int32 [batch]: N_r, cached tokens including the current one.
+ *   Ragged token axis: request r owns positions [off_r, off_r + N_r) with
+ *   off_r = N_0 + ... + N_{r-1} (computed on the device from seq_lens).
+ *   logits     fp32: request r, query head h, token i at off_r * H + h * N_r + i.
+ *   head_stats fp32 [batch][H][2]: (M_h, Z_h) = (max_i z, sum_i exp(z - M_h)).
+ *   vote       fp32: request r, token i at off_r + i.
+ *   sel_idx    int32 [batch][top_k]: the TopK positions of request r, ascending,
+ *              in the first sel_count[r] = min(top_k, N_r) entries.
+ *   out        [batch][H][d] element type `dtype` (bf16 results are rounded to
+ *              nearest even from fp32 accumulators).
+ */
+#ifndef TOKENSELECT_H
+#define TOKENSELECT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TS_OK = 0,
+  TS_ERR_INVALID_ARG = 1,   /* null pointer, inconsistent sizes, negative values */
+  TS_ERR_UNSUPPORTED = 2,   /* valid but not built: head_dim != 128, page_size != 16, G > 8 ... */
+  TS_ERR_WORKSPACE = 3,     /* ws_bytes smaller than tokenselect_workspace_size() */
+  TS_ERR_DEVICE = 4         /* a HIP launch failed; the HIP error text is in last_error */
+} ts_status;
+
+typedef enum { TS_F32 = 0, TS_BF16 = 1 } ts_dtype;
+
+/* Problem shape (host struct). */
+typedef struct {
+  int32_t num_q_heads;        /* H, >= 1                                         */
+  int32_t num_kv_heads;       /* H_kv, >= 1, H % H_kv == 0, H / H_kv <= 8         */
+  int32_t head_dim;           /* d; this build supports 128                     */
+  int32_t page_size;          /* tokens per page; this build supports 16        */
+  int32_t batch;              /* requests, 1 ... 1024                           */
+  int32_t block_table_stride; /* int32 entries per block-table row, >= 1        */
+  int64_t max_total_tokens;   /* upper bound of sum_r N_r (sizes grids/workspace) */
+  int32_t dtype;              /* ts_dtype of q, K/V pools and out               */
+} ts_shape;
+
+/* Selection parameters (host struct). */
+typedef struct {
+  int32_t top_k;              /* k >= 1: TopK budget of the head soft vote       */
+  int32_t n_local;            /* L >= 0: most recent positions always attended   */
+  float score_scale;          /* multiplies <q, k> before the selection softmax;
+                                 1.0 is the printed vote equation (raw logits)  */
+  float attn_scale;           /* SDPA scale, normally 1/sqrt(d)                  */
+  double cos_threshold;       /* theta: reuse the cached selection iff cos >= theta */
+} ts_select;
+
+/* Selection Cache state, caller-owned device buffers kept across steps
+   (deepnotes appendix Algorithm 1: C_Q, C_T and the first-query flag). */
+typedef struct {
+  void* cached_q;             /* [batch][H * d], element type dtype: C_Q         */
+  int32_t* cached_idx;        /* [batch][top_k]: C_T, the TopK of the last miss  */
+  int32_t* cached_count;      /* [batch]: entries of cached_idx in use           */
+  int32_t* valid;             /* [batch]: 0 = no cached query (forces a miss);
+                                 the caller zeroes it to reset a request         */
+} ts_cache;
+
+/* Bytes of workspace every entry point below needs for `shape` and `sel`
+   (the decode step's need, which covers the others). Returns 0 if the shape or
+   the selection parameters are invalid. */
+size_t tokenselect_workspace_size(const ts_shape* shape, const ts_select* sel);
+
+/* Steps 1-2. Paged dot product z[h][i] = score_scale * <q_h, K_{h/G}[i]> for every
+   cached token i < N_r of every request (deepnotes appendix Algorithm 2), and the
+   per-head softmax statistics (M_h, Z_h) over all N_r tokens (head soft vote
+   equation). `logits` holds max_total_tokens * H floats, `head_stats`
+   batch * H * 2 floats. */
+ts_status tokenselect_score(const ts_shape* shape, const ts_select* sel,
+                            const void* q, const void* k_pool,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            float* logits, float* head_stats,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Steps 3-4 (TopK part). Head soft vote v_i = sum_h exp(z[h][i] - M_h) / Z_h and
+   TopK over all N_r positions: the k largest votes, ties to the lower position,
+   written ascending to sel_idx[r][0 .. sel_count[r]) with sel_count[r] =
+   min(top_k, N_r). `vote` (max_total_tokens floats) may be NULL; then the votes
+   stay in the workspace. The local window is not written: step 5 adds it. */
+ts_status tokenselect_vote_topk(const ts_shape* shape, const ts_select* sel,
+                                const float* logits, const float* head_stats,
+                                const int32_t* seq_lens, float* vote,
+                                int32_t* sel_idx, int32_t* sel_count,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Step 5. Attention of every query head over S_r = TopK_r united with
+   [max(0, N_r - n_local), N_r), without duplicates: out[r][h] = sum_{i in S_r}
+   softmax_i(attn_scale * <q_h, K_{h/G}[i]>) V_{h/G}[i] (deepnotes selective
+   sparse attention formalisation). sel_idx rows must be ascending. */
+ts_status tokenselect_sparse_attn(const ts_shape* shape, const ts_select* sel,
+                                  const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  const int32_t* sel_idx, const int32_t* sel_count,
+                                  void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Steps 0-5 for one decode step of every request, with no host synchronisation.
+   Per request: hit = valid && |Q| > 0 && |C_Q| > 0 && cos(Q, C_Q) >= theta, with
+   Q the H*d query elements and the cosine accumulated in fp64 (deepnotes appendix
+   Algorithm 1). On a miss steps 1-4 run, C_Q <- Q, C_T <- TopK, valid <- 1;
+   on a hit C_T is reused. Step 5 always runs with the current N_r window.
+   hit[r] (device int32 [batch]) receives 1 for a reuse, 0 for a reselection. */
+ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel,
+                                  const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  const ts_cache* cache, int32_t* hit, void* out,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* tokenselect_status_string(ts_status status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* tokenselect_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENSELECT_H */

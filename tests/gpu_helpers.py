@@ -1,0 +1,165 @@
+"""Shared helpers of the GPU parity tests: run the HIP path, run the oracle, compare.
+
+Comparison bands (fp32 arithmetic on the GPU against the fp64 oracle):
+  logits   |z_gpu - z_ora| <= 16 u * score_scale * sum_d |q_d k_d| + 1e-30
+  (a) vote |v_gpu - v_ora| <= 1e-4 v_ora + e_i  (e_i: oracle first-order fp32 budget)
+  (b) TopK the GPU set differs from the oracle set only at positions whose oracle
+      vote is within tolerance of the k-th vote; and, with the decision taken in
+      the GPU's own precision, it is exactly the TopK of the GPU's fp32 votes
+      (ties to the lower position)
+  (c) out  max-abs <= 1e-4 (fp32; plus the attention budget) or 2e-2 (bf16)
+      against the oracle's attention over the GPU's own selected set
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+import token_level_sparse_amd as ts
+from oracle import tokenselect_oracle as ora
+from oracle import tolerance as tol
+from synth import workloads as wl
+
+U32 = 2.0 ** -24
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def np32(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+@dataclass
+class PathOut:
+    logits: List[np.ndarray]      # per request [H][N_r]
+    stats: np.ndarray             # [b][H][2]
+    vote: List[np.ndarray]        # per request [N_r]
+    T: List[np.ndarray]           # per request ascending TopK
+    out: np.ndarray               # [b][H][d] (as fp32)
+    raw: dict
+
+
+def select_params(geo: wl.Geometry, top_k=None, n_local=None, score_scale=1.0, theta=None):
+    return ts.make_select(geo.top_k if top_k is None else top_k,
+                          geo.n_local if n_local is None else n_local,
+                          score_scale, geo.attn_scale,
+                          geo.cos_threshold if theta is None else theta)
+
+
+def run_path(batch: wl.PagedBatch, geo: wl.Geometry, top_k=None, n_local=None,
+             score_scale=1.0, max_total: Optional[int] = None, sel_override=None) -> PathOut:
+    """Run score -> vote_topk -> sparse_attn through the C ABI on the batch."""
+    b = batch.q.shape[0]
+    total = batch.total_tokens
+    max_total = max_total or total
+    shape = ts.make_shape(geo.num_q_heads, geo.num_kv_heads, b, batch.block_table.shape[1],
+                          max_total, geo.torch_dtype)
+    sel = select_params(geo, top_k, n_local, score_scale)
+    k = sel.top_k
+    dev = batch.q.device
+    ws = ts.alloc_workspace(shape, sel, dev)
+    H = geo.num_q_heads
+    logits = torch.full((H * max_total,), float("nan"), dtype=torch.float32, device=dev)
+    stats = torch.full((b * H * 2,), float("nan"), dtype=torch.float32, device=dev)
+    vote = torch.full((max_total,), float("nan"), dtype=torch.float32, device=dev)
+    sel_idx = torch.full((b, k), -7, dtype=torch.int32, device=dev)
+    sel_count = torch.full((b,), -7, dtype=torch.int32, device=dev)
+    out = torch.full((b, H, geo.head_dim), float("nan"), dtype=geo.torch_dtype, device=dev)
+    ts.score(shape, sel, batch.q, batch.k_pool, batch.block_table, batch.seq_lens, logits, stats, ws)
+    ts.vote_topk(shape, sel, logits, stats, batch.seq_lens, vote, sel_idx, sel_count, ws)
+    if sel_override is not None:
+        sel_idx, sel_count = sel_override
+    ts.sparse_attn(shape, sel, batch.q, batch.k_pool, batch.v_pool, batch.block_table,
+                   batch.seq_lens, sel_idx, sel_count, out, ws)
+    torch.cuda.synchronize()
+    offs = batch.token_offsets.cpu().tolist()
+    lens = batch.seq_lens.cpu().tolist()
+    lg = logits.cpu().numpy()
+    vt = vote.cpu().numpy()
+    si = sel_idx.cpu().numpy()
+    sc = sel_count.cpu().numpy()
+    L, V, T = [], [], []
+    for r in range(b):
+        n = lens[r]
+        L.append(lg[offs[r] * H: offs[r] * H + H * n].reshape(H, n))
+        V.append(vt[offs[r]: offs[r] + n])
+        assert sc[r] == min(k, n), (r, sc[r], k, n)
+        T.append(si[r, : sc[r]].astype(np.int64))
+    return PathOut(L, stats.cpu().numpy().reshape(b, H, 2), V, T, np32(out),
+                   dict(logits=logits, vote=vote, sel_idx=sel_idx, sel_count=sel_count, out=out))
+
+
+def check_logits(z_gpu, q, K, ref, score_scale=1.0, factor=16.0):
+    A = tol.abs_dot(q, K)
+    lim = factor * U32 * abs(score_scale) * A + 1e-30
+    err = np.abs(z_gpu.astype(np.float64) - ref)
+    bad = err > lim
+    assert not bad.any(), f"logits: {bad.sum()} outside, worst excess {np.max(err - lim):.3e}"
+
+
+def check_stats(stats_gpu, sel_ora, q, K, score_scale=1.0):
+    """M_h within the logit band; Z_h within a relative 1e-4 plus the fp32 budget."""
+    A = tol.abs_dot(q, K)
+    for h in range(q.shape[0]):
+        M, Z = stats_gpu[h]
+        i = int(np.argmax(sel_ora["z"][h]))
+        assert abs(M - sel_ora["M"][h]) <= 16 * U32 * score_scale * A[h, i] + 1e-30, (h, M, sel_ora["M"][h])
+        bz = 4 * U32 * np.sum(sel_ora["p"][h] * (np.abs(sel_ora["z"][h]) + abs(sel_ora["M"][h])
+                                                  + score_scale * A[h]))
+        assert abs(Z - sel_ora["Z"][h]) <= 1e-4 * sel_ora["Z"][h] + bz * sel_ora["Z"][h], (h, Z, sel_ora["Z"][h])
+
+
+def check_vote(v_gpu, sel_ora, q, K, score_scale=1.0, factor=4.0):
+    budget = tol.vote_budget(q, K, sel_ora["z"], sel_ora["p"], sel_ora["M"], score_scale) * (factor / 4.0)
+    ok, excess = tol.vote_within(v_gpu, sel_ora["vote"], budget)
+    strict = np.abs(v_gpu - sel_ora["vote"]) <= 1e-4 * sel_ora["vote"]
+    assert ok.all(), f"vote: {(~ok).sum()} outside band (a), worst excess {excess.max():.3e}"
+    return budget, int((~strict).sum())
+
+
+def check_topk(T_gpu, v_gpu, sel_ora, budget, k):
+    N = len(v_gpu)
+    assert np.all(np.diff(T_gpu) > 0), "TopK not strictly ascending"
+    assert len(T_gpu) == min(k, N)
+    assert T_gpu.min() >= 0 and T_gpu.max() < N
+    # the decision in the GPU's own precision: exact TopK of the fp32 votes
+    exact = ora.topk_indices(v_gpu.astype(np.float64), k)
+    assert np.array_equal(T_gpu, exact), "TopK differs from the exact TopK of the GPU votes"
+    amb = tol.ambiguous_positions(sel_ora["vote"], budget, k)
+    diff = np.setxor1d(T_gpu, sel_ora["T"])
+    assert np.all(amb[diff]), f"TopK differs from the oracle outside band (b) at {diff[~amb[diff]][:10]}"
+    return len(diff)
+
+
+def check_attention(out_gpu, q, K, V, T_gpu, N, n_local, attn_scale, fp32: bool):
+    S = ora.union_local(T_gpu, N, n_local)
+    ref = ora.sparse_attention(q, K, V, S, attn_scale)
+    err = np.abs(out_gpu.astype(np.float64) - ref)
+    if fp32:
+        lim = 1e-4 + tol.attn_budget(q, K, V, S, attn_scale, ref)
+    else:
+        lim = 2e-2
+    assert np.all(err <= lim), f"attention max-abs {err.max():.3e} (limit {np.max(lim):.3e})"
+    return float(err.max())
+
+
+def check_request(po: PathOut, r: int, req: wl.Request, geo: wl.Geometry, top_k=None,
+                  n_local=None, score_scale=1.0):
+    k = geo.top_k if top_k is None else top_k
+    L = geo.n_local if n_local is None else n_local
+    q, K, V = np32(req.q), np32(req.k), np32(req.v)
+    sel = ora.select(q, K, k, score_scale)
+    check_logits(po.logits[r], q, K, sel["z"], score_scale)
+    check_stats(po.stats[r], sel, q, K, score_scale)
+    budget, n_loose = check_vote(po.vote[r], sel, q, K, score_scale)
+    n_diff = check_topk(po.T[r], po.vote[r], sel, budget, k)
+    err = check_attention(po.out[r], q, K, V, po.T[r], K.shape[1], L, geo.attn_scale,
+                          geo.dtype == "f32")
+    return dict(n_loose=n_loose, n_diff=n_diff, attn_err=err)

@@ -1,0 +1,145 @@
+"""Host-side checks of the C ABI: exports, workspace sizing and argument validation.
+
+Every call here fails validation before any launch, so no GPU is needed (the
+HIP runtime is never initialised by these paths).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_level_sparse_amd as ts
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tokenselect.h")
+
+FAKE = ctypes.c_void_p(4096)      # non-null, never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ts.LIB_PATH):
+        pytest.skip("library not built")
+    return ts.load_library()
+
+
+def _shape(**kw):
+    d = dict(num_q_heads=32, num_kv_heads=8, batch=1, block_table_stride=8192,
+             max_total_tokens=131072, dtype=ts.TS_BF16)
+    d.update(kw)
+    return ts.make_shape(**d)
+
+
+def _sel(**kw):
+    d = dict(top_k=2048, n_local=512)
+    d.update(kw)
+    return ts.make_select(**d)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = set(re.findall(r"\b(tokenselect_\w+)\s*\(", open(HEADER).read()))
+    assert names == set(ts.ENTRY_POINTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_workspace_size_valid_and_monotone(lib):
+    a = ts.workspace_size(_shape(), _sel())
+    b = ts.workspace_size(_shape(max_total_tokens=1 << 20), _sel())
+    assert a > 0 and b > a
+    # logits (H * N fp32) dominate: at least 16 MiB at 128K tokens x 32 heads
+    assert a >= 32 * 131072 * 4
+    assert a % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=30), ts.TS_ERR_INVALID_ARG),       # 30 % 8 != 0
+    (dict(num_q_heads=0), ts.TS_ERR_INVALID_ARG),
+    (dict(num_q_heads=72, num_kv_heads=8), ts.TS_ERR_UNSUPPORTED),   # group 9 > 8
+    (dict(head_dim=64), ts.TS_ERR_UNSUPPORTED),
+    (dict(page_size=32), ts.TS_ERR_UNSUPPORTED),
+    (dict(batch=0), ts.TS_ERR_INVALID_ARG),
+    (dict(batch=2000, max_total_tokens=1 << 22), ts.TS_ERR_INVALID_ARG),
+    (dict(block_table_stride=0), ts.TS_ERR_INVALID_ARG),
+    (dict(max_total_tokens=0), ts.TS_ERR_INVALID_ARG),
+    (dict(dtype=7), ts.TS_ERR_UNSUPPORTED),
+])
+def test_invalid_shapes_rejected(lib, kw, status):
+    shape = _shape(**kw)
+    sel = _sel()
+    assert ts.workspace_size(shape, sel) == 0
+    st = lib.tokenselect_score(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == status
+    assert lib.tokenselect_last_error().decode()
+
+
+@pytest.mark.parametrize("kw", [dict(top_k=0), dict(n_local=-1)])
+def test_invalid_selection_rejected(lib, kw):
+    shape, sel = _shape(), _sel(**kw)
+    assert ts.workspace_size(shape, sel) == 0
+    st = lib.tokenselect_vote_topk(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE, None,
+                                   FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+
+
+def test_null_pointers_rejected_with_their_name(lib):
+    shape, sel = _shape(), _sel()
+    big = 1 << 40
+    st = lib.tokenselect_score(ctypes.byref(shape), ctypes.byref(sel), FAKE, None, FAKE, FAKE,
+                               FAKE, FAKE, FAKE, big, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+    assert "k_pool" in lib.tokenselect_last_error().decode()
+    st = lib.tokenselect_sparse_attn(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, None, FAKE, FAKE, FAKE, big, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+    assert "sel_idx" in lib.tokenselect_last_error().decode()
+    cache = ts.Cache(FAKE, FAKE, None, FAKE)
+    st = lib.tokenselect_decode_step(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, ctypes.byref(cache), FAKE, FAKE, FAKE, big, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+    assert "cached_count" in lib.tokenselect_last_error().decode()
+    st = lib.tokenselect_decode_step(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, None, FAKE, FAKE, FAKE, big, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+
+
+def test_small_workspace_rejected_before_launch(lib):
+    shape, sel = _shape(), _sel()
+    need = ts.workspace_size(shape, sel)
+    st = lib.tokenselect_score(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, FAKE, need - 1, None)
+    assert st == ts.TS_ERR_WORKSPACE
+    assert str(need) in lib.tokenselect_last_error().decode()
+    st = lib.tokenselect_score(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, None, need, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+    misaligned = ctypes.c_void_p(4096 + 4)
+    st = lib.tokenselect_score(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, misaligned, need, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+
+
+def test_top_k_above_capacity_rejected_for_attention(lib):
+    shape, sel = _shape(max_total_tokens=1000), _sel(top_k=2048)
+    need = ts.workspace_size(shape, sel)
+    assert need > 0
+    cache = ts.Cache(FAKE, FAKE, FAKE, FAKE)
+    st = lib.tokenselect_decode_step(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, ctypes.byref(cache), FAKE, FAKE, FAKE, need, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.tokenselect_status_string(code).decode()
+    assert lib.tokenselect_status_string(99).decode() == "unknown status"
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    shape, sel = _shape(max_total_tokens=64), _sel(top_k=8, n_local=4)
+    x = torch.zeros(4)
+    with pytest.raises(ValueError):
+        ts.score(shape, sel, x, x, x, x, x, x, x)

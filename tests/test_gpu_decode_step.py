@@ -1,0 +1,113 @@
+"""GPU parity of tokenselect_decode_step (Selection Cache + steps 1-5) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import token_level_sparse_amd as ts
+from tests import gpu_helpers as gh
+from synth import workloads as wl
+from oracle import tokenselect_oracle as ora
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_sequence(geo, N0, steps, theta, qs=None, reset_at=()):
+    """Decode `steps` consecutive steps; token N0 + t - 1 is the newest at step t."""
+    gen = torch.Generator(device=DEV).manual_seed(geo.seed)
+    req = wl.make_request(gen, geo, N0, DEV, extra_tokens=steps - 1)
+    batch = wl.page_requests([req], geo, gen, DEV)
+    if qs is None:
+        qs, _ = wl.ar1_queries(geo, req.q_master, steps, seed=geo.seed + 1, device=DEV)
+    H, d = geo.num_q_heads, geo.head_dim
+    shape = ts.make_shape(H, geo.num_kv_heads, 1, batch.block_table.shape[1], N0 + steps - 1,
+                          geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, theta)
+    ws = ts.alloc_workspace(shape, sel, DEV)
+    cache = ts.CacheState.allocate(1, H, d, geo.top_k, geo.torch_dtype, DEV)
+    hit = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.empty(1, H, d, dtype=geo.torch_dtype, device=DEV)
+    lens = torch.arange(N0, N0 + steps, dtype=torch.int32, device=DEV)
+    hits, Ts, outs = [], [], []
+    for t in range(steps):
+        if t in reset_at:
+            cache.valid.zero_()
+        ts.decode_step(shape, sel, qs[t:t + 1].contiguous(), batch.k_pool, batch.v_pool,
+                       batch.block_table, lens[t:t + 1], cache, hit, out, ws)
+        hits.append(hit.clone())
+        Ts.append(cache.cached_idx[0, :].clone())
+        outs.append(out.clone())
+        Ts[-1] = (Ts[-1], cache.cached_count.clone())
+    torch.cuda.synchronize()
+    hits = np.array([int(h.item()) for h in hits], dtype=bool)
+    T = [ti[: int(c.item())].cpu().numpy().astype(np.int64) for ti, c in Ts]
+    outs = np.stack([gh.np32(o[0]) for o in outs])
+    return req, qs, lens.cpu().numpy(), hits, T, outs
+
+
+def compare(geo, req, qs, lens, hits, T, outs, theta, band_steps=24):
+    q_all = gh.np32(qs)
+    K, V = gh.np32(req.k), gh.np32(req.v)
+    ref = ora.decode_sequence(q_all, K, V, lens, geo.top_k, geo.n_local, theta, want_outputs=False)
+    c = ref["cos"]
+    margin = np.abs(c[~np.isnan(c)] - theta)
+    gh.log(f"  hits gpu={hits.sum()}/{len(hits)} min|cos-theta|={margin.min() if len(margin) else float('nan'):.3e}")
+    assert margin.size == 0 or margin.min() > 1e-9
+    assert np.array_equal(hits, ref["hit"]), f"hit vectors differ at {np.nonzero(hits != ref['hit'])[0][:10]}"
+    checked = 0
+    last_miss_T = None
+    for t in range(len(hits)):
+        N = int(lens[t])
+        if not hits[t]:
+            last_miss_T = T[t]
+            if checked < band_steps:
+                sel = ora.select(q_all[t], K[:, :N], geo.top_k)
+                budget = gh.tol.vote_budget(q_all[t], K[:, :N], sel["z"], sel["p"], sel["M"])
+                amb = gh.tol.ambiguous_positions(sel["vote"], budget, geo.top_k)
+                diff = np.setxor1d(T[t], sel["T"])
+                assert np.all(amb[diff]), (t, diff[~amb[diff]][:10])
+                checked += 1
+        else:
+            assert np.array_equal(T[t], last_miss_T), f"step {t}: a hit must reuse the last miss's TopK"
+        gh.check_attention(outs[t], q_all[t], K[:, :N], V[:, :N], T[t], N, geo.n_local,
+                           geo.attn_scale, geo.dtype == "f32")
+
+
+def test_decode_sequence_reduced():
+    geo = wl.workload("qwen2-7b-cache256", top_k=256, n_local=64, n_planted=16)
+    gh.log("[qwen2 decode N0=4096 48 steps k=256]")
+    res = run_sequence(geo, 4096, 48, 0.9)
+    compare(geo, *res, theta=0.9)
+
+
+def test_decode_sequence_full_256_steps():
+    geo = wl.workload("qwen2-7b-cache256")
+    gh.log(f"[qwen2-7b-cache256] N0={geo.seq_len} {geo.steps} steps")
+    res = run_sequence(geo, geo.seq_len, geo.steps, geo.cos_threshold)
+    compare(geo, *res, theta=geo.cos_threshold)
+
+
+def test_cache_identical_queries_and_thresholds():
+    geo = wl.workload("llama3-8b-128k", seq_len=3000, top_k=128, n_local=16, n_planted=4)
+    gh.log("[cache] identical queries / theta extremes / reset")
+    gen = torch.Generator(device=DEV).manual_seed(3)
+    q0 = torch.randn(1, geo.num_q_heads, geo.head_dim, generator=gen, device=DEV).to(torch.bfloat16)
+    same = q0.repeat(6, 1, 1)
+    _, _, _, hits, T, _ = run_sequence(geo, 3000, 6, 0.9, qs=same)
+    assert hits.tolist() == [False] + [True] * 5
+    _, _, _, hits, _, _ = run_sequence(geo, 3000, 6, 1.5, qs=same)
+    assert hits.tolist() == [False] * 6
+    other = torch.randn(6, geo.num_q_heads, geo.head_dim, generator=gen, device=DEV).to(torch.bfloat16)
+    _, _, _, hits, T, _ = run_sequence(geo, 3000, 6, -1.0, qs=other)
+    assert hits.tolist() == [False] + [True] * 5
+    assert all(np.array_equal(T[i], T[0]) for i in range(6))
+    _, _, _, hits, _, _ = run_sequence(geo, 3000, 6, 0.9, qs=same, reset_at=(3,))
+    assert hits.tolist() == [False, True, True, False, True, True]
+
+
+def test_zero_query_misses():
+    geo = wl.workload("llama3-8b-128k", seq_len=500, top_k=64, n_local=8, n_planted=4)
+    gh.log("[cache] zero query")
+    q = torch.zeros(3, geo.num_q_heads, geo.head_dim, dtype=torch.bfloat16, device=DEV)
+    _, _, _, hits, _, _ = run_sequence(geo, 500, 3, -1.0, qs=q)
+    assert hits.tolist() == [False, False, False]

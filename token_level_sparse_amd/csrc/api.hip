@@ -1,0 +1,290 @@
+// C ABI of the decode-step path: argument validation, workspace layout, launches.
+// The entry points and their contracts are declared and documented in
+// include/tokenselect.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "common.h"
+#include "kernels.h"
+#include "tokenselect.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ts_status fail(ts_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ts_status fail(ts_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ts_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TS_OK;
+  return fail(TS_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kMinChunkPages = 4;     // smallest score work unit (pages)
+constexpr int kMaxChunkPages = 32;
+constexpr int kScoreUnitsTarget = 16384;
+constexpr int kMaxGrid = 2048;
+
+// Byte offsets of the workspace regions.
+struct Layout {
+  size_t logits, partials, stats, vote, hist, state, tiles, attn, total;
+};
+
+int64_t max_chunks(const ts_shape& s) {
+  return cdiv(s.max_total_tokens, (int64_t)kMinChunkPages * ts::kPage) + s.batch;
+}
+int64_t max_tiles(const ts_shape& s) { return cdiv(s.max_total_tokens, ts::kVoteTile) + s.batch; }
+
+// Attention work items per (request, KV head): TopK list plus window, capped by
+// the largest possible N.
+int eff_top_k(const ts_shape& s, const ts_select& sel) {
+  return (int)std::min<int64_t>(sel.top_k, s.max_total_tokens);
+}
+int eff_local(const ts_shape& s, const ts_select& sel) {
+  return (int)std::min<int64_t>(sel.n_local, s.max_total_tokens);
+}
+
+Layout layout(const ts_shape& s, const ts_select& sel) {
+  Layout L;
+  size_t off = 0;
+  const int64_t T = s.max_total_tokens;
+  const int H = s.num_q_heads;
+  L.logits = off;   off += align_up(sizeof(float) * (size_t)H * T);
+  L.partials = off; off += align_up(sizeof(float) * 2 * (size_t)H * max_chunks(s));
+  L.stats = off;    off += align_up(sizeof(float) * 2 * (size_t)H * s.batch);
+  L.vote = off;     off += align_up(sizeof(float) * (size_t)T);
+  L.hist = off;     off += align_up(sizeof(uint32_t) * 3 * ts::kHistBins * (size_t)s.batch);
+  L.state = off;    off += align_up(sizeof(int32_t) * 8 * (size_t)s.batch);
+  L.tiles = off;    off += align_up(sizeof(int32_t) * 2 * (size_t)max_tiles(s));
+  const int S = ts::attn_splits(eff_top_k(s, sel), eff_local(s, sel));
+  L.attn = off;     off += align_up(sizeof(float) * (ts::kHeadDim + 2) * (size_t)s.batch * H * S);
+  L.total = off;
+  return L;
+}
+
+ts_status check_shape(const ts_shape* s, const ts_select* sel) {
+  if (!s || !sel) return fail(TS_ERR_INVALID_ARG, "shape and select must not be NULL");
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return fail(TS_ERR_INVALID_ARG, "num_q_heads (%d) and num_kv_heads (%d) must be >= 1",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(TS_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads / s->num_kv_heads > ts::kMaxGroup)
+    return fail(TS_ERR_UNSUPPORTED, "GQA group %d > %d", s->num_q_heads / s->num_kv_heads, ts::kMaxGroup);
+  if (s->num_q_heads > 256) return fail(TS_ERR_UNSUPPORTED, "num_q_heads %d > 256", s->num_q_heads);
+  if (s->head_dim != ts::kHeadDim) return fail(TS_ERR_UNSUPPORTED, "head_dim %d != 128", s->head_dim);
+  if (s->page_size != ts::kPage) return fail(TS_ERR_UNSUPPORTED, "page_size %d != 16", s->page_size);
+  if (s->batch < 1 || s->batch > ts::kMaxBatch)
+    return fail(TS_ERR_INVALID_ARG, "batch %d outside [1, %d]", s->batch, ts::kMaxBatch);
+  if (s->block_table_stride < 1)
+    return fail(TS_ERR_INVALID_ARG, "block_table_stride %d < 1", s->block_table_stride);
+  if (s->max_total_tokens < s->batch || s->max_total_tokens > (int64_t)1 << 31)
+    return fail(TS_ERR_INVALID_ARG, "max_total_tokens %lld outside [batch, 2^31]",
+                (long long)s->max_total_tokens);
+  if (s->dtype != TS_F32 && s->dtype != TS_BF16)
+    return fail(TS_ERR_UNSUPPORTED, "dtype %d is neither TS_F32 nor TS_BF16", s->dtype);
+  if (sel->top_k < 1) return fail(TS_ERR_INVALID_ARG, "top_k %d < 1", sel->top_k);
+  if (sel->n_local < 0) return fail(TS_ERR_INVALID_ARG, "n_local %d < 0", sel->n_local);
+  return TS_OK;
+}
+
+ts_status check_ws(const ts_shape& s, const ts_select& sel, const void* ws, size_t ws_bytes) {
+  const size_t need = layout(s, sel).total;
+  if (!ws) return fail(TS_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws_bytes < need)
+    return fail(TS_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(TS_ERR_INVALID_ARG, "workspace must be %zu-byte aligned", kAlign);
+  return TS_OK;
+}
+
+#define TS_REQUIRE(ptr) \
+  do { if (!(ptr)) return fail(TS_ERR_INVALID_ARG, "%s must not be NULL", #ptr); } while (0)
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+int score_chunk_pages(const ts_shape& s) {
+  const int64_t pages = cdiv(s.max_total_tokens, ts::kPage) + s.batch;
+  int64_t cp = pages * s.num_kv_heads / kScoreUnitsTarget;
+  int c = kMinChunkPages;
+  while (c * 2 <= cp && c * 2 <= kMaxChunkPages) c *= 2;
+  return c;
+}
+
+ts::ScoreParams score_params(const ts_shape& s, const ts_select& sel, const void* q,
+                             const void* k_pool, const int32_t* bt, const int32_t* seq,
+                             const int32_t* skip, float* logits, float* stats, void* ws) {
+  const Layout L = layout(s, sel);
+  ts::ScoreParams p{};
+  p.q = q; p.k_pool = k_pool; p.block_table = bt; p.seq_lens = seq; p.skip = skip;
+  p.logits = logits; p.head_stats = stats; p.partials = at<float>(ws, L.partials);
+  p.H = s.num_q_heads; p.Hkv = s.num_kv_heads; p.b = s.batch; p.stride = s.block_table_stride;
+  p.chunk_pages = score_chunk_pages(s);
+  p.score_scale = sel.score_scale;
+  p.bf16 = s.dtype == TS_BF16;
+  const int64_t units = (cdiv(cdiv(s.max_total_tokens, ts::kPage) + s.batch, p.chunk_pages) + s.batch) *
+                        s.num_kv_heads;
+  p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxGrid, cdiv(units, 4)));
+  return p;
+}
+
+ts::VoteParams vote_params(const ts_shape& s, const ts_select& sel, const float* logits,
+                           const float* stats, const int32_t* seq, const int32_t* skip,
+                           float* vote, int32_t* sel_idx, int32_t* sel_count, void* ws) {
+  const Layout L = layout(s, sel);
+  ts::VoteParams p{};
+  p.logits = logits; p.head_stats = stats; p.seq_lens = seq; p.skip = skip;
+  p.vote = vote ? vote : at<float>(ws, L.vote);
+  p.hist = at<uint32_t>(ws, L.hist);
+  p.state = at<int32_t>(ws, L.state);
+  p.tile_counts = at<int32_t>(ws, L.tiles);
+  p.sel_idx = sel_idx; p.sel_count = sel_count;
+  p.H = s.num_q_heads; p.b = s.batch; p.top_k = sel.top_k;
+  p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxGrid, max_tiles(s)));
+  return p;
+}
+
+ts::AttnParams attn_params(const ts_shape& s, const ts_select& sel, const void* q,
+                           const void* k_pool, const void* v_pool, const int32_t* bt,
+                           const int32_t* seq, const int32_t* sel_idx, const int32_t* sel_count,
+                           void* out, void* ws) {
+  const Layout L = layout(s, sel);
+  ts::AttnParams p{};
+  p.q = q; p.k_pool = k_pool; p.v_pool = v_pool; p.block_table = bt; p.seq_lens = seq;
+  p.sel_idx = sel_idx; p.sel_count = sel_count; p.out = out;
+  p.partials = at<float>(ws, L.attn);
+  p.H = s.num_q_heads; p.Hkv = s.num_kv_heads; p.b = s.batch; p.stride = s.block_table_stride;
+  p.top_k = eff_top_k(s, sel);
+  p.n_local = eff_local(s, sel);
+  p.attn_scale = sel.attn_scale;
+  p.bf16 = s.dtype == TS_BF16;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tokenselect_workspace_size(const ts_shape* shape, const ts_select* sel) {
+  if (check_shape(shape, sel) != TS_OK) return 0;
+  return layout(*shape, *sel).total;
+}
+
+ts_status tokenselect_score(const ts_shape* shape, const ts_select* sel, const void* q,
+                            const void* k_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, float* logits, float* head_stats,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  ts_status st = check_shape(shape, sel);
+  if (st != TS_OK) return st;
+  TS_REQUIRE(q); TS_REQUIRE(k_pool); TS_REQUIRE(block_table); TS_REQUIRE(seq_lens);
+  TS_REQUIRE(logits); TS_REQUIRE(head_stats);
+  if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
+  const ts::ScoreParams p = score_params(*shape, *sel, q, k_pool, block_table, seq_lens, nullptr,
+                                         logits, head_stats, ws);
+  return device_status(ts::launch_score(p, stream), "score launch");
+}
+
+ts_status tokenselect_vote_topk(const ts_shape* shape, const ts_select* sel, const float* logits,
+                                const float* head_stats, const int32_t* seq_lens, float* vote,
+                                int32_t* sel_idx, int32_t* sel_count, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  ts_status st = check_shape(shape, sel);
+  if (st != TS_OK) return st;
+  TS_REQUIRE(logits); TS_REQUIRE(head_stats); TS_REQUIRE(seq_lens);
+  TS_REQUIRE(sel_idx); TS_REQUIRE(sel_count);
+  if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
+  const ts::VoteParams p = vote_params(*shape, *sel, logits, head_stats, seq_lens, nullptr, vote,
+                                       sel_idx, sel_count, ws);
+  return device_status(ts::launch_vote_topk(p, stream, true), "vote/top-k launch");
+}
+
+ts_status tokenselect_sparse_attn(const ts_shape* shape, const ts_select* sel, const void* q,
+                                  const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  const int32_t* sel_idx, const int32_t* sel_count, void* out,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  ts_status st = check_shape(shape, sel);
+  if (st != TS_OK) return st;
+  TS_REQUIRE(q); TS_REQUIRE(k_pool); TS_REQUIRE(v_pool); TS_REQUIRE(block_table);
+  TS_REQUIRE(seq_lens); TS_REQUIRE(sel_idx); TS_REQUIRE(sel_count); TS_REQUIRE(out);
+  if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
+  ts::AttnParams p = attn_params(*shape, *sel, q, k_pool, v_pool, block_table, seq_lens, sel_idx,
+                                 sel_count, out, ws);
+  p.top_k = sel->top_k;        // row stride of the caller's sel_idx
+  if (sel->top_k > shape->max_total_tokens)
+    return fail(TS_ERR_INVALID_ARG, "top_k %d > max_total_tokens for sparse_attn", sel->top_k);
+  return device_status(ts::launch_attn(p, stream), "sparse attention launch");
+}
+
+ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel, const void* q,
+                                  const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  const ts_cache* cache, int32_t* hit, void* out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  ts_status st = check_shape(shape, sel);
+  if (st != TS_OK) return st;
+  TS_REQUIRE(q); TS_REQUIRE(k_pool); TS_REQUIRE(v_pool); TS_REQUIRE(block_table);
+  TS_REQUIRE(seq_lens); TS_REQUIRE(cache); TS_REQUIRE(hit); TS_REQUIRE(out);
+  TS_REQUIRE(cache->cached_q); TS_REQUIRE(cache->cached_idx); TS_REQUIRE(cache->cached_count);
+  TS_REQUIRE(cache->valid);
+  if (sel->top_k > shape->max_total_tokens)
+    return fail(TS_ERR_INVALID_ARG, "top_k %d > max_total_tokens", sel->top_k);
+  if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
+  const Layout L = layout(*shape, *sel);
+  float* logits = at<float>(ws, L.logits);
+  float* stats = at<float>(ws, L.stats);
+
+  ts::CacheParams cp{};
+  cp.q = q; cp.cached_q = cache->cached_q; cp.valid = cache->valid; cp.hit = hit;
+  cp.hist = at<uint32_t>(ws, L.hist);
+  cp.H = shape->num_q_heads; cp.d = shape->head_dim; cp.b = shape->batch;
+  cp.theta = sel->cos_threshold; cp.bf16 = shape->dtype == TS_BF16;
+  if ((st = device_status(ts::launch_cache_check(cp, stream), "cache check launch")) != TS_OK) return st;
+
+  const ts::ScoreParams sp = score_params(*shape, *sel, q, k_pool, block_table, seq_lens, hit,
+                                          logits, stats, ws);
+  if ((st = device_status(ts::launch_score(sp, stream), "score launch")) != TS_OK) return st;
+
+  const ts::VoteParams vp = vote_params(*shape, *sel, logits, stats, seq_lens, hit, nullptr,
+                                        cache->cached_idx, cache->cached_count, ws);
+  if ((st = device_status(ts::launch_vote_topk(vp, stream, false), "vote/top-k launch")) != TS_OK)
+    return st;
+
+  ts::AttnParams ap = attn_params(*shape, *sel, q, k_pool, v_pool, block_table, seq_lens,
+                                  cache->cached_idx, cache->cached_count, out, ws);
+  ap.top_k = sel->top_k;
+  return device_status(ts::launch_attn(ap, stream), "sparse attention launch");
+}
+
+const char* tokenselect_status_string(ts_status s) {
+  switch (s) {
+    case TS_OK: return "ok";
+    case TS_ERR_INVALID_ARG: return "invalid argument";
+    case TS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TS_ERR_WORKSPACE: return "workspace too small";
+    case TS_ERR_DEVICE: return "device launch failed";
+  }
+  return "unknown status";
+}
+
+const char* tokenselect_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,234 @@
+// Step 5 of the decode step: scaled-dot-product attention over the selected set.
+//
+// Source: TokenSelect deepnotes page, selective sparse attention formalisation:
+// each head's output is the softmax of its query against the selected keys plus
+// the current one, scaled by 1/sqrt(d), applied to the matching values. The blog
+// page (section 3, Fig. 4) hands only the selected indices to the attention
+// kernel, with the paged KV left in place; section 4.2 adds a window of local
+// tokens to the selected budget.
+//
+// gfx950 design. The selected set of request r is the TopK list (ascending)
+// united with the window [N - L, N); TopK entries inside the window are skipped
+// because the window covers them, so no sort or merge is needed. Work items of
+// 32 tokens (one wavefront each) cover the TopK list and then the window, for one
+// KV head and all G query heads of its group: each key and value row (256 B in
+// bf16) is gathered once through the block table. Lane = 16 * row + col: the 4
+// rows of a wave take every 4th token and col picks 8 dims, DPP sums finish the
+// inner products, and each row keeps a (max, sum, o[8 dims]) online softmax in
+// registers. The rows merge by cross-row shuffles; a second kernel merges the
+// work items of each (request, head) and rounds the output.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace ts {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+constexpr int kTokPerRow = kAttnSplit / 4;   // 8 tokens per row of a wave
+
+template <bool kBf16> struct Row8;            // 8 dims of one token row held by a lane
+template <> struct Row8<true> { uint4 w; };
+template <> struct Row8<false> { float4 a, b; };
+
+__device__ __forceinline__ void load_row(Row8<true>& x, const uint16_t* rowp, int col) {
+  x.w = *reinterpret_cast<const uint4*>(rowp + 8 * col);
+}
+__device__ __forceinline__ void load_row(Row8<false>& x, const float* rowp, int col) {
+  x.a = *reinterpret_cast<const float4*>(rowp + 4 * col);
+  x.b = *reinterpret_cast<const float4*>(rowp + 64 + 4 * col);
+}
+__device__ __forceinline__ void to_f32(const Row8<true>& x, float (&f)[8]) {
+  f[0] = bf16_lo(x.w.x); f[1] = bf16_hi(x.w.x); f[2] = bf16_lo(x.w.y); f[3] = bf16_hi(x.w.y);
+  f[4] = bf16_lo(x.w.z); f[5] = bf16_hi(x.w.z); f[6] = bf16_lo(x.w.w); f[7] = bf16_hi(x.w.w);
+}
+__device__ __forceinline__ void to_f32(const Row8<false>& x, float (&f)[8]) {
+  f[0] = x.a.x; f[1] = x.a.y; f[2] = x.a.z; f[3] = x.a.w;
+  f[4] = x.b.x; f[5] = x.b.y; f[6] = x.b.z; f[7] = x.b.w;
+}
+// Dim index of element e of a lane's 8 (matches load_row).
+__device__ __forceinline__ int lane_dim(bool bf16, int col, int e) {
+  return bf16 ? 8 * col + e : (e < 4 ? 4 * col + e : 64 + 4 * col + (e - 4));
+}
+
+template <bool kBf16, int G>
+__global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
+  using T = typename std::conditional<kBf16, uint16_t, float>::type;
+  const int S = attn_splits(p.top_k, p.n_local);
+  const int nT = (p.top_k + kAttnSplit - 1) / kAttnSplit;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = lane >> 4, col = lane & 15;
+  const int w = blockIdx.x * 4 + wave;
+  if (w >= p.b * p.Hkv * S) return;
+  const int s = w % S;
+  const int rg = w / S;
+  const int g = rg % p.Hkv;
+  const int r = rg / p.Hkv;
+  const int H = p.H;
+  const int N = p.seq_lens[r];
+  const int lstart = max(0, N - p.n_local);
+
+  // Token of this wave's slot e = lane (lanes 0..31), then broadcast by shuffle.
+  int tok = 0;
+  bool ok = false;
+  if (lane < kAttnSplit) {
+    if (s < nT) {
+      const int e = s * kAttnSplit + lane;
+      if (e < min(p.sel_count[r], p.top_k)) {
+        tok = p.sel_idx[(int64_t)r * p.top_k + e];
+        ok = tok >= 0 && tok < lstart;
+      }
+    } else {
+      tok = lstart + (s - nT) * kAttnSplit + lane;
+      ok = tok < N;
+    }
+    if (!ok) tok = 0;                               // a real token; its weight is forced to 0
+  }
+  const int32_t* bt = p.block_table + (int64_t)r * p.stride;
+  int64_t rowoff = 0;
+  if (lane < kAttnSplit) {
+    const int64_t phys = bt[tok / kPage];
+    rowoff = ((phys * p.Hkv + g) * kPage + (tok % kPage)) * kHeadDim;
+  }
+
+  const T* kp = static_cast<const T*>(p.k_pool);
+  const T* vp = static_cast<const T*>(p.v_pool);
+  Row8<kBf16> kr[kTokPerRow], vr[kTokPerRow];
+  bool okr[kTokPerRow];
+#pragma unroll
+  for (int t = 0; t < kTokPerRow; ++t) {
+    const int e = row + 4 * t;
+    const int64_t off = __shfl(rowoff, e);
+    okr[t] = __shfl((int)ok, e) != 0;
+    load_row(kr[t], kp + off, col);
+    load_row(vr[t], vp + off, col);
+  }
+
+  // query slices of the group's G heads
+  const T* qb = static_cast<const T*>(p.q) + ((int64_t)r * H + g * G) * kHeadDim;
+  float qf[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    Row8<kBf16> x;
+    load_row(x, qb + h * kHeadDim, col);
+    to_f32(x, qf[h]);
+  }
+
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float a[kTokPerRow];
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < kTokPerRow; ++t) {
+      float kf[8];
+      to_f32(kr[t], kf);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(kf[e], qf[h][e], acc);
+      acc = row_sum16(acc) * p.attn_scale;
+      a[t] = okr[t] ? acc : kNegInf;
+      mx = fmaxf(mx, a[t]);
+    }
+    m[h] = mx;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+    if (mx != kNegInf) {
+#pragma unroll
+      for (int t = 0; t < kTokPerRow; ++t) {
+        const float pw = okr[t] ? exp_via2(a[t] - mx) : 0.f;
+        l[h] += pw;
+        float vf[8];
+        to_f32(vr[t], vf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pw, vf[e], o[h][e]);
+      }
+    }
+  }
+
+  // merge the 4 rows of the wave (partners at lane ^ 16 and lane ^ 32)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int x = 16; x <= 32; x <<= 1) {
+      const float m2 = __shfl_xor(m[h], x);
+      const float l2 = __shfl_xor(l[h], x);
+      const float mn = fmaxf(m[h], m2);
+      const float c1 = (m[h] == kNegInf) ? 0.f : exp_via2(m[h] - mn);
+      const float c2 = (m2 == kNegInf) ? 0.f : exp_via2(m2 - mn);
+      l[h] = l[h] * c1 + l2 * c2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float o2 = __shfl_xor(o[h][e], x);
+        o[h][e] = o[h][e] * c1 + o2 * c2;
+      }
+      m[h] = mn;
+    }
+  }
+  if (row == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float* dst = p.partials + (((int64_t)r * H + g * G + h) * S + s) * (kHeadDim + 2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[lane_dim(kBf16, col, e)] = o[h][e];
+      if (col == 0) {
+        dst[kHeadDim] = m[h];
+        dst[kHeadDim + 1] = l[h];
+      }
+    }
+  }
+}
+
+// One workgroup of d threads per (request, head): merge the work items.
+template <bool kBf16>
+__global__ __launch_bounds__(kHeadDim) void combine_kernel(AttnParams p) {
+  const int S = attn_splits(p.top_k, p.n_local);
+  const int rh = blockIdx.x;
+  const float* base = p.partials + (int64_t)rh * S * (kHeadDim + 2);
+  float M = kNegInf;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, base[s * (kHeadDim + 2) + kHeadDim]);
+  float acc = 0.f, L = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* src = base + s * (kHeadDim + 2);
+    const float ms = src[kHeadDim], ls = src[kHeadDim + 1];
+    if (ms == kNegInf || ls == 0.f) continue;
+    const float c = exp_via2(ms - M);
+    L = fmaf(c, ls, L);
+    acc = fmaf(c, src[threadIdx.x], acc);
+  }
+  const float res = acc / L;
+  if (kBf16)
+    static_cast<uint16_t*>(p.out)[(int64_t)rh * kHeadDim + threadIdx.x] = f32_to_bf16(res);
+  else
+    static_cast<float*>(p.out)[(int64_t)rh * kHeadDim + threadIdx.x] = res;
+}
+
+template <bool kBf16>
+hipError_t launch_attn_t(const AttnParams& p, hipStream_t st) {
+  const int G = p.H / p.Hkv;
+  const int waves = p.b * p.Hkv * attn_splits(p.top_k, p.n_local);
+  dim3 grid((waves + 3) / 4), block(256);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((attn_kernel<kBf16, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((attn_kernel<kBf16, 2>), grid, block, 0, st, p); break;
+    case 3: hipLaunchKernelGGL((attn_kernel<kBf16, 3>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((attn_kernel<kBf16, 4>), grid, block, 0, st, p); break;
+    case 5: hipLaunchKernelGGL((attn_kernel<kBf16, 5>), grid, block, 0, st, p); break;
+    case 6: hipLaunchKernelGGL((attn_kernel<kBf16, 6>), grid, block, 0, st, p); break;
+    case 7: hipLaunchKernelGGL((attn_kernel<kBf16, 7>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((attn_kernel<kBf16, 8>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL(combine_kernel<kBf16>, dim3(p.b * p.H), dim3(kHeadDim), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn(const AttnParams& p, hipStream_t st) {
+  return p.bf16 ? launch_attn_t<true>(p, st) : launch_attn_t<false>(p, st);
+}
+
+}  // namespace ts

@@ -1,0 +1,83 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ts {
+
+// Tokens per vote / top-k tile (one workgroup of 256 threads, 8 tokens each).
+constexpr int kVoteTile = 2048;
+// Radix digits of the top-k select over the 32-bit vote keys, most significant first.
+constexpr int kDigitBits0 = 11, kDigitBits1 = 11, kDigitBits2 = 10;
+constexpr int kHistBins = 1 << 11;
+// Selected tokens per attention work item (one wavefront).
+constexpr int kAttnSplit = 32;
+
+struct ScoreParams {
+  const void* q;              // [b][H][d]
+  const void* k_pool;         // [pages][H_kv][16][d]
+  const int32_t* block_table; // [b][stride]
+  const int32_t* seq_lens;    // [b]
+  const int32_t* skip;        // [b] nonzero: request skipped (cache hit); may be null
+  float* logits;              // ragged [H][N_r] per request
+  float* partials;            // [chunks][H][2] per-chunk (max, sum exp)
+  float* head_stats;          // [b][H][2]
+  int H, Hkv, b, stride;
+  int chunk_pages;            // pages per work unit
+  float score_scale;
+  int bf16;                   // element type of q / pool
+  int grid;                   // workgroups of the score kernel
+};
+
+struct VoteParams {
+  const float* logits;
+  const float* head_stats;    // [b][H][2]
+  const int32_t* seq_lens;
+  const int32_t* skip;
+  float* vote;                // ragged [N_r]
+  uint32_t* hist;             // [b][3][kHistBins]
+  int32_t* state;             // [b][8] select state (digits found, counts left)
+  int32_t* tile_counts;       // [tiles][2] (greater, equal) per tile
+  int32_t* sel_idx;           // [b][top_k]
+  int32_t* sel_count;         // [b]
+  int H, b, top_k;
+  int grid;                   // workgroups of the tile kernels
+};
+
+struct AttnParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* sel_idx;     // [b][top_k] ascending
+  const int32_t* sel_count;   // [b]
+  float* partials;            // [b][H][splits][d + 2]
+  void* out;                  // [b][H][d]
+  int H, Hkv, b, stride, top_k, n_local;
+  float attn_scale;
+  int bf16;
+};
+
+struct CacheParams {
+  const void* q;
+  void* cached_q;
+  int32_t* valid;
+  int32_t* hit;
+  uint32_t* hist;             // zeroed for the requests that reselect
+  int H, d, b;
+  double theta;
+  int bf16;
+};
+
+__host__ __device__ inline int attn_splits(int top_k, int n_local) {
+  return (top_k + kAttnSplit - 1) / kAttnSplit + (n_local + kAttnSplit - 1) / kAttnSplit;
+}
+
+hipError_t launch_score(const ScoreParams& p, hipStream_t s);
+hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist);
+hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+hipError_t launch_cache_check(const CacheParams& p, hipStream_t s);
+
+}  // namespace ts

@@ -1,0 +1,334 @@
+// Steps 3-4 of the decode step: head soft vote and TopK over all N positions.
+//
+// Source: TokenSelect deepnotes page, head soft vote equation: the TopK of the
+// sum over the H query heads of each head's softmax-normalised inner products.
+// Ties (which fp32 underflow makes common: every position whose weights all
+// round to zero votes exactly 0) go to the lower position; the result is written
+// in ascending position order.
+//
+// gfx950 design. The vote is a streaming reduction over the H x N logits (the
+// largest read after the K stream), one workgroup per tile of 2048 positions with
+// 8 positions per thread and coalesced dword loads. Because every vote is >= 0,
+// the fp32 bit pattern orders like the value, so the TopK is a radix select on
+// 32-bit keys, most significant digit first (11, 11, 10 bits). The vote kernel
+// builds the first digit's histogram (LDS, then global atomics); each later pass
+// reads the previous histogram, finds the digit holding the k-th largest key
+// (every workgroup redoes this 2048-bin scan instead of paying a launch), and
+// histograms the next digit of the keys that share the prefix. The last two
+// kernels count, per tile, keys above the exact threshold and keys equal to it,
+// and write positions through a prefix over tiles; equal keys are taken in
+// position order until k is reached, so the result is deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace ts {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerThread = kVoteTile / kThreads;   // 8 positions per thread
+
+__device__ __forceinline__ uint32_t vote_key(float v) { return __float_as_uint(v); }
+
+// Shared tables: token offsets and tile prefix of the ragged batch.
+struct Tables {
+  int64_t tok[kMaxBatch + 1];
+  int32_t tile[kMaxBatch + 1];
+};
+
+__device__ void build_tables(Tables& t, const VoteParams& p) {
+  block_prefix(t.tok, p.b, [&](int r) -> int64_t { return p.seq_lens[r]; });
+  block_prefix(t.tile, p.b, [&](int r) -> int32_t {
+    if (p.skip && p.skip[r]) return 0;
+    return (p.seq_lens[r] + kVoteTile - 1) / kVoteTile;
+  });
+}
+
+// Exclusive prefix over the block's threads (thread order), 256 threads.
+__device__ uint32_t block_excl_scan(uint32_t x, uint32_t* s_w, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc = x;
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) s_w[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += s_w[w];
+  total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+  __syncthreads();
+  return base + inc - x;
+}
+
+// Digit holding the kk-th largest key among the counts in hist[0..kBins) (bins in
+// increasing key order): s_out = {bin, kk - count(keys in higher bins)}.
+// 1 <= kk <= total count is required; exactly one thread finds the crossing.
+template <int kBins>
+__device__ void find_digit(const uint32_t* hist, int kk, int* s_out, uint32_t* s_w) {
+  constexpr int kPer = kBins / kThreads;            // 8 or 4 bins per thread
+  const int hi = kBins - kPer * threadIdx.x;        // thread 0 owns the top bins
+  uint32_t c[kPer];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) { c[e] = hist[hi - 1 - e]; sum += c[e]; }
+  uint32_t total;
+  const uint32_t above = block_excl_scan(sum, s_w, total);
+  if (above < (uint32_t)kk && (uint32_t)kk <= above + sum) {
+    uint32_t acc = above;
+    bool done = false;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (!done && acc + c[e] >= (uint32_t)kk) {
+        s_out[0] = hi - 1 - e;
+        s_out[1] = kk - (int)acc;
+        done = true;
+      }
+      acc += c[e];
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- vote + digit-0 histogram
+__global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
+  __shared__ Tables tb;
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ float s_m[256], s_iz[256];
+  build_tables(tb, p);
+  const int H = p.H;
+  const int total = tb.tile[p.b];
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int r = find_segment(tb.tile, p.b, tile);
+    const int t = tile - tb.tile[r];
+    const int N = p.seq_lens[r];
+    __syncthreads();
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_hist[i] = 0;
+    for (int h = threadIdx.x; h < H; h += kThreads) {
+      s_m[h] = p.head_stats[((int64_t)r * H + h) * 2 + 0];
+      s_iz[h] = 1.0f / p.head_stats[((int64_t)r * H + h) * 2 + 1];
+    }
+    __syncthreads();
+    const int i0 = t * kVoteTile + threadIdx.x;
+    const float* z = p.logits + tb.tok[r] * H;
+    float v[kPerThread];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) v[e] = 0.f;
+#pragma unroll 4
+    for (int h = 0; h < H; ++h) {
+      const float* zh = z + (int64_t)h * N;
+      const float mh = s_m[h], izh = s_iz[h];
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) {
+        const int i = i0 + e * kThreads;
+        if (i < N) v[e] = fmaf(exp_via2(zh[i] - mh), izh, v[e]);
+      }
+    }
+    float* vout = p.vote + tb.tok[r];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = i0 + e * kThreads;
+      if (i < N) {
+        vout[i] = v[e];
+        atomicAdd(&s_hist[vote_key(v[e]) >> (32 - kDigitBits0)], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads)
+      if (s_hist[i]) atomicAdd(&gh[i], s_hist[i]);
+  }
+}
+
+// ---------------------------------------------------------------- digits 1 and 2
+// kPass 1: find digit 0 from hist[0], histogram digit 1 of matching keys into hist[1].
+// kPass 2: read digit 0 from state, find digit 1 from hist[1], histogram digit 2 into hist[2].
+template <int kPass>
+__global__ __launch_bounds__(kThreads) void refine_kernel(VoteParams p) {
+  __shared__ Tables tb;
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ uint32_t s_w[4];
+  __shared__ int s_dig[2];
+  build_tables(tb, p);
+  const int total = tb.tile[p.b];
+  constexpr int kShift = (kPass == 1) ? (32 - kDigitBits0) : (32 - kDigitBits0 - kDigitBits1);
+  constexpr int kNextBits = (kPass == 1) ? kDigitBits1 : kDigitBits2;
+  constexpr int kNextShift = kShift - kNextBits;
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int r = find_segment(tb.tile, p.b, tile);
+    const int t = tile - tb.tile[r];
+    const int N = p.seq_lens[r];
+    if (p.top_k >= N) continue;                       // whole request selected: no radix work
+    int32_t* st = p.state + r * 8;
+    const uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
+    __syncthreads();
+    uint32_t prefix;
+    if (kPass == 1) {
+      find_digit<1 << kDigitBits0>(gh, p.top_k, s_dig, s_w);
+      prefix = (uint32_t)s_dig[0];
+      if (t == 0 && threadIdx.x == 0) { st[0] = s_dig[0]; st[1] = s_dig[1]; }
+    } else {
+      const int d0 = st[0], k0 = st[1];
+      find_digit<1 << kDigitBits1>(gh + kHistBins, k0, s_dig, s_w);
+      prefix = ((uint32_t)d0 << kDigitBits1) | (uint32_t)s_dig[0];
+      if (t == 0 && threadIdx.x == 0) { st[2] = s_dig[0]; st[3] = s_dig[1]; }
+    }
+    for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads) s_hist[i] = 0;
+    __syncthreads();
+    const float* vr = p.vote + tb.tok[r];
+    const int i0 = t * kVoteTile + threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = i0 + e * kThreads;
+      if (i < N) {
+        const uint32_t key = vote_key(vr[i]);
+        if ((key >> kShift) == prefix)
+          atomicAdd(&s_hist[(key >> kNextShift) & ((1u << kNextBits) - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t* gn = p.hist + ((int64_t)r * 3 + kPass) * kHistBins;
+    for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads)
+      if (s_hist[i]) atomicAdd(&gn[i], s_hist[i]);
+  }
+}
+
+// Exact threshold key of request r and how many keys equal to it are taken.
+__device__ void threshold(const VoteParams& p, int r, uint32_t& key_t, int& take_eq,
+                          int* s_dig, uint32_t* s_w, bool record) {
+  int32_t* st = p.state + r * 8;
+  const int d0 = st[0], d1 = st[2], k1 = st[3];
+  find_digit<1 << kDigitBits2>(p.hist + ((int64_t)r * 3 + 2) * kHistBins, k1, s_dig, s_w);
+  key_t = ((uint32_t)d0 << (kDigitBits1 + kDigitBits2)) | ((uint32_t)d1 << kDigitBits2) |
+          (uint32_t)s_dig[0];
+  take_eq = s_dig[1];
+  if (record && threadIdx.x == 0) { st[4] = s_dig[0]; st[5] = s_dig[1]; }
+}
+
+// ---------------------------------------------------------------- per-tile counts
+__global__ __launch_bounds__(kThreads) void count_kernel(VoteParams p) {
+  __shared__ Tables tb;
+  __shared__ uint32_t s_w[4];
+  __shared__ int s_dig[2];
+  __shared__ int s_cnt[2][4];
+  build_tables(tb, p);
+  const int total = tb.tile[p.b];
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int r = find_segment(tb.tile, p.b, tile);
+    const int t = tile - tb.tile[r];
+    const int N = p.seq_lens[r];
+    if (p.top_k >= N) continue;
+    __syncthreads();
+    uint32_t key_t;
+    int take_eq;
+    threshold(p, r, key_t, take_eq, s_dig, s_w, t == 0);
+    const float* vr = p.vote + tb.tok[r];
+    const int i0 = t * kVoteTile + threadIdx.x;
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = i0 + e * kThreads;
+      if (i < N) {
+        const uint32_t key = vote_key(vr[i]);
+        gt += key > key_t;
+        eq += key == key_t;
+      }
+    }
+    gt = wave_sum_i(gt);
+    eq = wave_sum_i(eq);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { s_cnt[0][wave] = gt; s_cnt[1][wave] = eq; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      p.tile_counts[(int64_t)tile * 2 + 0] = s_cnt[0][0] + s_cnt[0][1] + s_cnt[0][2] + s_cnt[0][3];
+      p.tile_counts[(int64_t)tile * 2 + 1] = s_cnt[1][0] + s_cnt[1][1] + s_cnt[1][2] + s_cnt[1][3];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- ascending positions
+__global__ __launch_bounds__(kThreads) void write_kernel(VoteParams p) {
+  __shared__ Tables tb;
+  __shared__ uint32_t s_w[4];
+  __shared__ int s_dig[2];
+  __shared__ int s_before[2][4];
+  build_tables(tb, p);
+  const int total = tb.tile[p.b];
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int r = find_segment(tb.tile, p.b, tile);
+    const int t = tile - tb.tile[r];
+    const int N = p.seq_lens[r];
+    const int k = p.top_k;
+    int32_t* out = p.sel_idx + (int64_t)r * k;
+    if (t == 0 && threadIdx.x == 0) p.sel_count[r] = min(k, N);
+    // this thread owns 8 consecutive positions
+    const int i0 = t * kVoteTile + threadIdx.x * kPerThread;
+    if (k >= N) {
+      for (int e = 0; e < kPerThread; ++e)
+        if (i0 + e < N) out[i0 + e] = i0 + e;
+      continue;
+    }
+    __syncthreads();
+    uint32_t key_t;
+    int take_eq;
+    threshold(p, r, key_t, take_eq, s_dig, s_w, false);
+    // counts of the request's earlier tiles
+    int gtb = 0, eqb = 0;
+    const int first = tb.tile[r];
+    for (int tt = threadIdx.x; tt < t; tt += kThreads) {
+      gtb += p.tile_counts[(int64_t)(first + tt) * 2 + 0];
+      eqb += p.tile_counts[(int64_t)(first + tt) * 2 + 1];
+    }
+    gtb = wave_sum_i(gtb);
+    eqb = wave_sum_i(eqb);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { s_before[0][wave] = gtb; s_before[1][wave] = eqb; }
+    __syncthreads();
+    gtb = s_before[0][0] + s_before[0][1] + s_before[0][2] + s_before[0][3];
+    eqb = s_before[1][0] + s_before[1][1] + s_before[1][2] + s_before[1][3];
+    const float* vr = p.vote + tb.tok[r];
+    uint32_t keys[kPerThread];
+    uint32_t packed = 0;                              // (equal << 16) | greater
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = i0 + e;
+      keys[e] = (i < N) ? vote_key(vr[i]) : 0u;
+      if (i < N) packed += (keys[e] > key_t) ? 1u : ((keys[e] == key_t) ? (1u << 16) : 0u);
+    }
+    uint32_t tot;
+    uint32_t pre = block_excl_scan(packed, s_w, tot);
+    int g_run = gtb + (int)(pre & 0xffffu);
+    int e_run = eqb + (int)(pre >> 16);
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = i0 + e;
+      if (i >= N) break;
+      const bool greater = keys[e] > key_t;
+      const bool equal = keys[e] == key_t;
+      const int pos = g_run + min(e_run, take_eq);
+      if ((greater || (equal && e_run < take_eq)) && pos < k) out[pos] = i;
+      g_run += greater;
+      e_run += equal;
+    }
+  }
+}
+
+__global__ void zero_u32(uint32_t* x, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    x[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist) {
+  if (zero_hist) {
+    const int64_t n = (int64_t)p.b * 3 * kHistBins;
+    hipLaunchKernelGGL(zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.hist, n);
+  }
+  const dim3 grid(p.grid), block(kThreads);
+  hipLaunchKernelGGL(vote_kernel, grid, block, 0, s, p);
+  hipLaunchKernelGGL(refine_kernel<1>, grid, block, 0, s, p);
+  hipLaunchKernelGGL(refine_kernel<2>, grid, block, 0, s, p);
+  hipLaunchKernelGGL(count_kernel, grid, block, 0, s, p);
+  hipLaunchKernelGGL(write_kernel, grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace ts
