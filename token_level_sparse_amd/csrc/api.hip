@@ -172,6 +172,7 @@ ts::AttnParams attn_params(const ts_shape& s, const ts_select& sel, const void* 
   p.sel_idx = sel_idx; p.sel_count = sel_count; p.out = out;
   p.partials = at<float>(ws, L.attn);
   p.H = s.num_q_heads; p.Hkv = s.num_kv_heads; p.b = s.batch; p.stride = s.block_table_stride;
+  p.sel_stride = sel.top_k;
   p.top_k = eff_top_k(s, sel);
   p.n_local = eff_local(s, sel);
   p.attn_scale = sel.attn_scale;
@@ -226,11 +227,8 @@ ts_status tokenselect_sparse_attn(const ts_shape* shape, const ts_select* sel, c
   TS_REQUIRE(q); TS_REQUIRE(k_pool); TS_REQUIRE(v_pool); TS_REQUIRE(block_table);
   TS_REQUIRE(seq_lens); TS_REQUIRE(sel_idx); TS_REQUIRE(sel_count); TS_REQUIRE(out);
   if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
-  ts::AttnParams p = attn_params(*shape, *sel, q, k_pool, v_pool, block_table, seq_lens, sel_idx,
-                                 sel_count, out, ws);
-  p.top_k = sel->top_k;        // row stride of the caller's sel_idx
-  if (sel->top_k > shape->max_total_tokens)
-    return fail(TS_ERR_INVALID_ARG, "top_k %d > max_total_tokens for sparse_attn", sel->top_k);
+  const ts::AttnParams p = attn_params(*shape, *sel, q, k_pool, v_pool, block_table, seq_lens,
+                                       sel_idx, sel_count, out, ws);
   return device_status(ts::launch_attn(p, stream), "sparse attention launch");
 }
 
@@ -245,8 +243,6 @@ ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel, c
   TS_REQUIRE(seq_lens); TS_REQUIRE(cache); TS_REQUIRE(hit); TS_REQUIRE(out);
   TS_REQUIRE(cache->cached_q); TS_REQUIRE(cache->cached_idx); TS_REQUIRE(cache->cached_count);
   TS_REQUIRE(cache->valid);
-  if (sel->top_k > shape->max_total_tokens)
-    return fail(TS_ERR_INVALID_ARG, "top_k %d > max_total_tokens", sel->top_k);
   if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
   const Layout L = layout(*shape, *sel);
   float* logits = at<float>(ws, L.logits);
@@ -268,9 +264,8 @@ ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel, c
   if ((st = device_status(ts::launch_vote_topk(vp, stream, false), "vote/top-k launch")) != TS_OK)
     return st;
 
-  ts::AttnParams ap = attn_params(*shape, *sel, q, k_pool, v_pool, block_table, seq_lens,
-                                  cache->cached_idx, cache->cached_count, out, ws);
-  ap.top_k = sel->top_k;
+  const ts::AttnParams ap = attn_params(*shape, *sel, q, k_pool, v_pool, block_table, seq_lens,
+                                        cache->cached_idx, cache->cached_count, out, ws);
   return device_status(ts::launch_attn(ap, stream), "sparse attention launch");
 }
 

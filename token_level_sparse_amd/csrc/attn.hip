@@ -75,8 +75,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   if (lane < kAttnSplit) {
     if (s < nT) {
       const int e = s * kAttnSplit + lane;
-      if (e < min(p.sel_count[r], p.top_k)) {
-        tok = p.sel_idx[(int64_t)r * p.top_k + e];
+      if (e < min(p.sel_count[r], p.sel_stride)) {
+        tok = p.sel_idx[(int64_t)r * p.sel_stride + e];
         ok = tok >= 0 && tok < lstart;
       }
     } else {

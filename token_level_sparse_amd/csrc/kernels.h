@@ -55,7 +55,9 @@ struct AttnParams {
   const int32_t* sel_count;   // [b]
   float* partials;            // [b][H][splits][d + 2]
   void* out;                  // [b][H][d]
-  int H, Hkv, b, stride, top_k, n_local;
+  int H, Hkv, b, stride;
+  int sel_stride;             // int32 entries per sel_idx row (the caller's top_k)
+  int top_k, n_local;         // min(top_k, max tokens), min(n_local, max tokens): work items
   float attn_scale;
   int bf16;
 };
