@@ -50,7 +50,8 @@
  *   off_r = N_0 + ... + N_{r-1} (computed on the device from seq_lens).
  *   logits     fp32: request r, query head h, token i at off_r * H + h * N_r + i.
  *   head_stats fp32 [batch][H][2]: (M_h, Z_h) = (max_i z, sum_i exp(z - M_h)).
- *   vote       fp32: request r, token i at off_r + i.
+ *   vote       fp32 log2 of the head soft vote, log2 v_i: request r, token i at
+ *              off_r + i (finite where the linear vote would underflow fp32).
  *   sel_idx    int32 [batch][top_k]: the TopK positions of request r, ascending,
  *              in the first sel_count[r] = min(top_k, N_r) entries.
  *   out        [batch][H][d] element type `dtype` (bf16 results are rounded to
@@ -125,11 +126,13 @@ ts_status tokenselect_score(const ts_shape* shape, const ts_select* sel,
                             float* logits, float* head_stats,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Steps 3-4 (TopK part). Head soft vote v_i = sum_h exp(z[h][i] - M_h) / Z_h and
-   TopK over all N_r positions: the k largest votes, ties to the lower position,
-   written ascending to sel_idx[r][0 .. sel_count[r]) with sel_count[r] =
-   min(top_k, N_r). `vote` (max_total_tokens floats) may be NULL; then the votes
-   stay in the workspace. The local window is not written: step 5 adds it. */
+/* Steps 3-4 (TopK part). Head soft vote v_i = sum_h exp(z[h][i] - M_h) / Z_h
+   (deepnotes head soft vote equation), computed as lv_i = log2 v_i by a
+   log-sum-exp over the heads, and TopK over all N_r positions: the k largest
+   votes (largest lv), ties to the lower position, written ascending to
+   sel_idx[r][0 .. sel_count[r]) with sel_count[r] = min(top_k, N_r). `vote`
+   (max_total_tokens floats) receives lv and may be NULL; then lv stays in the
+   workspace. The local window is not written: step 5 adds it. */
 ts_status tokenselect_vote_topk(const ts_shape* shape, const ts_select* sel,
                                 const float* logits, const float* head_stats,
                                 const int32_t* seq_lens, float* vote,

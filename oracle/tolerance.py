@@ -88,3 +88,56 @@ def attn_budget(q, K, V, S, attn_scale: float, out) -> np.ndarray:
         c = 4.0 * U32 * (A + np.abs(a) + np.abs(a.max()))
         b[h] = (w * c) @ np.abs(Vs - out[h][None, :])
     return b
+
+
+# ---------------------------------------------------------------- log-domain votes
+# A GPU path that keeps the vote as lv = log2(v) does not underflow, so its votes
+# are compared in the log domain with a relative budget and no underflow term.
+LN2 = 0.6931471805599453
+
+
+def vote_rel_budget(q, K, z, p, M, v, score_scale: float = 1.0) -> np.ndarray:
+    """r_i = 4u * sum_h p_h(i) (|z_hi| + |M_h| + score_scale A_hi) / v_i (inf where v_i == 0)."""
+    A = abs_dot(q, K)
+    t = (p * (np.abs(z) + np.abs(M)[:, None] + abs(score_scale) * A)).sum(axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(v > 0, 4.0 * U32 * t / np.where(v > 0, v, 1.0), np.inf)
+    return r
+
+
+def log_vote_within(lv2_gpu, v_ora, rel, rel_tol: float = 1e-4):
+    """Band (a) in the log domain: |lv2 ln2 - ln v| <= rel_tol + r_i + 4u |lv2 ln2|.
+
+    Where the fp64 vote underflows to 0 the GPU's log2 vote must lie below -1000.
+    Returns (ok mask, excess).
+    """
+    lg = np.asarray(lv2_gpu, dtype=np.float64) * LN2
+    v = np.asarray(v_ora, dtype=np.float64)
+    pos = v > 0
+    with np.errstate(divide="ignore"):
+        lo = np.where(pos, np.log(np.where(pos, v, 1.0)), -np.inf)
+    lim = rel_tol + np.where(np.isfinite(rel), rel, 0.0) + 4.0 * U32 * np.abs(lg)
+    err = np.where(pos, np.abs(lg - lo), 0.0)
+    ok = np.where(pos, err <= lim, lv2_gpu < -1000.0)
+    return ok, np.where(pos, err - lim, 0.0)
+
+
+def ambiguous_positions_log(v_ora, rel, k: int, rel_tol: float = 1e-4) -> np.ndarray:
+    """Band (b) in the log domain: |ln v_i - ln v_k| <= rel_tol + r_i + r_k + 4u(|ln v_i| + |ln v_k|).
+
+    v_k is the oracle's k-th largest vote. If it underflowed to 0, every zero vote
+    ties with it.
+    """
+    v = np.asarray(v_ora, dtype=np.float64)
+    N = v.shape[0]
+    if k >= N:
+        return np.zeros(N, dtype=bool)
+    order = np.lexsort((np.arange(N), -v))
+    kth = order[k - 1]
+    if v[kth] == 0.0:
+        return v == 0.0
+    with np.errstate(divide="ignore"):
+        lv = np.where(v > 0, np.log(np.where(v > 0, v, 1.0)), -np.inf)
+    r = np.where(np.isfinite(rel), rel, 0.0)
+    lim = rel_tol + r + r[kth] + 4.0 * U32 * (np.abs(lv) + abs(lv[kth]))
+    return (v > 0) & (np.abs(lv - lv[kth]) <= lim)

@@ -2,11 +2,12 @@
 
 Comparison bands (fp32 arithmetic on the GPU against the fp64 oracle):
   logits   |z_gpu - z_ora| <= 16 u * score_scale * sum_d |q_d k_d| + 1e-30
-  (a) vote |v_gpu - v_ora| <= 1e-4 v_ora + e_i  (e_i: oracle first-order fp32 budget)
+  (a) vote the GPU returns lv = log2(v) in fp32; |lv ln2 - ln v_ora| <= 1e-4 + r_i +
+      4u |lv ln2|, r_i = e_i / v_i the oracle's first-order relative fp32 budget
   (b) TopK the GPU set differs from the oracle set only at positions whose oracle
-      vote is within tolerance of the k-th vote; and, with the decision taken in
-      the GPU's own precision, it is exactly the TopK of the GPU's fp32 votes
-      (ties to the lower position)
+      vote is within that relative tolerance of the k-th vote; and, with the
+      decision taken in the GPU's own precision, it is exactly the TopK of the
+      GPU's fp32 log2 votes (ties to the lower position)
   (c) out  max-abs <= 1e-4 (fp32; plus the attention budget) or 2e-2 (bf16)
       against the oracle's attention over the GPU's own selected set
 """
@@ -116,23 +117,25 @@ def check_stats(stats_gpu, sel_ora, q, K, score_scale=1.0):
         assert abs(Z - sel_ora["Z"][h]) <= 1e-4 * sel_ora["Z"][h] + bz * sel_ora["Z"][h], (h, Z, sel_ora["Z"][h])
 
 
-def check_vote(v_gpu, sel_ora, q, K, score_scale=1.0, factor=4.0):
-    budget = tol.vote_budget(q, K, sel_ora["z"], sel_ora["p"], sel_ora["M"], score_scale) * (factor / 4.0)
-    ok, excess = tol.vote_within(v_gpu, sel_ora["vote"], budget)
-    strict = np.abs(v_gpu - sel_ora["vote"]) <= 1e-4 * sel_ora["vote"]
+def check_vote(lv_gpu, sel_ora, q, K, score_scale=1.0):
+    rel = tol.vote_rel_budget(q, K, sel_ora["z"], sel_ora["p"], sel_ora["M"], sel_ora["vote"],
+                              score_scale)
+    ok, excess = tol.log_vote_within(lv_gpu, sel_ora["vote"], rel)
     assert ok.all(), f"vote: {(~ok).sum()} outside band (a), worst excess {excess.max():.3e}"
-    return budget, int((~strict).sum())
+    v = sel_ora["vote"]
+    strict = np.abs(np.exp2(lv_gpu.astype(np.float64)) - v) <= 1e-4 * v
+    return rel, int((~strict).sum())
 
 
-def check_topk(T_gpu, v_gpu, sel_ora, budget, k):
-    N = len(v_gpu)
+def check_topk(T_gpu, lv_gpu, sel_ora, rel, k):
+    N = len(lv_gpu)
     assert np.all(np.diff(T_gpu) > 0), "TopK not strictly ascending"
     assert len(T_gpu) == min(k, N)
     assert T_gpu.min() >= 0 and T_gpu.max() < N
-    # the decision in the GPU's own precision: exact TopK of the fp32 votes
-    exact = ora.topk_indices(v_gpu.astype(np.float64), k)
+    # the decision in the GPU's own precision: exact TopK of its fp32 log2 votes
+    exact = ora.topk_indices(lv_gpu.astype(np.float64), k)
     assert np.array_equal(T_gpu, exact), "TopK differs from the exact TopK of the GPU votes"
-    amb = tol.ambiguous_positions(sel_ora["vote"], budget, k)
+    amb = tol.ambiguous_positions_log(sel_ora["vote"], rel, k)
     diff = np.setxor1d(T_gpu, sel_ora["T"])
     assert np.all(amb[diff]), f"TopK differs from the oracle outside band (b) at {diff[~amb[diff]][:10]}"
     return len(diff)
@@ -158,8 +161,8 @@ def check_request(po: PathOut, r: int, req: wl.Request, geo: wl.Geometry, top_k=
     sel = ora.select(q, K, k, score_scale)
     check_logits(po.logits[r], q, K, sel["z"], score_scale)
     check_stats(po.stats[r], sel, q, K, score_scale)
-    budget, n_loose = check_vote(po.vote[r], sel, q, K, score_scale)
-    n_diff = check_topk(po.T[r], po.vote[r], sel, budget, k)
+    rel, n_loose = check_vote(po.vote[r], sel, q, K, score_scale)
+    n_diff = check_topk(po.T[r], po.vote[r], sel, rel, k)
     err = check_attention(po.out[r], q, K, V, po.T[r], K.shape[1], L, geo.attn_scale,
                           geo.dtype == "f32")
     return dict(n_loose=n_loose, n_diff=n_diff, attn_err=err)

@@ -62,8 +62,9 @@ def compare(geo, req, qs, lens, hits, T, outs, theta, band_steps=24):
             last_miss_T = T[t]
             if checked < band_steps:
                 sel = ora.select(q_all[t], K[:, :N], geo.top_k)
-                budget = gh.tol.vote_budget(q_all[t], K[:, :N], sel["z"], sel["p"], sel["M"])
-                amb = gh.tol.ambiguous_positions(sel["vote"], budget, geo.top_k)
+                rel = gh.tol.vote_rel_budget(q_all[t], K[:, :N], sel["z"], sel["p"], sel["M"],
+                                             sel["vote"])
+                amb = gh.tol.ambiguous_positions_log(sel["vote"], rel, geo.top_k)
                 diff = np.setxor1d(T[t], sel["T"])
                 assert np.all(amb[diff]), (t, diff[~amb[diff]][:10])
                 checked += 1

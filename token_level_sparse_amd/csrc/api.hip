@@ -118,6 +118,14 @@ ts_status check_ws(const ts_shape& s, const ts_select& sel, const void* ws, size
 #define TS_REQUIRE(ptr) \
   do { if (!(ptr)) return fail(TS_ERR_INVALID_ARG, "%s must not be NULL", #ptr); } while (0)
 
+// The kernels read q, the pools and the cached query with 16-byte loads.
+#define TS_REQUIRE16(ptr)                                                                 \
+  do {                                                                                    \
+    if (!(ptr)) return fail(TS_ERR_INVALID_ARG, "%s must not be NULL", #ptr);             \
+    if (reinterpret_cast<uintptr_t>(ptr) % 16)                                            \
+      return fail(TS_ERR_INVALID_ARG, "%s must be 16-byte aligned", #ptr);               \
+  } while (0)
+
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
@@ -195,7 +203,7 @@ ts_status tokenselect_score(const ts_shape* shape, const ts_select* sel, const v
                             void* ws, size_t ws_bytes, hipStream_t stream) {
   ts_status st = check_shape(shape, sel);
   if (st != TS_OK) return st;
-  TS_REQUIRE(q); TS_REQUIRE(k_pool); TS_REQUIRE(block_table); TS_REQUIRE(seq_lens);
+  TS_REQUIRE16(q); TS_REQUIRE16(k_pool); TS_REQUIRE(block_table); TS_REQUIRE(seq_lens);
   TS_REQUIRE(logits); TS_REQUIRE(head_stats);
   if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
   const ts::ScoreParams p = score_params(*shape, *sel, q, k_pool, block_table, seq_lens, nullptr,
@@ -224,7 +232,7 @@ ts_status tokenselect_sparse_attn(const ts_shape* shape, const ts_select* sel, c
                                   void* ws, size_t ws_bytes, hipStream_t stream) {
   ts_status st = check_shape(shape, sel);
   if (st != TS_OK) return st;
-  TS_REQUIRE(q); TS_REQUIRE(k_pool); TS_REQUIRE(v_pool); TS_REQUIRE(block_table);
+  TS_REQUIRE16(q); TS_REQUIRE16(k_pool); TS_REQUIRE16(v_pool); TS_REQUIRE(block_table);
   TS_REQUIRE(seq_lens); TS_REQUIRE(sel_idx); TS_REQUIRE(sel_count); TS_REQUIRE(out);
   if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
   const ts::AttnParams p = attn_params(*shape, *sel, q, k_pool, v_pool, block_table, seq_lens,
@@ -239,9 +247,9 @@ ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel, c
                                   size_t ws_bytes, hipStream_t stream) {
   ts_status st = check_shape(shape, sel);
   if (st != TS_OK) return st;
-  TS_REQUIRE(q); TS_REQUIRE(k_pool); TS_REQUIRE(v_pool); TS_REQUIRE(block_table);
+  TS_REQUIRE16(q); TS_REQUIRE16(k_pool); TS_REQUIRE16(v_pool); TS_REQUIRE(block_table);
   TS_REQUIRE(seq_lens); TS_REQUIRE(cache); TS_REQUIRE(hit); TS_REQUIRE(out);
-  TS_REQUIRE(cache->cached_q); TS_REQUIRE(cache->cached_idx); TS_REQUIRE(cache->cached_count);
+  TS_REQUIRE16(cache->cached_q); TS_REQUIRE(cache->cached_idx); TS_REQUIRE(cache->cached_count);
   TS_REQUIRE(cache->valid);
   if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
   const Layout L = layout(*shape, *sel);

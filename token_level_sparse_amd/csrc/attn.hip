@@ -181,28 +181,51 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   }
 }
 
-// One workgroup of d threads per (request, head): merge the work items.
+// One workgroup of d threads per (request, head): merge the work items. The
+// per-item weights exp(m_s - M) are computed once per item by spread threads and
+// kept in LDS; each thread (one output dim) then sums its column with
+// independent loads.
+constexpr int kCombineChunk = 1024;
+
 template <bool kBf16>
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(AttnParams p) {
+  __shared__ float s_w[kCombineChunk];
+  __shared__ float s_red[2];
   const int S = attn_splits(p.top_k, p.n_local);
   const int rh = blockIdx.x;
+  const int tid = threadIdx.x;
   const float* base = p.partials + (int64_t)rh * S * (kHeadDim + 2);
   float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, base[s * (kHeadDim + 2) + kHeadDim]);
+  for (int s = tid; s < S; s += kHeadDim) M = fmaxf(M, base[s * (kHeadDim + 2) + kHeadDim]);
+  M = wave_max(M);
+  if ((tid & 63) == 0) s_red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(s_red[0], s_red[1]);
   float acc = 0.f, L = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float* src = base + s * (kHeadDim + 2);
-    const float ms = src[kHeadDim], ls = src[kHeadDim + 1];
-    if (ms == kNegInf || ls == 0.f) continue;
-    const float c = exp_via2(ms - M);
-    L = fmaf(c, ls, L);
-    acc = fmaf(c, src[threadIdx.x], acc);
+  for (int c0 = 0; c0 < S; c0 += kCombineChunk) {
+    const int n = min(kCombineChunk, S - c0);
+    __syncthreads();
+    for (int j = tid; j < n; j += kHeadDim) {
+      const float* src = base + (c0 + j) * (kHeadDim + 2);
+      const float ms = src[kHeadDim], ls = src[kHeadDim + 1];
+      const float w = (ms == kNegInf || ls == 0.f) ? 0.f : exp_via2(ms - M);
+      s_w[j] = w;
+      L = fmaf(w, ls, L);
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int j = 0; j < n; ++j) acc = fmaf(s_w[j], base[(c0 + j) * (kHeadDim + 2) + tid], acc);
   }
+  L = wave_sum(L);
+  __syncthreads();
+  if ((tid & 63) == 0) s_red[tid >> 6] = L;
+  __syncthreads();
+  L = s_red[0] + s_red[1];
   const float res = acc / L;
   if (kBf16)
-    static_cast<uint16_t*>(p.out)[(int64_t)rh * kHeadDim + threadIdx.x] = f32_to_bf16(res);
+    static_cast<uint16_t*>(p.out)[(int64_t)rh * kHeadDim + tid] = f32_to_bf16(res);
   else
-    static_cast<float*>(p.out)[(int64_t)rh * kHeadDim + threadIdx.x] = res;
+    static_cast<float*>(p.out)[(int64_t)rh * kHeadDim + tid] = res;
 }
 
 template <bool kBf16>

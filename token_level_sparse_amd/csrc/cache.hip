@@ -19,26 +19,49 @@
 namespace ts {
 namespace {
 
-template <bool kBf16>
-__device__ __forceinline__ double elem(const void* base, int64_t i) {
-  if (kBf16) return (double)__uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[i] << 16);
-  return (double)static_cast<const float*>(base)[i];
-}
+// 16-byte chunk of the concatenated query: 8 bf16 or 4 fp32 elements.
+template <bool kBf16> struct Chunk;
+template <> struct Chunk<true> {
+  static constexpr int kElems = 8;
+  static __device__ __forceinline__ void get(const void* base, int64_t chunk, double (&x)[8]) {
+    const uint4 w = static_cast<const uint4*>(base)[chunk];
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = (double)bf16_lo(v[e]);
+      x[2 * e + 1] = (double)bf16_hi(v[e]);
+    }
+  }
+};
+template <> struct Chunk<false> {
+  static constexpr int kElems = 4;
+  static __device__ __forceinline__ void get(const void* base, int64_t chunk, double (&x)[8]) {
+    const float4 w = static_cast<const float4*>(base)[chunk];
+    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+  }
+};
 
 template <bool kBf16>
 __global__ __launch_bounds__(256) void cache_check_kernel(CacheParams p) {
   __shared__ double s_part[3][4];
   __shared__ int s_hit;
+  using C = Chunk<kBf16>;
   const int r = blockIdx.x;
-  const int64_t n = (int64_t)p.H * p.d;
-  const int64_t base = (int64_t)r * n;
+  const int64_t n = (int64_t)p.H * p.d;            // multiple of 128
+  const int64_t nchunks = n / C::kElems;
+  const int64_t cbase = (int64_t)r * nchunks;
   double dot = 0.0, qq = 0.0, cc = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-    const double a = elem<kBf16>(p.q, base + i);
-    const double c = elem<kBf16>(p.cached_q, base + i);
-    dot = fma(a, c, dot);
-    qq = fma(a, a, qq);
-    cc = fma(c, c, cc);
+#pragma unroll 2
+  for (int64_t j = threadIdx.x; j < nchunks; j += blockDim.x) {
+    double a[8], c[8];
+    C::get(p.q, cbase + j, a);
+    C::get(p.cached_q, cbase + j, c);
+#pragma unroll
+    for (int e = 0; e < C::kElems; ++e) {
+      dot = fma(a[e], c[e], dot);
+      qq = fma(a[e], a[e], qq);
+      cc = fma(c[e], c[e], cc);
+    }
   }
   dot = wave_sum_d(dot);
   qq = wave_sum_d(qq);
@@ -57,15 +80,9 @@ __global__ __launch_bounds__(256) void cache_check_kernel(CacheParams p) {
   }
   __syncthreads();
   if (s_hit) return;
-  if (kBf16) {
-    const uint16_t* src = static_cast<const uint16_t*>(p.q) + base;
-    uint16_t* dst = static_cast<uint16_t*>(p.cached_q) + base;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
-  } else {
-    const float* src = static_cast<const float*>(p.q) + base;
-    float* dst = static_cast<float*>(p.cached_q) + base;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
-  }
+  const uint4* src = static_cast<const uint4*>(p.q) + cbase;
+  uint4* dst = static_cast<uint4*>(p.cached_q) + cbase;
+  for (int64_t j = threadIdx.x; j < nchunks; j += blockDim.x) dst[j] = src[j];
   uint32_t* h = p.hist + (int64_t)r * 3 * kHistBins;
   for (int i = threadIdx.x; i < 3 * kHistBins; i += blockDim.x) h[i] = 0u;
   if (threadIdx.x == 0) p.valid[r] = 1;

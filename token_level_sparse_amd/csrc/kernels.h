@@ -6,8 +6,8 @@
 
 namespace ts {
 
-// Tokens per vote / top-k tile (one workgroup of 256 threads, 8 tokens each).
-constexpr int kVoteTile = 2048;
+// Tokens per vote / top-k tile (one workgroup of 256 threads, 4 tokens each).
+constexpr int kVoteTile = 1024;
 // Radix digits of the top-k select over the 32-bit vote keys, most significant first.
 constexpr int kDigitBits0 = 11, kDigitBits1 = 11, kDigitBits2 = 10;
 constexpr int kHistBins = 1 << 11;

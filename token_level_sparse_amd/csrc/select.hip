@@ -2,22 +2,29 @@
 //
 // Source: TokenSelect deepnotes page, head soft vote equation: the TopK of the
 // sum over the H query heads of each head's softmax-normalised inner products.
-// Ties (which fp32 underflow makes common: every position whose weights all
-// round to zero votes exactly 0) go to the lower position; the result is written
-// in ascending position order.
+// Ties go to the lower position; the result is written in ascending position
+// order.
 //
-// gfx950 design. The vote is a streaming reduction over the H x N logits (the
-// largest read after the K stream), one workgroup per tile of 2048 positions with
-// 8 positions per thread and coalesced dword loads. Because every vote is >= 0,
-// the fp32 bit pattern orders like the value, so the TopK is a radix select on
-// 32-bit keys, most significant digit first (11, 11, 10 bits). The vote kernel
-// builds the first digit's histogram (LDS, then global atomics); each later pass
-// reads the previous histogram, finds the digit holding the k-th largest key
-// (every workgroup redoes this 2048-bin scan instead of paying a launch), and
-// histograms the next digit of the keys that share the prefix. The last two
-// kernels count, per tile, keys above the exact threshold and keys equal to it,
-// and write positions through a prefix over tiles; equal keys are taken in
-// position order until k is reached, so the result is deterministic.
+// gfx950 design.
+// * The vote is kept in the log2 domain: lv_i = log2 sum_h 2^(x_hi) with
+//   x_hi = (z_hi - M_h) log2(e) - log2(Z_h), accumulated by an online
+//   log-sum-exp over the heads. The TopK of lv equals the TopK of the vote (log
+//   is monotone), and lv stays finite where the linear fp32 vote would underflow
+//   to 0 (any token whose every head weight is below 2^-126), so tiny votes keep
+//   their order instead of tying at zero.
+// * The vote kernel streams the H x N logits (the largest read after the K
+//   stream) in tiles of 1024 positions, 4 per thread, with coalesced dword loads
+//   issued unconditionally (the last tile clamps its addresses), so every
+//   thread keeps 32 loads in flight.
+// * TopK is a radix select on the order-preserving 32-bit key of lv, most
+//   significant digit first (11, 11, 10 bits). The vote kernel builds the first
+//   digit's histogram (LDS, then global atomics); each later pass reads the
+//   previous histogram, finds the digit holding the k-th largest key (every
+//   workgroup redoes this scan instead of paying a launch), and histograms the
+//   next digit of the keys sharing the prefix. The last two kernels count, per
+//   tile, keys above the exact threshold and keys equal to it, and write
+//   positions through a prefix over tiles; equal keys are taken in position
+//   order until k is reached, so the result is deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,11 +32,15 @@ namespace ts {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = kVoteTile / kThreads;   // 8 positions per thread
+constexpr int kPerThread = kVoteTile / kThreads;   // positions per thread
+constexpr float kLog2eF = 1.4426950408889634f;
 
-__device__ __forceinline__ uint32_t vote_key(float v) { return __float_as_uint(v); }
+// Order-preserving map of an fp32 value to uint32 (larger value, larger key).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
-// Shared tables: token offsets and tile prefix of the ragged batch.
 struct Tables {
   int64_t tok[kMaxBatch + 1];
   int32_t tile[kMaxBatch + 1];
@@ -44,7 +55,7 @@ __device__ void build_tables(Tables& t, const VoteParams& p) {
 }
 
 // Exclusive prefix over the block's threads (thread order), 256 threads.
-__device__ uint32_t block_excl_scan(uint32_t x, uint32_t* s_w, uint32_t& total) {
+__device__ uint32_t block_excl_scan(uint32_t x, uint32_t* s_w) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t inc = x;
   for (int o = 1; o < 64; o <<= 1) {
@@ -55,7 +66,6 @@ __device__ uint32_t block_excl_scan(uint32_t x, uint32_t* s_w, uint32_t& total) 
   __syncthreads();
   uint32_t base = 0;
   for (int w = 0; w < wave; ++w) base += s_w[w];
-  total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
   __syncthreads();
   return base + inc - x;
 }
@@ -71,8 +81,7 @@ __device__ void find_digit(const uint32_t* hist, int kk, int* s_out, uint32_t* s
   uint32_t sum = 0;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) { c[e] = hist[hi - 1 - e]; sum += c[e]; }
-  uint32_t total;
-  const uint32_t above = block_excl_scan(sum, s_w, total);
+  const uint32_t above = block_excl_scan(sum, s_w);
   if (above < (uint32_t)kk && (uint32_t)kk <= above + sum) {
     uint32_t acc = above;
     bool done = false;
@@ -89,11 +98,21 @@ __device__ void find_digit(const uint32_t* hist, int kk, int* s_out, uint32_t* s
   __syncthreads();
 }
 
+// Keys of this thread's positions i0 + e * kThreads (clamped addresses; positions
+// past N get key 0, below every real key).
+__device__ __forceinline__ void load_keys(const float* lv, int i0, int N, uint32_t (&key)[kPerThread]) {
+  float x[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) x[e] = lv[min(i0 + e * kThreads, N - 1)];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) key[e] = (i0 + e * kThreads < N) ? order_key(x[e]) : 0u;
+}
+
 // ---------------------------------------------------------------- vote + digit-0 histogram
 __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
   __shared__ Tables tb;
   __shared__ uint32_t s_hist[kHistBins];
-  __shared__ float s_m[256], s_iz[256];
+  __shared__ float s_m[256], s_l[256];
   build_tables(tb, p);
   const int H = p.H;
   const int total = tb.tile[p.b];
@@ -103,24 +122,32 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
     const int N = p.seq_lens[r];
     __syncthreads();
     for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_hist[i] = 0;
+    // x_hi = (z_hi - M_h) log2e - log2 Z_h; z - M is exact near the head maximum
     for (int h = threadIdx.x; h < H; h += kThreads) {
       s_m[h] = p.head_stats[((int64_t)r * H + h) * 2 + 0];
-      s_iz[h] = 1.0f / p.head_stats[((int64_t)r * H + h) * 2 + 1];
+      s_l[h] = __builtin_amdgcn_logf(p.head_stats[((int64_t)r * H + h) * 2 + 1]);
     }
     __syncthreads();
     const int i0 = t * kVoteTile + threadIdx.x;
     const float* z = p.logits + tb.tok[r] * H;
-    float v[kPerThread];
+    int idx[kPerThread];
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) v[e] = 0.f;
-#pragma unroll 4
+    for (int e = 0; e < kPerThread; ++e) idx[e] = min(i0 + e * kThreads, N - 1);
+    float m[kPerThread], s[kPerThread];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) { m[e] = kNegInf; s[e] = 0.f; }
+#pragma unroll 8
     for (int h = 0; h < H; ++h) {
       const float* zh = z + (int64_t)h * N;
-      const float mh = s_m[h], izh = s_iz[h];
+      const float mh = s_m[h], lh = s_l[h];
 #pragma unroll
       for (int e = 0; e < kPerThread; ++e) {
-        const int i = i0 + e * kThreads;
-        if (i < N) v[e] = fmaf(exp_via2(zh[i] - mh), izh, v[e]);
+        const float x = fmaf(zh[idx[e]] - mh, kLog2eF, -lh);
+        // online log-sum-exp in base 2, one exp per term
+        const float d = x - m[e];
+        const float w = fast_exp2(-fabsf(d));
+        s[e] = (d > 0.f) ? fmaf(s[e], w, 1.f) : s[e] + w;
+        m[e] = fmaxf(m[e], x);
       }
     }
     float* vout = p.vote + tb.tok[r];
@@ -128,8 +155,9 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
     for (int e = 0; e < kPerThread; ++e) {
       const int i = i0 + e * kThreads;
       if (i < N) {
-        vout[i] = v[e];
-        atomicAdd(&s_hist[vote_key(v[e]) >> (32 - kDigitBits0)], 1u);
+        const float lv = m[e] + __builtin_amdgcn_logf(s[e]);
+        vout[i] = lv;
+        atomicAdd(&s_hist[order_key(lv) >> (32 - kDigitBits0)], 1u);
       }
     }
     __syncthreads();
@@ -160,6 +188,9 @@ __global__ __launch_bounds__(kThreads) void refine_kernel(VoteParams p) {
     if (p.top_k >= N) continue;                       // whole request selected: no radix work
     int32_t* st = p.state + r * 8;
     const uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
+    const int i0 = t * kVoteTile + threadIdx.x;
+    uint32_t key[kPerThread];
+    load_keys(p.vote + tb.tok[r], i0, N, key);
     __syncthreads();
     uint32_t prefix;
     if (kPass == 1) {
@@ -174,16 +205,10 @@ __global__ __launch_bounds__(kThreads) void refine_kernel(VoteParams p) {
     }
     for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads) s_hist[i] = 0;
     __syncthreads();
-    const float* vr = p.vote + tb.tok[r];
-    const int i0 = t * kVoteTile + threadIdx.x;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      const int i = i0 + e * kThreads;
-      if (i < N) {
-        const uint32_t key = vote_key(vr[i]);
-        if ((key >> kShift) == prefix)
-          atomicAdd(&s_hist[(key >> kNextShift) & ((1u << kNextBits) - 1)], 1u);
-      }
+      if (i0 + e * kThreads < N && (key[e] >> kShift) == prefix)
+        atomicAdd(&s_hist[(key[e] >> kNextShift) & ((1u << kNextBits) - 1)], 1u);
     }
     __syncthreads();
     uint32_t* gn = p.hist + ((int64_t)r * 3 + kPass) * kHistBins;
@@ -217,21 +242,19 @@ __global__ __launch_bounds__(kThreads) void count_kernel(VoteParams p) {
     const int t = tile - tb.tile[r];
     const int N = p.seq_lens[r];
     if (p.top_k >= N) continue;
+    const int i0 = t * kVoteTile + threadIdx.x;
+    uint32_t key[kPerThread];
+    load_keys(p.vote + tb.tok[r], i0, N, key);
     __syncthreads();
     uint32_t key_t;
     int take_eq;
     threshold(p, r, key_t, take_eq, s_dig, s_w, t == 0);
-    const float* vr = p.vote + tb.tok[r];
-    const int i0 = t * kVoteTile + threadIdx.x;
     int gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      const int i = i0 + e * kThreads;
-      if (i < N) {
-        const uint32_t key = vote_key(vr[i]);
-        gt += key > key_t;
-        eq += key == key_t;
-      }
+      const bool in = i0 + e * kThreads < N;
+      gt += in && key[e] > key_t;
+      eq += in && key[e] == key_t;
     }
     gt = wave_sum_i(gt);
     eq = wave_sum_i(eq);
@@ -260,17 +283,17 @@ __global__ __launch_bounds__(kThreads) void write_kernel(VoteParams p) {
     const int k = p.top_k;
     int32_t* out = p.sel_idx + (int64_t)r * k;
     if (t == 0 && threadIdx.x == 0) p.sel_count[r] = min(k, N);
-    // this thread owns 8 consecutive positions
+    // this thread owns kPerThread consecutive positions
     const int i0 = t * kVoteTile + threadIdx.x * kPerThread;
     if (k >= N) {
       for (int e = 0; e < kPerThread; ++e)
         if (i0 + e < N) out[i0 + e] = i0 + e;
       continue;
     }
-    __syncthreads();
-    uint32_t key_t;
-    int take_eq;
-    threshold(p, r, key_t, take_eq, s_dig, s_w, false);
+    const float* lv = p.vote + tb.tok[r];
+    float x[kPerThread];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) x[e] = lv[min(i0 + e, N - 1)];
     // counts of the request's earlier tiles
     int gtb = 0, eqb = 0;
     const int first = tb.tile[r];
@@ -278,6 +301,10 @@ __global__ __launch_bounds__(kThreads) void write_kernel(VoteParams p) {
       gtb += p.tile_counts[(int64_t)(first + tt) * 2 + 0];
       eqb += p.tile_counts[(int64_t)(first + tt) * 2 + 1];
     }
+    __syncthreads();
+    uint32_t key_t;
+    int take_eq;
+    threshold(p, r, key_t, take_eq, s_dig, s_w, false);
     gtb = wave_sum_i(gtb);
     eqb = wave_sum_i(eqb);
     const int wave = threadIdx.x >> 6;
@@ -285,23 +312,23 @@ __global__ __launch_bounds__(kThreads) void write_kernel(VoteParams p) {
     __syncthreads();
     gtb = s_before[0][0] + s_before[0][1] + s_before[0][2] + s_before[0][3];
     eqb = s_before[1][0] + s_before[1][1] + s_before[1][2] + s_before[1][3];
-    const float* vr = p.vote + tb.tok[r];
     uint32_t keys[kPerThread];
     uint32_t packed = 0;                              // (equal << 16) | greater
+#pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      const int i = i0 + e;
-      keys[e] = (i < N) ? vote_key(vr[i]) : 0u;
-      if (i < N) packed += (keys[e] > key_t) ? 1u : ((keys[e] == key_t) ? (1u << 16) : 0u);
+      const bool in = i0 + e < N;
+      keys[e] = in ? order_key(x[e]) : 0u;
+      if (in) packed += (keys[e] > key_t) ? 1u : ((keys[e] == key_t) ? (1u << 16) : 0u);
     }
-    uint32_t tot;
-    uint32_t pre = block_excl_scan(packed, s_w, tot);
+    const uint32_t pre = block_excl_scan(packed, s_w);
     int g_run = gtb + (int)(pre & 0xffffu);
     int e_run = eqb + (int)(pre >> 16);
+#pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
       const int i = i0 + e;
-      if (i >= N) break;
-      const bool greater = keys[e] > key_t;
-      const bool equal = keys[e] == key_t;
+      const bool in = i < N;
+      const bool greater = in && keys[e] > key_t;
+      const bool equal = in && keys[e] == key_t;
       const int pos = g_run + min(e_run, take_eq);
       if ((greater || (equal && e_run < take_eq)) && pos < k) out[pos] = i;
       g_run += greater;
