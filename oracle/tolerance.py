@@ -96,12 +96,23 @@ def attn_budget(q, K, V, S, attn_scale: float, out) -> np.ndarray:
 LN2 = 0.6931471805599453
 
 
+FP64_TINY = 2.0 ** -1074
+
+
 def vote_rel_budget(q, K, z, p, M, v, score_scale: float = 1.0) -> np.ndarray:
-    """r_i = 4u * sum_h p_h(i) (|z_hi| + |M_h| + score_scale A_hi) / v_i (inf where v_i == 0)."""
+    """Relative error budget of a vote, r_i (inf where v_i == 0).
+
+    r_i = (4u * sum_h p_h(i) (|z_hi| + |M_h| + score_scale A_hi) + H * 2^-1074) / v_i.
+    The first term is the fp32 logit error carried into each head weight; the
+    second is the oracle's own fp64 underflow: a head weight below 2^-1022 is a
+    subnormal with absolute spacing 2^-1074, so votes near 2^-1074 carry only a
+    few significant bits in the oracle.
+    """
     A = abs_dot(q, K)
+    H = p.shape[0]
     t = (p * (np.abs(z) + np.abs(M)[:, None] + abs(score_scale) * A)).sum(axis=0)
     with np.errstate(divide="ignore", invalid="ignore"):
-        r = np.where(v > 0, 4.0 * U32 * t / np.where(v > 0, v, 1.0), np.inf)
+        r = np.where(v > 0, (4.0 * U32 * t + H * FP64_TINY) / np.where(v > 0, v, 1.0), np.inf)
     return r
 
 
