@@ -48,7 +48,8 @@
  *   seq_lens   int32 [batch]: N_r, cached tokens including the current one.
  *   Ragged token axis: request r owns positions [off_r, off_r + N_r) with
  *   off_r = N_0 + ... + N_{r-1} (computed on the device from seq_lens).
- *   logits     fp32: request r, query head h, token i at off_r * H + h * N_r + i.
+ *   logits     fp32: request r, query head h = g * G + j (G = H / H_kv), token i at
+ *              off_r * H + (g * N_r + i) * G + j, i.e. [H_kv][N_r][G] per request.
  *   head_stats fp32 [batch][H][2]: (M_h, Z_h) = (max_i z, sum_i exp(z - M_h)).
  *   vote       fp32 log2 of the head soft vote, log2 v_i: request r, token i at
  *              off_r + i (finite where the linear vote would underflow fp32).

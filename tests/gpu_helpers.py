@@ -89,7 +89,9 @@ def run_path(batch: wl.PagedBatch, geo: wl.Geometry, top_k=None, n_local=None,
     L, V, T = [], [], []
     for r in range(b):
         n = lens[r]
-        L.append(lg[offs[r] * H: offs[r] * H + H * n].reshape(H, n))
+        G = H // geo.num_kv_heads
+        blk = lg[offs[r] * H: offs[r] * H + H * n].reshape(geo.num_kv_heads, n, G)
+        L.append(np.ascontiguousarray(blk.transpose(0, 2, 1)).reshape(H, n))
         V.append(vt[offs[r]: offs[r] + n])
         assert sc[r] == min(k, n), (r, sc[r], k, n)
         T.append(si[r, : sc[r]].astype(np.int64))

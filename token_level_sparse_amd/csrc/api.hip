@@ -36,9 +36,22 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Score work units: runs of chunk_pages pages of one KV head, sized so a launch
+// has about kScoreUnitsTarget units; the grid is capped at kScoreMaxGrid
+// workgroups of 4 waves that loop over the units.
+#ifndef TS_SCORE_UNITS_TARGET
+#define TS_SCORE_UNITS_TARGET 16384
+#endif
+#ifndef TS_SCORE_MAX_GRID
+#define TS_SCORE_MAX_GRID 2048
+#endif
+#ifndef TS_SCORE_MAX_CHUNK_PAGES
+#define TS_SCORE_MAX_CHUNK_PAGES 32
+#endif
 constexpr int kMinChunkPages = 4;     // smallest score work unit (pages)
-constexpr int kMaxChunkPages = 32;
-constexpr int kScoreUnitsTarget = 16384;
+constexpr int kMaxChunkPages = TS_SCORE_MAX_CHUNK_PAGES;
+constexpr int kScoreUnitsTarget = TS_SCORE_UNITS_TARGET;
+constexpr int kScoreMaxGrid = TS_SCORE_MAX_GRID;
 constexpr int kMaxGrid = 2048;
 
 // Byte offsets of the workspace regions.
@@ -150,7 +163,8 @@ ts::ScoreParams score_params(const ts_shape& s, const ts_select& sel, const void
   p.bf16 = s.dtype == TS_BF16;
   const int64_t units = (cdiv(cdiv(s.max_total_tokens, ts::kPage) + s.batch, p.chunk_pages) + s.batch) *
                         s.num_kv_heads;
-  p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxGrid, cdiv(units, 4)));
+  p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(kScoreMaxGrid, cdiv(units, 4)));
+  if (p.grid >= 8 * ts::kXcds) p.grid -= p.grid % ts::kXcds;   // whole rounds over the XCDs
   return p;
 }
 
@@ -165,7 +179,7 @@ ts::VoteParams vote_params(const ts_shape& s, const ts_select& sel, const float*
   p.state = at<int32_t>(ws, L.state);
   p.tile_counts = at<int32_t>(ws, L.tiles);
   p.sel_idx = sel_idx; p.sel_count = sel_count;
-  p.H = s.num_q_heads; p.b = s.batch; p.top_k = sel.top_k;
+  p.H = s.num_q_heads; p.G = s.num_q_heads / s.num_kv_heads; p.b = s.batch; p.top_k = sel.top_k;
   p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxGrid, max_tiles(s)));
   return p;
 }

@@ -9,6 +9,7 @@ namespace ts {
 constexpr int kHeadDim = 128;     // d handled by this build
 constexpr int kPage = 16;         // tokens per page handled by this build
 constexpr int kWave = 64;         // CDNA wavefront
+constexpr int kXcds = 8;          // accelerator complex dies; workgroup i runs on XCD i % 8
 constexpr int kMaxBatch = 1024;   // requests per call (LDS prefix tables)
 constexpr int kMaxGroup = 8;      // query heads per KV head
 constexpr float kLog2e = 1.4426950408889634f;

@@ -41,7 +41,7 @@ struct VoteParams {
   int32_t* tile_counts;       // [tiles][2] (greater, equal) per tile
   int32_t* sel_idx;           // [b][top_k]
   int32_t* sel_count;         // [b]
-  int H, b, top_k;
+  int H, G, b, top_k;
   int grid;                   // workgroups of the tile kernels
 };
 

@@ -15,7 +15,8 @@
 // fp32 FMAs), and DPP sums over the 16 lanes of a row finish each inner product.
 // The lanes then split the 4 tokens x G heads of a row among themselves to store
 // the logits and keep a running (max, sum exp) per head; a second small kernel
-// folds the per-unit pairs into (M_h, Z_h).
+// folds the per-unit pairs into (M_h, Z_h). Logits are laid out [H_kv][N][G], so
+// a page's 16 tokens x G heads land as one contiguous 64 G-byte block.
 #include <type_traits>
 
 #include "common.h"
@@ -26,48 +27,103 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kUnroll = 4;        // pages in flight per wave
+#ifndef TS_SCORE_UNROLL
+#define TS_SCORE_UNROLL 4
+#endif
+constexpr int kUnroll = TS_SCORE_UNROLL;   // pages in flight per wave
 
-template <bool kBf16, int G> struct QRegs;
-template <int G> struct QRegs<true, G> { uint32_t w[G][4]; };
-template <int G> struct QRegs<false, G> { float w[G][8]; };
+// Query head slots. A lane holds kSlots query slices; slot s of lane col is head
+//   h(col, s) = (sA ^ b3) + 2 (sB ^ b2 ^ b3) + 4 sC,  s = sA + 2 sB + 4 sC,
+// with b2, b3 bits 2 and 3 of col (heads >= G are zero). This per-lane order makes
+// the first two butterfly steps of the row reduction below pair equal heads with
+// a plain DPP add, without selects.
+template <int G> struct Slots { static constexpr int kN = (G <= 4) ? 4 : 8; };
+
+__device__ __forceinline__ int slot_head(int col, int s) {
+  const int b2 = (col >> 2) & 1, b3 = (col >> 3) & 1;
+  return ((s & 1) ^ b3) + 2 * (((s >> 1) & 1) ^ b2 ^ b3) + 4 * (s >> 2);
+}
+
+template <bool kBf16, int S> struct QRegs;
+template <int S> struct QRegs<true, S> { uint32_t w[S][4]; };
+template <int S> struct QRegs<false, S> { float w[S][8]; };
 
 template <bool kBf16> struct PageRegs;
 template <> struct PageRegs<true> { uint4 w[4]; };
 template <> struct PageRegs<false> { float4 w[4][2]; };
 
+#ifndef TS_SCORE_NT
+#define TS_SCORE_NT 1
+#endif
+// The K stream is read once per step: its loads are marked nontemporal.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+#if TS_SCORE_NT
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
+__device__ __forceinline__ float4 stream_load(const float4* p) {
+#if TS_SCORE_NT
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
+
+#ifndef TS_SCORE_NT_STORE
+#define TS_SCORE_NT_STORE 0
+#endif
+__device__ __forceinline__ void stream_store(float* p, float v) {
+#if TS_SCORE_NT_STORE
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
 // bf16: a token row is 256 B, lane col reads dims [8 col, 8 col + 8).
 // fp32: a token row is 512 B, lane col reads dims [4 col, 4 col + 4) and
 // [64 + 4 col, 64 + 4 col + 4), so each load instruction covers 256 contiguous bytes.
-template <int G>
-__device__ __forceinline__ void load_q(QRegs<true, G>& qr, const uint16_t* qb, int col) {
+template <int G, int S>
+__device__ __forceinline__ void load_q(QRegs<true, S>& qr, const uint16_t* qb, int col) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 v = *reinterpret_cast<const uint4*>(qb + h * kHeadDim + 8 * col);
-    qr.w[h][0] = v.x; qr.w[h][1] = v.y; qr.w[h][2] = v.z; qr.w[h][3] = v.w;
+  for (int s = 0; s < S; ++s) {
+    const int h = slot_head(col, s);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (h < G) v = *reinterpret_cast<const uint4*>(qb + h * kHeadDim + 8 * col);
+    qr.w[s][0] = v.x; qr.w[s][1] = v.y; qr.w[s][2] = v.z; qr.w[s][3] = v.w;
   }
 }
-template <int G>
-__device__ __forceinline__ void load_q(QRegs<false, G>& qr, const float* qb, int col) {
+template <int G, int S>
+__device__ __forceinline__ void load_q(QRegs<false, S>& qr, const float* qb, int col) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float4 a = *reinterpret_cast<const float4*>(qb + h * kHeadDim + 4 * col);
-    const float4 c = *reinterpret_cast<const float4*>(qb + h * kHeadDim + 64 + 4 * col);
-    qr.w[h][0] = a.x; qr.w[h][1] = a.y; qr.w[h][2] = a.z; qr.w[h][3] = a.w;
-    qr.w[h][4] = c.x; qr.w[h][5] = c.y; qr.w[h][6] = c.z; qr.w[h][7] = c.w;
+  for (int s = 0; s < S; ++s) {
+    const int h = slot_head(col, s);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
+    if (h < G) {
+      a = *reinterpret_cast<const float4*>(qb + h * kHeadDim + 4 * col);
+      c = *reinterpret_cast<const float4*>(qb + h * kHeadDim + 64 + 4 * col);
+    }
+    qr.w[s][0] = a.x; qr.w[s][1] = a.y; qr.w[s][2] = a.z; qr.w[s][3] = a.w;
+    qr.w[s][4] = c.x; qr.w[s][5] = c.y; qr.w[s][6] = c.z; qr.w[s][7] = c.w;
   }
 }
 
 __device__ __forceinline__ void load_page(PageRegs<true>& pr, const uint16_t* base, int row, int col) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    pr.w[j] = *reinterpret_cast<const uint4*>(base + (4 * j + row) * kHeadDim + 8 * col);
+    pr.w[j] = stream_load(reinterpret_cast<const uint4*>(base + (4 * j + row) * kHeadDim + 8 * col));
 }
 __device__ __forceinline__ void load_page(PageRegs<false>& pr, const float* base, int row, int col) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    pr.w[j][0] = *reinterpret_cast<const float4*>(base + (4 * j + row) * kHeadDim + 4 * col);
-    pr.w[j][1] = *reinterpret_cast<const float4*>(base + (4 * j + row) * kHeadDim + 64 + 4 * col);
+    pr.w[j][0] = stream_load(reinterpret_cast<const float4*>(base + (4 * j + row) * kHeadDim + 4 * col));
+    pr.w[j][1] = stream_load(reinterpret_cast<const float4*>(base + (4 * j + row) * kHeadDim + 64 + 4 * col));
   }
 }
 
@@ -76,46 +132,79 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-template <int G>
-__device__ __forceinline__ void lane_dots(const PageRegs<true>& pr, const QRegs<true, G>& qr,
-                                          float (&acc)[4][G]) {
+// Partial inner products of the lane's 8 dims: acc[j][s] for token 4 j + row, slot s.
+template <int S>
+__device__ __forceinline__ void lane_dots(const PageRegs<true>& pr, const QRegs<true, S>& qr,
+                                          float (&acc)[4][S]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float a = dot2(pr.w[j].x, qr.w[h][0], 0.f);
-      a = dot2(pr.w[j].y, qr.w[h][1], a);
-      a = dot2(pr.w[j].z, qr.w[h][2], a);
-      acc[j][h] = dot2(pr.w[j].w, qr.w[h][3], a);
+    for (int s = 0; s < S; ++s) {
+      float a = dot2(pr.w[j].x, qr.w[s][0], 0.f);
+      a = dot2(pr.w[j].y, qr.w[s][1], a);
+      a = dot2(pr.w[j].z, qr.w[s][2], a);
+      acc[j][s] = dot2(pr.w[j].w, qr.w[s][3], a);
     }
   }
 }
-template <int G>
-__device__ __forceinline__ void lane_dots(const PageRegs<false>& pr, const QRegs<false, G>& qr,
-                                          float (&acc)[4][G]) {
+template <int S>
+__device__ __forceinline__ void lane_dots(const PageRegs<false>& pr, const QRegs<false, S>& qr,
+                                          float (&acc)[4][S]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float a = pr.w[j][0].x * qr.w[h][0];
-      a = fmaf(pr.w[j][0].y, qr.w[h][1], a);
-      a = fmaf(pr.w[j][0].z, qr.w[h][2], a);
-      a = fmaf(pr.w[j][0].w, qr.w[h][3], a);
-      a = fmaf(pr.w[j][1].x, qr.w[h][4], a);
-      a = fmaf(pr.w[j][1].y, qr.w[h][5], a);
-      a = fmaf(pr.w[j][1].z, qr.w[h][6], a);
-      acc[j][h] = fmaf(pr.w[j][1].w, qr.w[h][7], a);
+    for (int s = 0; s < S; ++s) {
+      float a = pr.w[j][0].x * qr.w[s][0];
+      a = fmaf(pr.w[j][0].y, qr.w[s][1], a);
+      a = fmaf(pr.w[j][0].z, qr.w[s][2], a);
+      a = fmaf(pr.w[j][0].w, qr.w[s][3], a);
+      a = fmaf(pr.w[j][1].x, qr.w[s][4], a);
+      a = fmaf(pr.w[j][1].y, qr.w[s][5], a);
+      a = fmaf(pr.w[j][1].z, qr.w[s][6], a);
+      acc[j][s] = fmaf(pr.w[j][1].w, qr.w[s][7], a);
     }
+  }
+}
+
+constexpr int kDppXor3 = 0x1B;        // quad_perm [3,2,1,0]
+
+// Reduce-scatter over the 16 lanes of a row: 4 tokens x S slots in, S/4 values
+// out. Partners lane ^ 15, ^ 7, ^ 3, ^ 1 span the row. Steps 1-2 pair slots of
+// equal head (see slot_head); steps 3-4 split the tokens by lane bits 1 and 0.
+// Lane col ends with token j = col & 3 of its row and heads b3 + 2 (b2 ^ b3) + 4 c.
+template <int S>
+__device__ __forceinline__ void row_reduce_scatter(const float (&acc)[4][S], int col,
+                                                   float (&out)[S / 4]) {
+  float r1[4][S / 2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int t = 0; t < S / 2; ++t) r1[j][t] = acc[j][2 * t] + dpp_f<kDppMirror>(acc[j][2 * t + 1]);
+  float r2[4][S / 4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int c = 0; c < S / 4; ++c) r2[j][c] = r1[j][2 * c] + dpp_f<kDppHalfMirror>(r1[j][2 * c + 1]);
+  const bool b1 = (col >> 1) & 1, b0 = col & 1;
+#pragma unroll
+  for (int c = 0; c < S / 4; ++c) {
+    float r3[2];
+#pragma unroll
+    for (int j0 = 0; j0 < 2; ++j0) {
+      const float lo = r2[j0][c], hi = r2[j0 + 2][c];
+      r3[j0] = (b1 ? hi : lo) + dpp_f<kDppXor3>(b1 ? lo : hi);
+    }
+    out[c] = (b0 ? r3[1] : r3[0]) + dpp_f<kDppXor1>(b0 ? r3[0] : r3[1]);
   }
 }
 
 template <bool kBf16, int G>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
   using T = typename std::conditional<kBf16, uint16_t, float>::type;
-  constexpr int kSlots = (4 * G + 15) / 16;   // (token, head) values a lane owns per page
+  constexpr int S = Slots<G>::kN;
+  constexpr int C = S / 4;                     // values a lane owns per page
   __shared__ int64_t s_tok[kMaxBatch + 1];
   __shared__ int32_t s_chunk[kMaxBatch + 1];
-  __shared__ float s_red[4][4 * G][4][2];
 
   const int b = p.b;
   const int chunk_tokens = p.chunk_pages * kPage;
@@ -131,101 +220,111 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
   const int total_units = s_chunk[b] * Hkv;
   const T* qall = static_cast<const T*>(p.q);
   const T* pool = static_cast<const T*>(p.k_pool);
-  float(*red)[4][2] = s_red[wave];
-
-  // Which (token j, head h) of its row this lane stores, per slot.
-  int slot_j[kSlots], slot_h[kSlots];
-  bool slot_on[kSlots];
+  // this lane's outputs: token 4 (col & 3) + row of each page, heads hd[c]
+  const int tok_in_page = 4 * (col & 3) + row;
+  int hd[C];
 #pragma unroll
-  for (int s = 0; s < kSlots; ++s) {
-    const int idx = col + 16 * s;
-    slot_on[s] = idx < 4 * G;
-    slot_j[s] = idx / G;
-    slot_h[s] = idx % G;
-  }
+  for (int c = 0; c < C; ++c) hd[c] = slot_head(col, 4 * c);
 
-  for (int u = blockIdx.x * 4 + wave; u < total_units; u += gridDim.x * 4) {
-    const int cg = u / Hkv, g = u - cg * Hkv;
-    const int r = find_segment(s_chunk, b, cg);
-    const int c = cg - s_chunk[r];
+  // XCD-aware order: workgroup i runs on XCD i % 8, so each XCD takes one
+  // contiguous range of unit blocks (4 units = 4 waves), and all KV heads of a
+  // chunk (adjacent blocks in the pool) are read through the same L2 and TLB.
+  const int n_xcd = (gridDim.x % kXcds == 0) ? kXcds : 1;
+  const int xcd = blockIdx.x % n_xcd, rank = blockIdx.x / n_xcd;
+  const int per_xcd_wg = gridDim.x / n_xcd;
+  const int blocks = (total_units + 3) / 4;
+  const int blk_lo = (int)((int64_t)blocks * xcd / n_xcd);
+  const int blk_hi = (int)((int64_t)blocks * (xcd + 1) / n_xcd);
+  for (int blk = blk_lo + rank; blk < blk_hi; blk += per_xcd_wg) {
+    const int u = blk * 4 + wave;
+    if (u >= total_units) break;
+    // Wave-uniform unit coordinates (readfirstlane lets the block-table reads
+    // below be scalar loads, which do not wait on the in-flight page loads).
+    const int cg = __builtin_amdgcn_readfirstlane(u / Hkv);
+    const int g = __builtin_amdgcn_readfirstlane(u - cg * Hkv);
+    const int r = __builtin_amdgcn_readfirstlane(find_segment(s_chunk, b, cg));
+    const int c0 = cg - __builtin_amdgcn_readfirstlane(s_chunk[r]);
     const int N = p.seq_lens[r];
     const int n_pages = (N + kPage - 1) / kPage;
-    const int pg0 = c * p.chunk_pages;
+    const int pg0 = c0 * p.chunk_pages;
     const int pg1 = min(n_pages, pg0 + p.chunk_pages);
 
-    QRegs<kBf16, G> q;
-    load_q(q, qall + ((int64_t)r * H + g * G) * kHeadDim, col);
+    QRegs<kBf16, S> q;
+    load_q<G>(q, qall + ((int64_t)r * H + g * G) * kHeadDim, col);
     const int32_t* bt = p.block_table + (int64_t)r * p.stride;
-    float* zrow = p.logits + s_tok[r] * H + (int64_t)(g * G) * N;
+    // logits of KV head g: [N][G] (token-major, the group's heads adjacent)
+    float* zrow = p.logits + (int64_t)__builtin_amdgcn_readfirstlane((int)s_tok[r]) * H +
+                  (int64_t)(g * G) * N;
 
-    float m[kSlots], s[kSlots];
+    float m[C], s[C];
 #pragma unroll
-    for (int k = 0; k < kSlots; ++k) { m[k] = kNegInf; s[k] = 0.f; }
+    for (int c = 0; c < C; ++c) { m[c] = kNegInf; s[c] = 0.f; }
+
+    // Logits of a group are stored after the next group's loads are issued, so
+    // the in-order memory counter never makes a page load wait on a store.
+    float zq[kUnroll][C];
+    int iq[kUnroll];
+    bool pending = false;
+    auto flush = [&]() {
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k) {
+        if (iq[k] < N) {
+#pragma unroll
+          for (int c = 0; c < C; ++c)
+            if (hd[c] < G) stream_store(&zrow[(int64_t)iq[k] * G + hd[c]], zq[k][c]);
+        }
+      }
+    };
 
     for (int pg = pg0; pg < pg1; pg += kUnroll) {
       PageRegs<kBf16> pr[kUnroll];
+      int64_t phys[kUnroll];
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k) phys[k] = bt[min(pg + k, pg1 - 1)];
+      // pages past the unit's end reload its last page (in bounds); they are not used
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k)
+        load_page(pr[k], pool + (phys[k] * Hkv + g) * (kPage * kHeadDim), row, col);
+      if (pending) flush();
 #pragma unroll
       for (int k = 0; k < kUnroll; ++k) {
-        if (pg + k < pg1) {
-          const int64_t phys = bt[pg + k];
-          load_page(pr[k], pool + (phys * Hkv + g) * (kPage * kHeadDim), row, col);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < kUnroll; ++k) {
-        if (pg + k >= pg1) break;
-        float acc[4][G];
+        const int i = (pg + k) * kPage + tok_in_page;
+        iq[k] = (pg + k < pg1) ? i : N;
+        float acc[4][S];
         lane_dots(pr[k], q, acc);
+        float v[C];
+        row_reduce_scatter(acc, col, v);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int h = 0; h < G; ++h) acc[j][h] = row_sum16(acc[j][h]);
-        const int tok0 = (pg + k) * kPage + row;
-#pragma unroll
-        for (int sl = 0; sl < kSlots; ++sl) {
-          float val = 0.f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-              val = (slot_j[sl] == j && slot_h[sl] == h) ? acc[j][h] : val;
-          const int i = tok0 + 4 * slot_j[sl];
-          if (slot_on[sl] && i < N) {
-            const float z = val * p.score_scale;
-            zrow[(int64_t)slot_h[sl] * N + i] = z;
-            const float mn = fmaxf(m[sl], z);
-            s[sl] = s[sl] * exp_via2(m[sl] - mn) + exp_via2(z - mn);
-            m[sl] = mn;
+        for (int c = 0; c < C; ++c) {
+          const float z = v[c] * p.score_scale;
+          zq[k][c] = z;
+          if (iq[k] < N && hd[c] < G) {
+            // online (max, sum exp) with one exp per element
+            const float d = z - m[c];
+            const float w = exp_via2(-fabsf(d));
+            s[c] = (d > 0.f) ? fmaf(s[c], w, 1.f) : s[c] + w;
+            m[c] = fmaxf(m[c], z);
           }
         }
       }
+      pending = true;
     }
+    if (pending) flush();
 
-    // Fold the per-lane pairs of each head: 4 tokens-in-row x 4 rows per head.
+    // fold the 16 lanes that own each head: col bits 0-1 (DPP) and the 4 rows
 #pragma unroll
-    for (int sl = 0; sl < kSlots; ++sl) {
-      if (slot_on[sl]) {
-        const int idx = slot_j[sl] * G + slot_h[sl];
-        red[idx][row][0] = m[sl];
-        red[idx][row][1] = s[sl];
+    for (int c = 0; c < C; ++c) {
+      float mm = m[c], ss = s[c];
+      merge_ms(mm, ss, dpp_f<kDppXor1>(mm), dpp_f<kDppXor1>(ss));
+      merge_ms(mm, ss, dpp_f<kDppXor2>(mm), dpp_f<kDppXor2>(ss));
+#pragma unroll
+      for (int x = 16; x <= 32; x <<= 1) merge_ms(mm, ss, __shfl_xor(mm, x), __shfl_xor(ss, x));
+      if (row == 0 && (col & 3) == 0 && hd[c] < G) {
+        float* dst = p.partials + ((int64_t)cg * H + g * G + hd[c]) * 2;
+        dst[0] = mm;
+        dst[1] = ss;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (lane < G) {
-      float M = kNegInf, S = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) merge_ms(M, S, red[j * G + lane][rr][0], red[j * G + lane][rr][1]);
-      float* dst = p.partials + ((int64_t)cg * H + g * G + lane) * 2;
-      dst[0] = M;
-      dst[1] = S;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 

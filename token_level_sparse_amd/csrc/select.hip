@@ -109,12 +109,30 @@ __device__ __forceinline__ void load_keys(const float* lv, int i0, int N, uint32
 }
 
 // ---------------------------------------------------------------- vote + digit-0 histogram
+// Logits are [H_kv][N][G] per request: for each KV head a thread reads the G
+// adjacent logits of each of its positions (16-byte loads when G is a multiple
+// of 4).
+template <int G>
+__device__ __forceinline__ void load_group(const float* zg, int i, float (&x)[G]) {
+  if constexpr (G % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < G; j += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(zg + (int64_t)i * G + j);
+      x[j] = v.x; x[j + 1] = v.y; x[j + 2] = v.z; x[j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < G; ++j) x[j] = zg[(int64_t)i * G + j];
+  }
+}
+
+template <int G>
 __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
   __shared__ Tables tb;
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ float s_m[256], s_l[256];
   build_tables(tb, p);
-  const int H = p.H;
+  const int H = p.H, Hkv = H / G;
   const int total = tb.tile[p.b];
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int r = find_segment(tb.tile, p.b, tile);
@@ -136,18 +154,24 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
     float m[kPerThread], s[kPerThread];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) { m[e] = kNegInf; s[e] = 0.f; }
-#pragma unroll 8
-    for (int h = 0; h < H; ++h) {
-      const float* zh = z + (int64_t)h * N;
-      const float mh = s_m[h], lh = s_l[h];
+#pragma unroll 2
+    for (int g = 0; g < Hkv; ++g) {
+      const float* zg = z + (int64_t)g * N * G;
+      float x[kPerThread][G];
 #pragma unroll
-      for (int e = 0; e < kPerThread; ++e) {
-        const float x = fmaf(zh[idx[e]] - mh, kLog2eF, -lh);
-        // online log-sum-exp in base 2, one exp per term
-        const float d = x - m[e];
-        const float w = fast_exp2(-fabsf(d));
-        s[e] = (d > 0.f) ? fmaf(s[e], w, 1.f) : s[e] + w;
-        m[e] = fmaxf(m[e], x);
+      for (int e = 0; e < kPerThread; ++e) load_group<G>(zg, idx[e], x[e]);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float mh = s_m[g * G + j], lh = s_l[g * G + j];
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+          const float xv = fmaf(x[e][j] - mh, kLog2eF, -lh);
+          // online log-sum-exp in base 2, one exp per term
+          const float d = xv - m[e];
+          const float w = fast_exp2(-fabsf(d));
+          s[e] = (d > 0.f) ? fmaf(s[e], w, 1.f) : s[e] + w;
+          m[e] = fmaxf(m[e], xv);
+        }
       }
     }
     float* vout = p.vote + tb.tok[r];
@@ -350,7 +374,17 @@ hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist) 
     hipLaunchKernelGGL(zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.hist, n);
   }
   const dim3 grid(p.grid), block(kThreads);
-  hipLaunchKernelGGL(vote_kernel, grid, block, 0, s, p);
+  switch (p.G) {
+    case 1: hipLaunchKernelGGL(vote_kernel<1>, grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL(vote_kernel<2>, grid, block, 0, s, p); break;
+    case 3: hipLaunchKernelGGL(vote_kernel<3>, grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL(vote_kernel<4>, grid, block, 0, s, p); break;
+    case 5: hipLaunchKernelGGL(vote_kernel<5>, grid, block, 0, s, p); break;
+    case 6: hipLaunchKernelGGL(vote_kernel<6>, grid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL(vote_kernel<7>, grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL(vote_kernel<8>, grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL(refine_kernel<1>, grid, block, 0, s, p);
   hipLaunchKernelGGL(refine_kernel<2>, grid, block, 0, s, p);
   hipLaunchKernelGGL(count_kernel, grid, block, 0, s, p);
