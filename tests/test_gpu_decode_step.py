@@ -112,3 +112,59 @@ def test_zero_query_misses():
     q = torch.zeros(3, geo.num_q_heads, geo.head_dim, dtype=torch.bfloat16, device=DEV)
     _, _, _, hits, _, _ = run_sequence(geo, 500, 3, -1.0, qs=q)
     assert hits.tolist() == [False, False, False]
+
+
+def test_ragged_batch_mixed_hits():
+    """Four requests of different lengths decoded together: requests 0 and 2 repeat
+    their query (hits after the first step), 1 and 3 draw a new one every step
+    (misses), so every kernel sees skipped and active requests in one launch."""
+    geo = wl.workload("llama3-8b-128k", top_k=300, n_local=40, n_planted=8)
+    gh.log("[decode ragged b=4 mixed hits]")
+    steps, lens0 = 5, [3000, 5000, 2000, 7001]
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    reqs = [wl.make_request(gen, geo, n, DEV, extra_tokens=steps - 1) for n in lens0]
+    batch = wl.page_requests(reqs, geo, gen, DEV)
+    H, d, b = geo.num_q_heads, geo.head_dim, len(reqs)
+    qs = torch.randn(steps, b, H, d, generator=gen, device=DEV).to(torch.bfloat16)
+    qs[:, 0] = qs[0, 0]
+    qs[:, 2] = qs[0, 2]
+    shape = ts.make_shape(H, geo.num_kv_heads, b, batch.block_table.shape[1],
+                          sum(lens0) + b * (steps - 1), geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, 0.9)
+    ws = ts.alloc_workspace(shape, sel, DEV)
+    cache = ts.CacheState.allocate(b, H, d, geo.top_k, geo.torch_dtype, DEV)
+    hit = torch.zeros(b, dtype=torch.int32, device=DEV)
+    out = torch.empty(b, H, d, dtype=geo.torch_dtype, device=DEV)
+    hits, Ts, outs = [], [], []
+    for t in range(steps):
+        lens = torch.tensor([n + t for n in lens0], dtype=torch.int32, device=DEV)
+        ts.decode_step(shape, sel, qs[t].contiguous(), batch.k_pool, batch.v_pool,
+                       batch.block_table, lens, cache, hit, out, ws)
+        torch.cuda.synchronize()
+        hits.append(hit.cpu().numpy().astype(bool))
+        cnt = cache.cached_count.cpu().numpy()
+        idx = cache.cached_idx.cpu().numpy()
+        Ts.append([idx[r, :cnt[r]].astype(np.int64) for r in range(b)])
+        outs.append(gh.np32(out))
+    hits = np.array(hits)                              # [steps][b]
+    assert hits[:, 0].tolist() == [False] + [True] * (steps - 1)
+    assert hits[:, 2].tolist() == [False] + [True] * (steps - 1)
+    assert not hits[:, 1].any() and not hits[:, 3].any()
+    for r in range(b):
+        q_all = gh.np32(qs[:, r])
+        K, V = gh.np32(reqs[r].k), gh.np32(reqs[r].v)
+        lens_r = np.array([lens0[r] + t for t in range(steps)])
+        ref = ora.decode_sequence(q_all, K, V, lens_r, geo.top_k, geo.n_local, 0.9, want_outputs=False)
+        assert np.array_equal(hits[:, r], ref["hit"])
+        for t in range(steps):
+            N = int(lens_r[t])
+            if not hits[t, r]:
+                s = ora.select(q_all[t], K[:, :N], geo.top_k)
+                rel = gh.tol.vote_rel_budget(q_all[t], K[:, :N], s["z"], s["p"], s["M"], s["vote"])
+                amb = gh.tol.ambiguous_positions_log(s["vote"], rel, geo.top_k)
+                diff = np.setxor1d(Ts[t][r], s["T"])
+                assert np.all(amb[diff]), (r, t)
+            else:
+                assert np.array_equal(Ts[t][r], Ts[t - 1][r])
+            gh.check_attention(outs[t][r], q_all[t], K[:, :N], V[:, :N], Ts[t][r], N, geo.n_local,
+                               geo.attn_scale, False)

@@ -191,88 +191,89 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
   }
 }
 
-// ---------------------------------------------------------------- digits 1 and 2
+// ---------------------------------------------------------------- TopK phases
+// Four kernels, one per phase; every workgroup loops over its share of the tiles.
+// (A single cooperative kernel with grid barriers between the phases was measured
+// on MI355X at 321 us per 1M-token step against 26 us for the four launches.)
+struct SelectShared {
+  Tables tb;
+  uint32_t hist[kHistBins];
+  uint32_t w[4];
+  int dig[2];
+  int cnt[2][4];
+};
+
 // kPass 1: find digit 0 from hist[0], histogram digit 1 of matching keys into hist[1].
 // kPass 2: read digit 0 from state, find digit 1 from hist[1], histogram digit 2 into hist[2].
 template <int kPass>
-__global__ __launch_bounds__(kThreads) void refine_kernel(VoteParams p) {
-  __shared__ Tables tb;
-  __shared__ uint32_t s_hist[kHistBins];
-  __shared__ uint32_t s_w[4];
-  __shared__ int s_dig[2];
-  build_tables(tb, p);
-  const int total = tb.tile[p.b];
+__device__ void refine_phase(const VoteParams& p, SelectShared& sh) {
+  const int total = sh.tb.tile[p.b];
   constexpr int kShift = (kPass == 1) ? (32 - kDigitBits0) : (32 - kDigitBits0 - kDigitBits1);
   constexpr int kNextBits = (kPass == 1) ? kDigitBits1 : kDigitBits2;
   constexpr int kNextShift = kShift - kNextBits;
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int r = find_segment(tb.tile, p.b, tile);
-    const int t = tile - tb.tile[r];
+    const int r = find_segment(sh.tb.tile, p.b, tile);
+    const int t = tile - sh.tb.tile[r];
     const int N = p.seq_lens[r];
     if (p.top_k >= N) continue;                       // whole request selected: no radix work
     int32_t* st = p.state + r * 8;
     const uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
     const int i0 = t * kVoteTile + threadIdx.x;
     uint32_t key[kPerThread];
-    load_keys(p.vote + tb.tok[r], i0, N, key);
+    load_keys(p.vote + sh.tb.tok[r], i0, N, key);
     __syncthreads();
     uint32_t prefix;
     if (kPass == 1) {
-      find_digit<1 << kDigitBits0>(gh, p.top_k, s_dig, s_w);
-      prefix = (uint32_t)s_dig[0];
-      if (t == 0 && threadIdx.x == 0) { st[0] = s_dig[0]; st[1] = s_dig[1]; }
+      find_digit<1 << kDigitBits0>(gh, p.top_k, sh.dig, sh.w);
+      prefix = (uint32_t)sh.dig[0];
+      if (t == 0 && threadIdx.x == 0) { st[0] = sh.dig[0]; st[1] = sh.dig[1]; }
     } else {
       const int d0 = st[0], k0 = st[1];
-      find_digit<1 << kDigitBits1>(gh + kHistBins, k0, s_dig, s_w);
-      prefix = ((uint32_t)d0 << kDigitBits1) | (uint32_t)s_dig[0];
-      if (t == 0 && threadIdx.x == 0) { st[2] = s_dig[0]; st[3] = s_dig[1]; }
+      find_digit<1 << kDigitBits1>(gh + kHistBins, k0, sh.dig, sh.w);
+      prefix = ((uint32_t)d0 << kDigitBits1) | (uint32_t)sh.dig[0];
+      if (t == 0 && threadIdx.x == 0) { st[2] = sh.dig[0]; st[3] = sh.dig[1]; }
     }
-    for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads) s_hist[i] = 0;
+    for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads) sh.hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
       if (i0 + e * kThreads < N && (key[e] >> kShift) == prefix)
-        atomicAdd(&s_hist[(key[e] >> kNextShift) & ((1u << kNextBits) - 1)], 1u);
+        atomicAdd(&sh.hist[(key[e] >> kNextShift) & ((1u << kNextBits) - 1)], 1u);
     }
     __syncthreads();
     uint32_t* gn = p.hist + ((int64_t)r * 3 + kPass) * kHistBins;
     for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads)
-      if (s_hist[i]) atomicAdd(&gn[i], s_hist[i]);
+      if (sh.hist[i]) atomicAdd(&gn[i], sh.hist[i]);
   }
 }
 
 // Exact threshold key of request r and how many keys equal to it are taken.
 __device__ void threshold(const VoteParams& p, int r, uint32_t& key_t, int& take_eq,
-                          int* s_dig, uint32_t* s_w, bool record) {
+                          SelectShared& sh, bool record) {
   int32_t* st = p.state + r * 8;
   const int d0 = st[0], d1 = st[2], k1 = st[3];
-  find_digit<1 << kDigitBits2>(p.hist + ((int64_t)r * 3 + 2) * kHistBins, k1, s_dig, s_w);
+  find_digit<1 << kDigitBits2>(p.hist + ((int64_t)r * 3 + 2) * kHistBins, k1, sh.dig, sh.w);
   key_t = ((uint32_t)d0 << (kDigitBits1 + kDigitBits2)) | ((uint32_t)d1 << kDigitBits2) |
-          (uint32_t)s_dig[0];
-  take_eq = s_dig[1];
-  if (record && threadIdx.x == 0) { st[4] = s_dig[0]; st[5] = s_dig[1]; }
+          (uint32_t)sh.dig[0];
+  take_eq = sh.dig[1];
+  if (record && threadIdx.x == 0) { st[4] = sh.dig[0]; st[5] = sh.dig[1]; }
 }
 
-// ---------------------------------------------------------------- per-tile counts
-__global__ __launch_bounds__(kThreads) void count_kernel(VoteParams p) {
-  __shared__ Tables tb;
-  __shared__ uint32_t s_w[4];
-  __shared__ int s_dig[2];
-  __shared__ int s_cnt[2][4];
-  build_tables(tb, p);
-  const int total = tb.tile[p.b];
+// Per tile: keys above the exact threshold and keys equal to it.
+__device__ void count_phase(const VoteParams& p, SelectShared& sh) {
+  const int total = sh.tb.tile[p.b];
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int r = find_segment(tb.tile, p.b, tile);
-    const int t = tile - tb.tile[r];
+    const int r = find_segment(sh.tb.tile, p.b, tile);
+    const int t = tile - sh.tb.tile[r];
     const int N = p.seq_lens[r];
     if (p.top_k >= N) continue;
     const int i0 = t * kVoteTile + threadIdx.x;
     uint32_t key[kPerThread];
-    load_keys(p.vote + tb.tok[r], i0, N, key);
+    load_keys(p.vote + sh.tb.tok[r], i0, N, key);
     __syncthreads();
     uint32_t key_t;
     int take_eq;
-    threshold(p, r, key_t, take_eq, s_dig, s_w, t == 0);
+    threshold(p, r, key_t, take_eq, sh, t == 0);
     int gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -283,26 +284,21 @@ __global__ __launch_bounds__(kThreads) void count_kernel(VoteParams p) {
     gt = wave_sum_i(gt);
     eq = wave_sum_i(eq);
     const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { s_cnt[0][wave] = gt; s_cnt[1][wave] = eq; }
+    if ((threadIdx.x & 63) == 0) { sh.cnt[0][wave] = gt; sh.cnt[1][wave] = eq; }
     __syncthreads();
     if (threadIdx.x == 0) {
-      p.tile_counts[(int64_t)tile * 2 + 0] = s_cnt[0][0] + s_cnt[0][1] + s_cnt[0][2] + s_cnt[0][3];
-      p.tile_counts[(int64_t)tile * 2 + 1] = s_cnt[1][0] + s_cnt[1][1] + s_cnt[1][2] + s_cnt[1][3];
+      p.tile_counts[(int64_t)tile * 2 + 0] = sh.cnt[0][0] + sh.cnt[0][1] + sh.cnt[0][2] + sh.cnt[0][3];
+      p.tile_counts[(int64_t)tile * 2 + 1] = sh.cnt[1][0] + sh.cnt[1][1] + sh.cnt[1][2] + sh.cnt[1][3];
     }
   }
 }
 
-// ---------------------------------------------------------------- ascending positions
-__global__ __launch_bounds__(kThreads) void write_kernel(VoteParams p) {
-  __shared__ Tables tb;
-  __shared__ uint32_t s_w[4];
-  __shared__ int s_dig[2];
-  __shared__ int s_before[2][4];
-  build_tables(tb, p);
-  const int total = tb.tile[p.b];
+// Ascending positions through a prefix over the request's tiles.
+__device__ void write_phase(const VoteParams& p, SelectShared& sh) {
+  const int total = sh.tb.tile[p.b];
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int r = find_segment(tb.tile, p.b, tile);
-    const int t = tile - tb.tile[r];
+    const int r = find_segment(sh.tb.tile, p.b, tile);
+    const int t = tile - sh.tb.tile[r];
     const int N = p.seq_lens[r];
     const int k = p.top_k;
     int32_t* out = p.sel_idx + (int64_t)r * k;
@@ -314,13 +310,13 @@ __global__ __launch_bounds__(kThreads) void write_kernel(VoteParams p) {
         if (i0 + e < N) out[i0 + e] = i0 + e;
       continue;
     }
-    const float* lv = p.vote + tb.tok[r];
+    const float* lv = p.vote + sh.tb.tok[r];
     float x[kPerThread];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) x[e] = lv[min(i0 + e, N - 1)];
     // counts of the request's earlier tiles
     int gtb = 0, eqb = 0;
-    const int first = tb.tile[r];
+    const int first = sh.tb.tile[r];
     for (int tt = threadIdx.x; tt < t; tt += kThreads) {
       gtb += p.tile_counts[(int64_t)(first + tt) * 2 + 0];
       eqb += p.tile_counts[(int64_t)(first + tt) * 2 + 1];
@@ -328,14 +324,14 @@ __global__ __launch_bounds__(kThreads) void write_kernel(VoteParams p) {
     __syncthreads();
     uint32_t key_t;
     int take_eq;
-    threshold(p, r, key_t, take_eq, s_dig, s_w, false);
+    threshold(p, r, key_t, take_eq, sh, false);
     gtb = wave_sum_i(gtb);
     eqb = wave_sum_i(eqb);
     const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { s_before[0][wave] = gtb; s_before[1][wave] = eqb; }
+    if ((threadIdx.x & 63) == 0) { sh.cnt[0][wave] = gtb; sh.cnt[1][wave] = eqb; }
     __syncthreads();
-    gtb = s_before[0][0] + s_before[0][1] + s_before[0][2] + s_before[0][3];
-    eqb = s_before[1][0] + s_before[1][1] + s_before[1][2] + s_before[1][3];
+    gtb = sh.cnt[0][0] + sh.cnt[0][1] + sh.cnt[0][2] + sh.cnt[0][3];
+    eqb = sh.cnt[1][0] + sh.cnt[1][1] + sh.cnt[1][2] + sh.cnt[1][3];
     uint32_t keys[kPerThread];
     uint32_t packed = 0;                              // (equal << 16) | greater
 #pragma unroll
@@ -344,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void write_kernel(VoteParams p) {
       keys[e] = in ? order_key(x[e]) : 0u;
       if (in) packed += (keys[e] > key_t) ? 1u : ((keys[e] == key_t) ? (1u << 16) : 0u);
     }
-    const uint32_t pre = block_excl_scan(packed, s_w);
+    const uint32_t pre = block_excl_scan(packed, sh.w);
     int g_run = gtb + (int)(pre & 0xffffu);
     int e_run = eqb + (int)(pre >> 16);
 #pragma unroll
@@ -359,6 +355,16 @@ __global__ __launch_bounds__(kThreads) void write_kernel(VoteParams p) {
       e_run += equal;
     }
   }
+}
+
+template <int kPhase>
+__global__ __launch_bounds__(kThreads) void select_phase_kernel(VoteParams p) {
+  __shared__ SelectShared sh;
+  build_tables(sh.tb, p);
+  if (kPhase == 1) refine_phase<1>(p, sh);
+  if (kPhase == 2) refine_phase<2>(p, sh);
+  if (kPhase == 3) count_phase(p, sh);
+  if (kPhase == 4) write_phase(p, sh);
 }
 
 __global__ void zero_u32(uint32_t* x, int64_t n) {
@@ -385,10 +391,10 @@ hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist) 
     case 8: hipLaunchKernelGGL(vote_kernel<8>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(refine_kernel<1>, grid, block, 0, s, p);
-  hipLaunchKernelGGL(refine_kernel<2>, grid, block, 0, s, p);
-  hipLaunchKernelGGL(count_kernel, grid, block, 0, s, p);
-  hipLaunchKernelGGL(write_kernel, grid, block, 0, s, p);
+  hipLaunchKernelGGL(select_phase_kernel<1>, grid, block, 0, s, p);
+  hipLaunchKernelGGL(select_phase_kernel<2>, grid, block, 0, s, p);
+  hipLaunchKernelGGL(select_phase_kernel<3>, grid, block, 0, s, p);
+  hipLaunchKernelGGL(select_phase_kernel<4>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 
