@@ -9,14 +9,17 @@
 //
 // gfx950 design. The selected set of request r is the TopK list (ascending)
 // united with the window [N - L, N); TopK entries inside the window are skipped
-// because the window covers them, so no sort or merge is needed. Work items of
-// 32 tokens (one wavefront each) cover the TopK list and then the window, for one
-// KV head and all G query heads of its group: each key and value row (256 B in
-// bf16) is gathered once through the block table. Lane = 16 * row + col: the 4
-// rows of a wave take every 4th token and col picks 8 dims, DPP sums finish the
-// inner products, and each row keeps a (max, sum, o[8 dims]) online softmax in
-// registers. The rows merge by cross-row shuffles; a second kernel merges the
-// work items of each (request, head) and rounds the output.
+// because the window covers them, so no sort or merge is needed. A workgroup
+// covers 128 selected slots (32 per wavefront) of the TopK list or of the window,
+// for one KV head and all G query heads of its group: each key and value row
+// (256 B in bf16) is gathered once through the block table. Lane = 16 * row +
+// col: the 4 rows of a wave take every 4th token and col picks 8 dims, DPP sums
+// finish the inner products, and each row keeps a (max, sum, o[8 dims]) online
+// softmax in registers. Rows merge by cross-row shuffles and waves through LDS
+// into one partial per workgroup; a small kernel merges the partials of each
+// (request, head) and rounds the output. (Merging in the last workgroup behind an
+// atomic ticket was measured slower: the device-scope release each workgroup then
+// needs writes back its XCD's whole L2.)
 #include <type_traits>
 
 #include "common.h"
@@ -55,14 +58,13 @@ __device__ __forceinline__ int lane_dim(bool bf16, int col, int e) {
 template <bool kBf16, int G>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   using T = typename std::conditional<kBf16, uint16_t, float>::type;
+  __shared__ float s_part[4][G][kHeadDim + 2];
   const int S = attn_splits(p.top_k, p.n_local);
-  const int nT = (p.top_k + kAttnSplit - 1) / kAttnSplit;
+  const int nT = (p.top_k + kAttnTile - 1) / kAttnTile;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = lane >> 4, col = lane & 15;
-  const int w = blockIdx.x * 4 + wave;
-  if (w >= p.b * p.Hkv * S) return;
-  const int s = w % S;
-  const int rg = w / S;
+  const int s = blockIdx.x % S;
+  const int rg = blockIdx.x / S;
   const int g = rg % p.Hkv;
   const int r = rg / p.Hkv;
   const int H = p.H;
@@ -74,13 +76,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   bool ok = false;
   if (lane < kAttnSplit) {
     if (s < nT) {
-      const int e = s * kAttnSplit + lane;
+      const int e = s * kAttnTile + wave * kAttnSplit + lane;
       if (e < min(p.sel_count[r], p.sel_stride)) {
         tok = p.sel_idx[(int64_t)r * p.sel_stride + e];
         ok = tok >= 0 && tok < lstart;
       }
     } else {
-      tok = lstart + (s - nT) * kAttnSplit + lane;
+      tok = lstart + (s - nT) * kAttnTile + wave * kAttnSplit + lane;
       ok = tok < N;
     }
     if (!ok) tok = 0;                               // a real token; its weight is forced to 0
@@ -167,22 +169,45 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
       m[h] = mn;
     }
   }
+  // the 4 waves of the workgroup merge through LDS into one partial per head
   if (row == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float* dst = p.partials + (((int64_t)r * H + g * G + h) * S + s) * (kHeadDim + 2);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dst[lane_dim(kBf16, col, e)] = o[h][e];
+      for (int e = 0; e < 8; ++e) s_part[wave][h][lane_dim(kBf16, col, e)] = o[h][e];
       if (col == 0) {
-        dst[kHeadDim] = m[h];
-        dst[kHeadDim + 1] = l[h];
+        s_part[wave][h][kHeadDim] = m[h];
+        s_part[wave][h][kHeadDim + 1] = l[h];
       }
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * kHeadDim; e += blockDim.x) {
+    const int h = e / kHeadDim, dim = e % kHeadDim;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_part[w][h][kHeadDim]);
+    float acc = 0.f, L = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = s_part[w][h][kHeadDim];
+        const float c = (mw == kNegInf) ? 0.f : exp_via2(mw - M);
+        acc = fmaf(c, s_part[w][h][dim], acc);
+        L = fmaf(c, s_part[w][h][kHeadDim + 1], L);
+      }
+    }
+    float* dst = p.partials + (((int64_t)r * H + g * G + h) * S + s) * (kHeadDim + 2);
+    dst[dim] = acc;
+    if (dim == 0) {
+      dst[kHeadDim] = M;
+      dst[kHeadDim + 1] = L;
     }
   }
 }
 
-// One workgroup of d threads per (request, head): merge the work items. The
-// per-item weights exp(m_s - M) are computed once per item by spread threads and
+// One workgroup of d threads per (request, head): merge the workgroup partials.
+// The per-partial weights exp(m_s - M) are computed once by spread threads and
 // kept in LDS; each thread (one output dim) then sums its column with
 // independent loads.
 constexpr int kCombineChunk = 1024;
@@ -196,7 +221,7 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const float* base = p.partials + (int64_t)rh * S * (kHeadDim + 2);
   float M = kNegInf;
-  for (int s = tid; s < S; s += kHeadDim) M = fmaxf(M, base[s * (kHeadDim + 2) + kHeadDim]);
+  for (int j = tid; j < S; j += kHeadDim) M = fmaxf(M, base[j * (kHeadDim + 2) + kHeadDim]);
   M = wave_max(M);
   if ((tid & 63) == 0) s_red[tid >> 6] = M;
   __syncthreads();
@@ -207,13 +232,13 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(AttnParams p) {
     __syncthreads();
     for (int j = tid; j < n; j += kHeadDim) {
       const float* src = base + (c0 + j) * (kHeadDim + 2);
-      const float ms = src[kHeadDim], ls = src[kHeadDim + 1];
-      const float w = (ms == kNegInf || ls == 0.f) ? 0.f : exp_via2(ms - M);
+      const float mj = src[kHeadDim], lj = src[kHeadDim + 1];
+      const float w = (mj == kNegInf || lj == 0.f) ? 0.f : exp_via2(mj - M);
       s_w[j] = w;
-      L = fmaf(w, ls, L);
+      L = fmaf(w, lj, L);
     }
     __syncthreads();
-#pragma unroll 8
+#pragma unroll 4
     for (int j = 0; j < n; ++j) acc = fmaf(s_w[j], base[(c0 + j) * (kHeadDim + 2) + tid], acc);
   }
   L = wave_sum(L);
@@ -231,8 +256,7 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(AttnParams p) {
 template <bool kBf16>
 hipError_t launch_attn_t(const AttnParams& p, hipStream_t st) {
   const int G = p.H / p.Hkv;
-  const int waves = p.b * p.Hkv * attn_splits(p.top_k, p.n_local);
-  dim3 grid((waves + 3) / 4), block(256);
+  dim3 grid(p.b * p.Hkv * attn_splits(p.top_k, p.n_local)), block(256);
   switch (G) {
     case 1: hipLaunchKernelGGL((attn_kernel<kBf16, 1>), grid, block, 0, st, p); break;
     case 2: hipLaunchKernelGGL((attn_kernel<kBf16, 2>), grid, block, 0, st, p); break;

@@ -11,8 +11,9 @@ constexpr int kVoteTile = 1024;
 // Radix digits of the top-k select over the 32-bit vote keys, most significant first.
 constexpr int kDigitBits0 = 11, kDigitBits1 = 11, kDigitBits2 = 10;
 constexpr int kHistBins = 1 << 11;
-// Selected tokens per attention work item (one wavefront).
+// Selected tokens per attention wavefront and per attention workgroup (4 waves).
 constexpr int kAttnSplit = 32;
+constexpr int kAttnTile = 4 * kAttnSplit;
 
 struct ScoreParams {
   const void* q;              // [b][H][d]
@@ -74,7 +75,7 @@ struct CacheParams {
 };
 
 __host__ __device__ inline int attn_splits(int top_k, int n_local) {
-  return (top_k + kAttnSplit - 1) / kAttnSplit + (n_local + kAttnSplit - 1) / kAttnSplit;
+  return (top_k + kAttnTile - 1) / kAttnTile + (n_local + kAttnTile - 1) / kAttnTile;
 }
 
 hipError_t launch_score(const ScoreParams& p, hipStream_t s);
