@@ -11,7 +11,9 @@ steps cycle through the 32 layers, so each step streams a different 2 GiB K pool
 
 Prints one JSON line: decode steps/s (value), the scoring kernel's achieved HBM
 bandwidth against the 8 TB/s peak (roofline), the same metric at N = 131072
-(secondary), and the fp64 oracle timed on host cores (cpu_baseline).
+(secondary), the 16-request ragged batch (ragged_batch), the 256-step
+Selection Cache sequence on Qwen2-7B shapes (selection_cache: steps/s, hit rate,
+hit vector), and the fp64 oracle timed on host cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -129,6 +131,91 @@ def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False):
     return res, host
 
 
+def time_ragged(geo, steps, warmup, dev):
+    """Ragged batch: 16 requests in one shared shuffled pool, one launch per kernel per step."""
+    import torch
+    import token_level_sparse_amd as ts
+    from synth import workloads as wl
+    b = wl.make_batch(geo, device=dev)
+    B, H, d = geo.batch, geo.num_q_heads, geo.head_dim
+    shape = ts.make_shape(H, geo.num_kv_heads, B, b.block_table.shape[1], b.total_tokens, geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, 2.0)
+    ws = ts.alloc_workspace(shape, sel, dev)
+    cache = ts.CacheState.allocate(B, H, d, geo.top_k, geo.torch_dtype, dev)
+    hit = torch.zeros(B, dtype=torch.int32, device=dev)
+    out = torch.empty(B, H, d, dtype=geo.torch_dtype, device=dev)
+
+    def step():
+        ts.decode_step(shape, sel, b.q, b.k_pool, b.v_pool, b.block_table, b.seq_lens, cache, hit, out, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kbytes = geo.num_kv_heads * geo.head_dim * 2 * b.total_tokens
+    log(f"[{geo.name}] batch of {B}, sum N = {b.total_tokens}: decode step {ms:.4f} ms")
+    res = {"workload": geo.name, "batch": B, "total_tokens": b.total_tokens,
+           "decode_steps_per_s": 1e3 / ms, "ms_per_step": ms,
+           "k_stream_gbps_whole_step": kbytes / (ms * 1e-3) / 1e9}
+    del b, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_cache_sequence(geo, dev):
+    """Consecutive decode steps with the Selection Cache: N grows by one token per
+    step, queries follow the AR(1) recursion, theta = 0.9. The whole sequence is
+    timed once after one untimed pass (the cache is reset in between)."""
+    import torch
+    import token_level_sparse_amd as ts
+    from synth import workloads as wl
+    steps = geo.steps
+    gen = torch.Generator(device=dev).manual_seed(geo.seed)
+    req = wl.make_request(gen, geo, geo.seq_len, dev, extra_tokens=steps - 1)
+    batch = wl.page_requests([req], geo, gen, dev)
+    qs, _ = wl.ar1_queries(geo, req.q_master, steps, seed=geo.seed + 1, device=dev)
+    qs = [qs[t:t + 1].contiguous() for t in range(steps)]
+    lens = torch.arange(geo.seq_len, geo.seq_len + steps, dtype=torch.int32, device=dev)
+    lens = [lens[t:t + 1] for t in range(steps)]
+    H, d = geo.num_q_heads, geo.head_dim
+    shape = ts.make_shape(H, geo.num_kv_heads, 1, batch.block_table.shape[1], geo.seq_len + steps - 1,
+                          geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, geo.cos_threshold)
+    ws = ts.alloc_workspace(shape, sel, dev)
+    cache = ts.CacheState.allocate(1, H, d, geo.top_k, geo.torch_dtype, dev)
+    hits = torch.zeros(steps, dtype=torch.int32, device=dev)
+    out = torch.empty(1, H, d, dtype=geo.torch_dtype, device=dev)
+
+    def run():
+        for t in range(steps):
+            ts.decode_step(shape, sel, qs[t], batch.k_pool, batch.v_pool, batch.block_table, lens[t],
+                           cache, hits[t:t + 1], out, ws)
+
+    run()
+    torch.cuda.synchronize()
+    cache.valid.zero_()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    hv = hits.cpu().tolist()
+    log(f"[{geo.name}] {steps} steps: {ms:.4f} ms/step, hit rate {sum(hv) / steps:.3f}")
+    res = {"workload": geo.name, "steps": steps, "decode_steps_per_s": 1e3 / ms, "ms_per_step": ms,
+           "hit_rate": sum(hv) / steps, "hits": "".join(str(h) for h in hv)}
+    del batch, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(geo, host):
     """The fp64 oracle, as it stands, on one decode step of layer 0."""
     from oracle import tokenselect_oracle as ora
@@ -180,6 +267,10 @@ def main():
         secondary = {"workload": g1.name, "N": g1.seq_len, "decode_steps_per_s": 1e3 / r1["ms_per_step"],
                      "ms_per_step": r1["ms_per_step"], "score_ms": r1["score_ms"],
                      "score_gbps": r1["score_gbps"], "k_gbps": r1["k_gbps"], "rotating_layers": 8}
+    ragged = cache_seq = None
+    if not args.no_secondary:
+        ragged = time_ragged(wl.workload("llama3-8b-ragged16"), max(8, args.steps // 4), 2, dev)
+        cache_seq = time_cache_sequence(wl.workload("qwen2-7b-cache256"), dev)
     cpu = cpu_baseline(geo, host) if host is not None else None
 
     ms = main_res["ms_per_step"]
@@ -207,6 +298,8 @@ def main():
         "k_stream_gbps": main_res["k_gbps"],
         "scored_tokens_per_s": main_res["tokens"] * 1e3 / ms,
         "secondary": secondary,
+        "ragged_batch": ragged,
+        "selection_cache": cache_seq,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
