@@ -34,6 +34,29 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per scoring launch from the committed counter summary, or None.
+
+    The summary records the sha256 of the score kernel source it was measured on;
+    if the source has changed since, the figure no longer describes the kernel.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "score_kernel_traffic_llama3-8b-1m.md")
+    src = os.path.join(ROOT, "token_level_sparse_amd", "csrc", "score.hip")
+    try:
+        fields = {}
+        for line in open(path):
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "score_source_sha256"):
+                k, v = line.split(":", 1)
+                fields[k] = v.strip()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if fields.get("score_source_sha256") != digest:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def score_bytes_per_token(geo) -> float:
     """Algorithmic bytes the scoring kernel moves per cached token.
 
@@ -216,6 +239,34 @@ def time_cache_sequence(geo, dev):
     return res
 
 
+def counter_run(geo, dev, launches=4, layers=4):
+    """Short program for rocprofv3 --pmc passes: a few scoring launches on the 1M
+    workload, then a plain device copy of 1 GiB (the calibration kernel whose true
+    traffic is known: 1 GiB read, 1 GiB written)."""
+    import torch
+    import token_level_sparse_amd as ts
+    Ls = [Layer(geo, l, dev) for l in range(layers)]
+    L0 = Ls[0]
+    shape = ts.make_shape(geo.num_q_heads, geo.num_kv_heads, 1, L0.block_table.shape[1], L0.total,
+                          geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, 2.0)
+    ws = ts.alloc_workspace(shape, sel, dev)
+    logits = torch.empty(geo.num_q_heads * L0.total, dtype=torch.float32, device=dev)
+    stats = torch.empty(geo.num_q_heads * 2, dtype=torch.float32, device=dev)
+    for s in range(launches):
+        L = Ls[s % layers]
+        ts.score(shape, sel, L.q, L.k_pool, L.block_table, L.seq_lens, logits, stats, ws)
+    torch.cuda.synchronize()
+    del Ls, ws, logits
+    torch.cuda.empty_cache()
+    x = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(launches):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"[counters] {launches} score launches and {launches} 1 GiB copies done")
+
+
 def cpu_baseline(geo, host):
     """The fp64 oracle, as it stands, on one decode step of layer 0."""
     from oracle import tokenselect_oracle as ora
@@ -243,6 +294,8 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="short program for rocprofv3 --pmc passes (scoring launches + a 1 GiB copy)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -257,6 +310,9 @@ def main():
     torch.cuda.set_device(0)
 
     geo = wl.workload("llama3-8b-1m")
+    if args.counters:
+        counter_run(geo, dev)
+        return
     main_res, host = time_workload(geo, args.layers, args.steps, args.warmup, dev,
                                    keep_host=not args.no_cpu_baseline)
     secondary = None
@@ -292,7 +348,8 @@ def main():
                    "top_k": geo.top_k, "n_local": geo.n_local, "page_size": geo.page_size,
                    "layers": args.layers, "cache": "every step reselects"},
         "roofline": {"bound": "hbm", "achieved": main_res["score_gbps"], "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": main_res["score_gbps"] / PEAK_HBM_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": main_res["score_gbps"] / PEAK_HBM_GBPS,
+                     "traffic": measured_traffic(),
                      "kernel": "score (tokenselect_score launch)",
                      "bytes_per_launch": main_res["score_bytes"], "launch_ms": main_res["score_ms"]},
         "k_stream_gbps": main_res["k_gbps"],
