@@ -25,6 +25,8 @@
 //   tile, keys above the exact threshold and keys equal to it, and write
 //   positions through a prefix over tiles; equal keys are taken in position
 //   order until k is reached, so the result is deterministic.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -32,6 +34,15 @@ namespace ts {
 namespace {
 
 constexpr int kThreads = 256;
+#ifndef TS_VOTE_MAX_GRID
+#define TS_VOTE_MAX_GRID 512
+#endif
+// Vote workgroups: each takes several tiles and flushes its histogram once.
+constexpr int kVoteMaxGrid = TS_VOTE_MAX_GRID;
+#ifndef TS_REFINE_MAX_GRID
+#define TS_REFINE_MAX_GRID 256
+#endif
+constexpr int kRefineMaxGrid = TS_REFINE_MAX_GRID;
 constexpr int kPerThread = kVoteTile / kThreads;   // positions per thread
 constexpr float kLog2eF = 1.4426950408889634f;
 
@@ -134,18 +145,32 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
   build_tables(tb, p);
   const int H = p.H, Hkv = H / G;
   const int total = tb.tile[p.b];
+  // The LDS histogram accumulates every tile this workgroup takes of one request
+  // and is flushed to the global histogram (atomics) when the request changes
+  // and at the end: fewer global atomics on the hot bins.
+  int cur_r = -1;
+  auto flush = [&](int r) {
+    __syncthreads();
+    uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads)
+      if (s_hist[i]) atomicAdd(&gh[i], s_hist[i]);
+  };
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int r = find_segment(tb.tile, p.b, tile);
     const int t = tile - tb.tile[r];
     const int N = p.seq_lens[r];
-    __syncthreads();
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_hist[i] = 0;
-    // x_hi = (z_hi - M_h) log2e - log2 Z_h; z - M is exact near the head maximum
-    for (int h = threadIdx.x; h < H; h += kThreads) {
-      s_m[h] = p.head_stats[((int64_t)r * H + h) * 2 + 0];
-      s_l[h] = __builtin_amdgcn_logf(p.head_stats[((int64_t)r * H + h) * 2 + 1]);
+    if (r != cur_r) {
+      if (cur_r >= 0) flush(cur_r);
+      __syncthreads();
+      for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_hist[i] = 0;
+      // x_hi = (z_hi - M_h) log2e - log2 Z_h; z - M is exact near the head maximum
+      for (int h = threadIdx.x; h < H; h += kThreads) {
+        s_m[h] = p.head_stats[((int64_t)r * H + h) * 2 + 0];
+        s_l[h] = __builtin_amdgcn_logf(p.head_stats[((int64_t)r * H + h) * 2 + 1]);
+      }
+      __syncthreads();
+      cur_r = r;
     }
-    __syncthreads();
     const int i0 = t * kVoteTile + threadIdx.x;
     const float* z = p.logits + tb.tok[r] * H;
     int idx[kPerThread];
@@ -184,11 +209,8 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
         atomicAdd(&s_hist[order_key(lv) >> (32 - kDigitBits0)], 1u);
       }
     }
-    __syncthreads();
-    uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads)
-      if (s_hist[i]) atomicAdd(&gh[i], s_hist[i]);
   }
+  if (cur_r >= 0) flush(cur_r);
 }
 
 // ---------------------------------------------------------------- TopK phases
@@ -205,46 +227,60 @@ struct SelectShared {
 
 // kPass 1: find digit 0 from hist[0], histogram digit 1 of matching keys into hist[1].
 // kPass 2: read digit 0 from state, find digit 1 from hist[1], histogram digit 2 into hist[2].
+// A workgroup finds a request's digit once, accumulates its LDS histogram over all
+// its tiles of that request and flushes it once.
 template <int kPass>
 __device__ void refine_phase(const VoteParams& p, SelectShared& sh) {
   const int total = sh.tb.tile[p.b];
   constexpr int kShift = (kPass == 1) ? (32 - kDigitBits0) : (32 - kDigitBits0 - kDigitBits1);
   constexpr int kNextBits = (kPass == 1) ? kDigitBits1 : kDigitBits2;
   constexpr int kNextShift = kShift - kNextBits;
+  int cur_r = -1;
+  uint32_t prefix = 0;
+  auto flush = [&](int r) {
+    __syncthreads();
+    uint32_t* gn = p.hist + ((int64_t)r * 3 + kPass) * kHistBins;
+    for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads)
+      if (sh.hist[i]) atomicAdd(&gn[i], sh.hist[i]);
+  };
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int r = find_segment(sh.tb.tile, p.b, tile);
     const int t = tile - sh.tb.tile[r];
     const int N = p.seq_lens[r];
     if (p.top_k >= N) continue;                       // whole request selected: no radix work
-    int32_t* st = p.state + r * 8;
-    const uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
     const int i0 = t * kVoteTile + threadIdx.x;
     uint32_t key[kPerThread];
     load_keys(p.vote + sh.tb.tok[r], i0, N, key);
-    __syncthreads();
-    uint32_t prefix;
-    if (kPass == 1) {
-      find_digit<1 << kDigitBits0>(gh, p.top_k, sh.dig, sh.w);
-      prefix = (uint32_t)sh.dig[0];
-      if (t == 0 && threadIdx.x == 0) { st[0] = sh.dig[0]; st[1] = sh.dig[1]; }
-    } else {
-      const int d0 = st[0], k0 = st[1];
-      find_digit<1 << kDigitBits1>(gh + kHistBins, k0, sh.dig, sh.w);
-      prefix = ((uint32_t)d0 << kDigitBits1) | (uint32_t)sh.dig[0];
-      if (t == 0 && threadIdx.x == 0) { st[2] = sh.dig[0]; st[3] = sh.dig[1]; }
+    if (r != cur_r) {
+      if (cur_r >= 0) flush(cur_r);
+      __syncthreads();
+      int32_t* st = p.state + r * 8;
+      const uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
+      if (kPass == 1) {
+        find_digit<1 << kDigitBits0>(gh, p.top_k, sh.dig, sh.w);
+        prefix = (uint32_t)sh.dig[0];
+        if (t == 0 && threadIdx.x == 0) { st[0] = sh.dig[0]; st[1] = sh.dig[1]; }
+      } else {
+        const int d0 = st[0], k0 = st[1];
+        find_digit<1 << kDigitBits1>(gh + kHistBins, k0, sh.dig, sh.w);
+        prefix = ((uint32_t)d0 << kDigitBits1) | (uint32_t)sh.dig[0];
+        if (t == 0 && threadIdx.x == 0) { st[2] = sh.dig[0]; st[3] = sh.dig[1]; }
+      }
+      for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads) sh.hist[i] = 0;
+      __syncthreads();
+      cur_r = r;
+    } else if (t == 0 && threadIdx.x == 0) {
+      int32_t* st = p.state + r * 8;
+      if (kPass == 1) { st[0] = sh.dig[0]; st[1] = sh.dig[1]; }
+      else { st[2] = sh.dig[0]; st[3] = sh.dig[1]; }
     }
-    for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads) sh.hist[i] = 0;
-    __syncthreads();
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
       if (i0 + e * kThreads < N && (key[e] >> kShift) == prefix)
         atomicAdd(&sh.hist[(key[e] >> kNextShift) & ((1u << kNextBits) - 1)], 1u);
     }
-    __syncthreads();
-    uint32_t* gn = p.hist + ((int64_t)r * 3 + kPass) * kHistBins;
-    for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads)
-      if (sh.hist[i]) atomicAdd(&gn[i], sh.hist[i]);
   }
+  if (cur_r >= 0) flush(cur_r);
 }
 
 // Exact threshold key of request r and how many keys equal to it are taken.
@@ -380,18 +416,20 @@ hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist) 
     hipLaunchKernelGGL(zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.hist, n);
   }
   const dim3 grid(p.grid), block(kThreads);
+  const dim3 vgrid(std::min(p.grid, kVoteMaxGrid));
   switch (p.G) {
-    case 1: hipLaunchKernelGGL(vote_kernel<1>, grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL(vote_kernel<2>, grid, block, 0, s, p); break;
-    case 3: hipLaunchKernelGGL(vote_kernel<3>, grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL(vote_kernel<4>, grid, block, 0, s, p); break;
-    case 5: hipLaunchKernelGGL(vote_kernel<5>, grid, block, 0, s, p); break;
-    case 6: hipLaunchKernelGGL(vote_kernel<6>, grid, block, 0, s, p); break;
-    case 7: hipLaunchKernelGGL(vote_kernel<7>, grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL(vote_kernel<8>, grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL(vote_kernel<1>, vgrid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL(vote_kernel<2>, vgrid, block, 0, s, p); break;
+    case 3: hipLaunchKernelGGL(vote_kernel<3>, vgrid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL(vote_kernel<4>, vgrid, block, 0, s, p); break;
+    case 5: hipLaunchKernelGGL(vote_kernel<5>, vgrid, block, 0, s, p); break;
+    case 6: hipLaunchKernelGGL(vote_kernel<6>, vgrid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL(vote_kernel<7>, vgrid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL(vote_kernel<8>, vgrid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(select_phase_kernel<1>, grid, block, 0, s, p);
+  const dim3 rgrid(std::min(p.grid, kRefineMaxGrid));
+  hipLaunchKernelGGL(select_phase_kernel<1>, rgrid, block, 0, s, p);
   hipLaunchKernelGGL(select_phase_kernel<2>, grid, block, 0, s, p);
   hipLaunchKernelGGL(select_phase_kernel<3>, grid, block, 0, s, p);
   hipLaunchKernelGGL(select_phase_kernel<4>, grid, block, 0, s, p);
