@@ -198,7 +198,8 @@ def request_lengths(gen: torch.Generator, geo: Geometry, device) -> List[int]:
 
 def page_requests(requests: List[Request], geo: Geometry, gen: Optional[torch.Generator],
                   device, permute: bool = True, pad_value: float = float("nan"),
-                  spare_pages: int = 0, stride: Optional[int] = None) -> PagedBatch:
+                  spare_pages: int = 0, stride: Optional[int] = None,
+                  pools: Optional[tuple] = None) -> PagedBatch:
     """Lay requests out in one pool of pages [pages][H_kv][P][d].
 
     Token i of request r lives at pool page block_table[r][i // P], slot i % P.
@@ -206,7 +207,8 @@ def page_requests(requests: List[Request], geo: Geometry, gen: Optional[torch.Ge
     when ``permute`` is off). Slots past a request's last token, and
     ``spare_pages`` unused pages, hold ``pad_value`` so that a kernel reading
     them into a result shows up. Block-table entries past a request's last page
-    are -1.
+    are -1. ``pools`` = (k_pool, v_pool) fills caller-allocated pools of the
+    right shape instead of allocating new ones.
     """
     P = geo.page_size
     Hkv, d = geo.num_kv_heads, geo.head_dim
@@ -217,8 +219,15 @@ def page_requests(requests: List[Request], geo: Geometry, gen: Optional[torch.Ge
     else:
         perm = torch.arange(total_pages, device=device)
     stride = stride or max(n_pages)
-    k_pool = torch.full((total_pages, Hkv, P, d), pad_value, dtype=geo.torch_dtype, device=device)
-    v_pool = torch.full_like(k_pool, pad_value)
+    if pools is None:
+        k_pool = torch.full((total_pages, Hkv, P, d), pad_value, dtype=geo.torch_dtype, device=device)
+        v_pool = torch.full_like(k_pool, pad_value)
+    else:
+        k_pool, v_pool = pools
+        assert k_pool.shape == (total_pages, Hkv, P, d) and v_pool.shape == k_pool.shape
+        assert k_pool.dtype == geo.torch_dtype and v_pool.dtype == geo.torch_dtype
+        k_pool.fill_(pad_value)
+        v_pool.fill_(pad_value)
     bt = torch.full((len(requests), stride), -1, dtype=torch.int32, device=device)
     base = 0
     for r, req in enumerate(requests):
@@ -241,7 +250,7 @@ def page_requests(requests: List[Request], geo: Geometry, gen: Optional[torch.Ge
 
 def make_batch(geo: Geometry, device="cpu", layer: int = 0, permute: bool = True,
                scale_spread: bool = True, pad_value: float = float("nan"),
-               seq_len: Optional[int] = None) -> PagedBatch:
+               seq_len: Optional[int] = None, pools: Optional[tuple] = None) -> PagedBatch:
     """Draw a whole workload (one layer) and page it.
 
     Single-request workloads use ``seq_len`` (default the workload's N). The
@@ -253,7 +262,7 @@ def make_batch(geo: Geometry, device="cpu", layer: int = 0, permute: bool = True
     else:
         lens = [seq_len or geo.seq_len] * geo.batch
     reqs = [make_request(gen, geo, n, device, scale_spread=scale_spread) for n in lens]
-    return page_requests(reqs, geo, gen, device, permute=permute, pad_value=pad_value)
+    return page_requests(reqs, geo, gen, device, permute=permute, pad_value=pad_value, pools=pools)
 
 
 def ar1_queries(geo: Geometry, q0_master: torch.Tensor, steps: int, seed: int, device="cpu"):
