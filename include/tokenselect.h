@@ -162,6 +162,65 @@ ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel,
                                   const ts_cache* cache, int32_t* hit, void* out,
                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- chunk-wise prefill
+   A prefill chunk of request r is its c_r newest tokens: their K/V are already in
+   the pool at positions [P_r, P_r + c_r) with P_r = N_r - c_r (seq_lens[r] = N_r
+   counts the chunk). The chunk selects once from the mean of its c_r queries over
+   the past positions [0, P_r), and chunk query j attends
+     S_j = TopK_r  united with  [max(0, P_r - n_local), P_r + j]
+   (the window of n_local positions before the chunk plus the chunk's causal part).
+   Sources: deepnotes page, selection frequency of the prefill stage (the c x d
+   query block of a chunk is averaged and the mean goes through the selection
+   function) and the selective sparse attention formalisation; blog review section
+   3.2 (chunk-wise selection in prefill: the chunk shares one selection).
+   Layouts (in addition to the decode ones):
+     q_chunk    [batch][max_chunk][H][d] element type dtype; rows j >= c_r unused
+     chunk_lens int32 [batch] device: c_r, 1 <= c_r <= min(max_chunk, N_r)
+     out        [batch][max_chunk][H][d] element type dtype; rows j >= c_r untouched
+     sel_idx    int32 [batch][top_k]: TopK over the past, ascending, sel_count[r] =
+                min(top_k, P_r) entries (0 for a first chunk, P_r = 0)
+   Out-of-contract chunk lengths are clamped on the device (no access leaves the
+   request's pages; results are then unspecified). The decode entry points' rules on
+   pointers, streams, ownership and errors apply. */
+
+/* Workspace bytes of the prefill entry points for chunks of up to max_chunk
+   tokens; 0 if the arguments are invalid. */
+size_t tokenselect_prefill_workspace_size(const ts_shape* shape, const ts_select* sel,
+                                          int32_t max_chunk);
+
+/* Selection of a chunk: qbar_h = (1/c_r) sum_j q_chunk[r][j][h] (fp64 sum, rounded
+   once to fp32), then steps 1-4 of the decode path with qbar over [0, P_r): logits
+   z = score_scale * <qbar_h, K>, per-head (M_h, Z_h), log2 head soft vote and TopK.
+   logits, head_stats and vote are optional outputs in the decode layouts with
+   N_r replaced by P_r (NULL keeps them in the workspace). */
+ts_status tokenselect_prefill_select(const ts_shape* shape, const ts_select* sel, int32_t max_chunk,
+                                     const void* q_chunk, const int32_t* chunk_lens,
+                                     const void* k_pool, const int32_t* block_table,
+                                     const int32_t* seq_lens, float* logits, float* head_stats,
+                                     float* vote, int32_t* sel_idx, int32_t* sel_count, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
+/* Chunk attention: out[r][j][h] = sum_{i in S_j} softmax_i(attn_scale * <q_h, K_{h/G}[i]>)
+   V_{h/G}[i] for every chunk query j < c_r, given TopK_r in sel_idx / sel_count
+   (ascending, entries in [0, P_r)). Runs on the matrix cores (bf16: products in
+   bf16 with fp32 accumulation, probabilities rounded to bf16 for the value product;
+   fp32: fp32 throughout). */
+ts_status tokenselect_chunk_attn(const ts_shape* shape, const ts_select* sel, int32_t max_chunk,
+                                 const void* q_chunk, const int32_t* chunk_lens,
+                                 const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* sel_idx, const int32_t* sel_count, void* out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One prefill chunk: tokenselect_prefill_select (TopK into sel_idx / sel_count)
+   followed by tokenselect_chunk_attn, with no host synchronisation. */
+ts_status tokenselect_prefill_chunk(const ts_shape* shape, const ts_select* sel, int32_t max_chunk,
+                                    const void* q_chunk, const int32_t* chunk_lens,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    int32_t* sel_idx, int32_t* sel_count, void* out, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* tokenselect_status_string(ts_status status);
 

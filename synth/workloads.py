@@ -48,6 +48,7 @@ class Geometry:
     seed: int = 0
     scale_lo: float = 1.0
     scale_hi: float = 1000.0
+    chunk: int = 0        # prefill chunk size c (chunk workloads); seq_len counts the chunk
 
     @property
     def group(self) -> int:
@@ -82,7 +83,26 @@ CONFIGS = {
         name="qwen2-7b-cache256", dtype="bf16", num_q_heads=28, num_kv_heads=4, head_dim=128,
         page_size=16, top_k=2048, n_local=512, n_planted=64, seq_len=131072, steps=256,
         cos_threshold=0.9, seed=4000),
+    # Chunk-wise prefill (blog page section 3.3, Fig. 5: chunk 512, 128K cached tokens,
+    # 4K attended = 3072 selected + 512 local + the 512-token chunk; Fig. 7c: 1M
+    # cached tokens with a 2048-token selection budget).
+    "prefill-tiny-f32": Geometry(
+        name="prefill-tiny-f32", dtype="f32", num_q_heads=8, num_kv_heads=2, head_dim=128,
+        page_size=16, top_k=256, n_local=64, n_planted=32, seq_len=8192, chunk=64, seed=5000),
+    "prefill-llama3-128k": Geometry(
+        name="prefill-llama3-128k", dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+        page_size=16, top_k=3072, n_local=512, n_planted=64, seq_len=131072, chunk=512,
+        layers=8, seed=6000),
+    "prefill-llama3-1m": Geometry(
+        name="prefill-llama3-1m", dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+        page_size=16, top_k=2048, n_local=512, n_planted=128, seq_len=1048576, chunk=512,
+        seed=7000),
 }
+
+# Spread of a chunk's queries around their shared master query: q_j = q_master +
+# CHUNK_SIGMA * eps_j, eps_j ~ N(0, I_d), so neighbouring queries have cosine
+# about 1 / (1 + CHUNK_SIGMA^2) = 0.945 (blog page section 2, Fig. 3a).
+CHUNK_SIGMA = 0.24
 
 
 def workload(name: str, **overrides) -> Geometry:
@@ -287,3 +307,52 @@ def ar1_queries(geo: Geometry, q0_master: torch.Tensor, steps: int, seed: int, d
         qs[t] = cur.to(geo.torch_dtype)
         rhos[t] = rho
     return qs, rhos
+
+
+@dataclass
+class ChunkBatch:
+    """A prefill chunk per request: the paged cache (chunk tokens included) and the
+    chunk's queries."""
+
+    paged: PagedBatch
+    q_chunk: torch.Tensor        # [b][c][H][d]
+    chunk_lens: torch.Tensor     # int32 [b]
+    seq_lens: torch.Tensor       # int32 [b]: P_r + c_r
+    past_lens: List[int] = field(default_factory=list)
+
+
+def make_chunk_batch(geo: Geometry, device="cpu", layer: int = 0, permute: bool = True,
+                     pad_value: float = float("nan"), seq_len: Optional[int] = None,
+                     chunk_lens: Optional[List[int]] = None,
+                     pools: Optional[tuple] = None, scale_spread: bool = True) -> ChunkBatch:
+    """Draw a prefill-chunk workload and page it.
+
+    Request r has N_r = seq_len tokens (ragged workloads draw N_r as in decode); its
+    last c = geo.chunk tokens are the chunk and its first N_r - c the past, which
+    holds the planted critical tokens. The c chunk queries are q_master + CHUNK_SIGMA
+    * eps_j, drawn after the request and rounded to the storage type. ``chunk_lens``
+    shortens the chunk of some requests to c_r <= c (their last c - c_r drawn tokens
+    stay in the pool, unused).
+    """
+    gen = _gen(geo.seed + layer, device)
+    c = geo.chunk
+    assert c >= 1
+    if geo.batch > 1 and geo.min_len:
+        lens = request_lengths(gen, geo, device)
+    else:
+        lens = [seq_len or geo.seq_len] * geo.batch
+    assert all(n >= c for n in lens)
+    reqs, qcs = [], []
+    for n in lens:
+        req = make_request(gen, geo, n - c, device, extra_tokens=c, scale_spread=scale_spread)
+        eps = torch.randn(c, geo.num_q_heads, geo.head_dim, generator=gen, device=device,
+                          dtype=torch.float64)
+        qcs.append((req.q_master[None] + CHUNK_SIGMA * eps).to(geo.torch_dtype))
+        reqs.append(req)
+    paged = page_requests(reqs, geo, gen, device, permute=permute, pad_value=pad_value, pools=pools)
+    cl = list(chunk_lens) if chunk_lens is not None else [c] * len(lens)
+    assert len(cl) == len(lens) and all(1 <= x <= c for x in cl)
+    past = [n - c for n in lens]
+    seq = torch.tensor([p + x for p, x in zip(past, cl)], dtype=torch.int32, device=device)
+    return ChunkBatch(paged=paged, q_chunk=torch.stack(qcs), chunk_lens=torch.tensor(cl, dtype=torch.int32,
+                      device=device), seq_lens=seq, past_lens=past)

@@ -168,3 +168,127 @@ def check_request(po: PathOut, r: int, req: wl.Request, geo: wl.Geometry, top_k=
     err = check_attention(po.out[r], q, K, V, po.T[r], K.shape[1], L, geo.attn_scale,
                           geo.dtype == "f32")
     return dict(n_loose=n_loose, n_diff=n_diff, attn_err=err)
+
+
+# ---------------------------------------------------------------- chunk-wise prefill
+@dataclass
+class PrefillOut:
+    logits: List[np.ndarray]      # per request [H][P_r]
+    stats: np.ndarray             # [b][H][2]
+    vote: List[np.ndarray]        # per request [P_r]
+    T: List[np.ndarray]           # per request ascending TopK over the past
+    out: np.ndarray               # [b][max_chunk][H][d] (fp32 copy)
+    raw: dict
+
+
+def run_prefill(cb: wl.ChunkBatch, geo: wl.Geometry, top_k=None, n_local=None, score_scale=1.0,
+                sel_override=None) -> PrefillOut:
+    """prefill_select then chunk_attn through the C ABI; also runs prefill_chunk and
+    checks that the one-call path gives bit-identical TopK and outputs."""
+    pb = cb.paged
+    b = pb.q.shape[0]
+    H, d = geo.num_q_heads, geo.head_dim
+    mc = cb.q_chunk.shape[1]
+    lens = cb.seq_lens.cpu().tolist()
+    past = [n - c for n, c in zip(lens, cb.chunk_lens.cpu().tolist())]
+    max_total = max(sum(lens), b)
+    shape = ts.make_shape(H, geo.num_kv_heads, b, pb.block_table.shape[1], max_total, geo.torch_dtype)
+    sel = select_params(geo, top_k, n_local, score_scale)
+    k = sel.top_k
+    dev = pb.q.device
+    ws = ts.alloc_prefill_workspace(shape, sel, mc, dev)
+    logits = torch.full((H * max_total,), float("nan"), dtype=torch.float32, device=dev)
+    stats = torch.full((b * H * 2,), float("nan"), dtype=torch.float32, device=dev)
+    vote = torch.full((max_total,), float("nan"), dtype=torch.float32, device=dev)
+    sel_idx = torch.full((b, k), -7, dtype=torch.int32, device=dev)
+    sel_count = torch.full((b,), -7, dtype=torch.int32, device=dev)
+    out = torch.full((b, mc, H, d), float("nan"), dtype=geo.torch_dtype, device=dev)
+    ts.prefill_select(shape, sel, mc, cb.q_chunk, cb.chunk_lens, pb.k_pool, pb.block_table, cb.seq_lens,
+                      logits, stats, vote, sel_idx, sel_count, ws)
+    si, sc = (sel_idx, sel_count) if sel_override is None else sel_override
+    ts.chunk_attn(shape, sel, mc, cb.q_chunk, cb.chunk_lens, pb.k_pool, pb.v_pool, pb.block_table,
+                  cb.seq_lens, si, sc, out, ws)
+    # one-call path on a fresh workspace
+    ws2 = ts.alloc_prefill_workspace(shape, sel, mc, dev)
+    sel_idx2 = torch.full((b, k), -9, dtype=torch.int32, device=dev)
+    sel_count2 = torch.full((b,), -9, dtype=torch.int32, device=dev)
+    out2 = torch.full((b, mc, H, d), float("nan"), dtype=geo.torch_dtype, device=dev)
+    ts.prefill_chunk(shape, sel, mc, cb.q_chunk, cb.chunk_lens, pb.k_pool, pb.v_pool, pb.block_table,
+                     cb.seq_lens, sel_idx2, sel_count2, out2, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_count, sel_count2)
+    for r in range(b):
+        n = int(sel_count[r])
+        assert torch.equal(sel_idx[r, :n], sel_idx2[r, :n])
+    if sel_override is None:
+        assert torch.equal(out.view(torch.uint8) if out.dtype == torch.bfloat16 else out.view(torch.int32),
+                           out2.view(torch.uint8) if out2.dtype == torch.bfloat16 else out2.view(torch.int32)), \
+            "prefill_chunk differs from prefill_select + chunk_attn"
+    lg, vt = logits.cpu().numpy(), vote.cpu().numpy()
+    si_h, sc_h = sel_idx.cpu().numpy(), sel_count.cpu().numpy()
+    G = H // geo.num_kv_heads
+    L, V, T = [], [], []
+    off = 0
+    for r in range(b):
+        P = past[r]
+        blk = lg[off * H: off * H + H * P].reshape(geo.num_kv_heads, P, G)
+        L.append(np.ascontiguousarray(blk.transpose(0, 2, 1)).reshape(H, P))
+        V.append(vt[off: off + P])
+        assert sc_h[r] == min(k, P), (r, sc_h[r], k, P)
+        T.append(si_h[r, : sc_h[r]].astype(np.int64))
+        off += P
+    return PrefillOut(L, stats.cpu().numpy().reshape(b, H, 2), V, T, np32(out),
+                      dict(sel_idx=sel_idx, sel_count=sel_count, out=out))
+
+
+def check_prefill_selection(po: PrefillOut, r: int, cb: wl.ChunkBatch, geo: wl.Geometry, top_k=None,
+                            score_scale=1.0):
+    """Logits, stats, votes and TopK of request r against the oracle run with the
+    exact fp64 mean query over the past."""
+    from oracle import prefill_oracle as pre
+    k = geo.top_k if top_k is None else top_k
+    req = cb.paged.requests[r]
+    c = int(cb.chunk_lens[r])
+    P = int(cb.seq_lens[r]) - c
+    if P == 0:
+        assert po.T[r].size == 0
+        return dict(n_diff=0)
+    Qc = np32(cb.q_chunk[r, :c])
+    K = np32(req.k[:, :P])
+    qbar = pre.chunk_mean_query(Qc)
+    sel = ora.select(qbar, K, k, score_scale)
+    check_logits(po.logits[r], qbar, K, sel["z"], score_scale)
+    check_stats(po.stats[r], sel, qbar, K, score_scale)
+    rel, n_loose = check_vote(po.vote[r], sel, qbar, K, score_scale)
+    n_diff = check_topk(po.T[r], po.vote[r], sel, rel, k)
+    return dict(n_diff=n_diff, n_loose=n_loose, T_ora=sel["T"])
+
+
+def check_chunk_attention(po: PrefillOut, r: int, cb: wl.ChunkBatch, geo: wl.Geometry, T,
+                          n_local=None, rows=None, fp32_factor=1.0):
+    """Chunk attention of request r (rows j of the chunk, all by default) against the
+    oracle over the attended sets built from T."""
+    from oracle import prefill_oracle as pre
+    L = geo.n_local if n_local is None else n_local
+    req = cb.paged.requests[r]
+    c = int(cb.chunk_lens[r])
+    N = int(cb.seq_lens[r])
+    P = N - c
+    K, V = np32(req.k[:, :N]), np32(req.v[:, :N])
+    Qc = np32(cb.q_chunk[r, :c])
+    sets = pre.chunk_sets(T, P, c, L)
+    fp32 = geo.dtype == "f32"
+    worst = 0.0
+    for j in (range(c) if rows is None else rows):
+        ref = ora.sparse_attention(Qc[j], K, V, sets[j], geo.attn_scale)
+        err = np.abs(po.out[r, j].astype(np.float64) - ref)
+        if fp32:
+            lim = 1e-4 + fp32_factor * tol.attn_budget(Qc[j], K, V, sets[j], geo.attn_scale, ref)
+        else:
+            lim = 2e-2
+        assert np.all(err <= lim), f"chunk row {j}: max-abs {err.max():.3e} (limit {np.max(lim):.3e})"
+        worst = max(worst, float(err.max()))
+    # rows past the chunk are untouched
+    if c < po.out.shape[1]:
+        assert np.isnan(po.out[r, c:]).all(), "rows past the chunk were written"
+    return worst

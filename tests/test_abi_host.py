@@ -140,3 +140,44 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(4)
     with pytest.raises(ValueError):
         ts.score(shape, sel, x, x, x, x, x, x, x)
+
+
+# ---------------------------------------------------------------- chunk-wise prefill
+def test_prefill_workspace_size(lib):
+    shape, sel = _shape(), _sel()
+    dec = ts.workspace_size(shape, sel)
+    a = ts.prefill_workspace_size(shape, sel, 512)
+    b = ts.prefill_workspace_size(shape, sel, 1024)
+    # the decode regions plus the mean query and the chunk partials
+    assert a > dec and b > a and a % 256 == 0
+    assert a - dec >= 512 * 32 * (128 + 4) * 4
+    assert ts.prefill_workspace_size(shape, sel, 0) == 0
+    assert ts.prefill_workspace_size(_shape(num_q_heads=30), sel, 512) == 0
+    assert ts.prefill_workspace_size(shape, sel, 131073) == 0     # chunk above max_total_tokens
+
+
+def test_prefill_validation_before_launch(lib):
+    shape, sel = _shape(), _sel()
+    big = 1 << 40
+    st = lib.tokenselect_prefill_chunk(ctypes.byref(shape), ctypes.byref(sel), 0, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
+    assert st == ts.TS_ERR_INVALID_ARG and "max_chunk" in lib.tokenselect_last_error().decode()
+    st = lib.tokenselect_prefill_chunk(ctypes.byref(shape), ctypes.byref(sel), 512, FAKE, None, FAKE,
+                                       FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
+    assert st == ts.TS_ERR_INVALID_ARG and "chunk_lens" in lib.tokenselect_last_error().decode()
+    st = lib.tokenselect_chunk_attn(ctypes.byref(shape), ctypes.byref(sel), 512, FAKE, FAKE, FAKE,
+                                    None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
+    assert st == ts.TS_ERR_INVALID_ARG and "v_pool" in lib.tokenselect_last_error().decode()
+    need = ts.prefill_workspace_size(shape, sel, 512)
+    st = lib.tokenselect_prefill_select(ctypes.byref(shape), ctypes.byref(sel), 512, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, need - 1, None)
+    assert st == ts.TS_ERR_WORKSPACE
+    # the decode-sized workspace is too small for a chunk
+    st = lib.tokenselect_prefill_select(ctypes.byref(shape), ctypes.byref(sel), 512, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE,
+                                        ts.workspace_size(shape, sel), None)
+    assert st == ts.TS_ERR_WORKSPACE
+    misaligned = ctypes.c_void_p(4096 + 8)
+    st = lib.tokenselect_prefill_chunk(ctypes.byref(shape), ctypes.byref(sel), 512, misaligned, FAKE,
+                                       FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
+    assert st == ts.TS_ERR_INVALID_ARG and "16-byte" in lib.tokenselect_last_error().decode()

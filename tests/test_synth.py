@@ -105,3 +105,17 @@ def test_ar1_queries_follow_the_recursion():
         a, b = qs[t - 1].double().flatten(), qs[t].double().flatten()
         c = float(a @ b / (a.norm() * b.norm()))
         assert abs(c - rho[t]) < 0.05
+
+
+def test_chunk_batch_layout_and_seed():
+    geo = wl.workload("prefill-tiny-f32", seq_len=700, chunk=40, batch=2, min_len=300, max_len=900)
+    a = wl.make_chunk_batch(geo, "cpu", chunk_lens=[40, 7])
+    b = wl.make_chunk_batch(geo, "cpu", chunk_lens=[40, 7])
+    assert torch.equal(a.q_chunk, b.q_chunk) and torch.equal(a.paged.k_pool.nan_to_num(), b.paged.k_pool.nan_to_num())
+    assert a.q_chunk.shape == (2, 40, 8, 128)
+    for r in range(2):
+        req = a.paged.requests[r]
+        P = a.past_lens[r]
+        assert int(a.seq_lens[r]) == P + int(a.chunk_lens[r])
+        assert req.k.shape[1] == P + 40
+        assert int(req.planted_pos.max()) < P          # critical tokens in the past only

@@ -28,6 +28,10 @@ ENTRY_POINTS = (
     "tokenselect_vote_topk",
     "tokenselect_sparse_attn",
     "tokenselect_decode_step",
+    "tokenselect_prefill_workspace_size",
+    "tokenselect_prefill_select",
+    "tokenselect_chunk_attn",
+    "tokenselect_prefill_chunk",
     "tokenselect_status_string",
     "tokenselect_last_error",
 )
@@ -96,6 +100,17 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tokenselect_decode_step.argtypes = [sp, selp, vp, vp, vp, vp, vp, ctypes.POINTER(Cache),
                                             vp, vp, vp, sz, vp]
     lib.tokenselect_decode_step.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.tokenselect_prefill_workspace_size.argtypes = [sp, selp, i32]
+    lib.tokenselect_prefill_workspace_size.restype = sz
+    lib.tokenselect_prefill_select.argtypes = [sp, selp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               vp, sz, vp]
+    lib.tokenselect_prefill_select.restype = ctypes.c_int
+    lib.tokenselect_chunk_attn.argtypes = [sp, selp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.tokenselect_chunk_attn.restype = ctypes.c_int
+    lib.tokenselect_prefill_chunk.argtypes = [sp, selp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              sz, vp]
+    lib.tokenselect_prefill_chunk.restype = ctypes.c_int
     lib.tokenselect_status_string.argtypes = [ctypes.c_int]
     lib.tokenselect_status_string.restype = ctypes.c_char_p
     lib.tokenselect_last_error.argtypes = []
@@ -204,3 +219,46 @@ def decode_step(shape, sel, q, k_pool, v_pool, block_table, seq_lens, cache: Cac
                                        _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                                        _ptr(seq_lens), ctypes.byref(cs), _ptr(hit), _ptr(out),
                                        _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------- chunk-wise prefill
+def prefill_workspace_size(shape: Shape, sel: Select, max_chunk: int) -> int:
+    return int(load_library().tokenselect_prefill_workspace_size(ctypes.byref(shape), ctypes.byref(sel),
+                                                                 int(max_chunk)))
+
+
+def alloc_prefill_workspace(shape: Shape, sel: Select, max_chunk: int, device="cuda") -> torch.Tensor:
+    n = prefill_workspace_size(shape, sel, max_chunk)
+    if n == 0:
+        raise TokenSelectError(TS_ERR_INVALID_ARG, load_library().tokenselect_last_error().decode())
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def prefill_select(shape, sel, max_chunk, q_chunk, chunk_lens, k_pool, block_table, seq_lens,
+                   logits, head_stats, vote, sel_idx, sel_count, ws, stream=None):
+    lib = load_library()
+    _check(lib.tokenselect_prefill_select(ctypes.byref(shape), ctypes.byref(sel), int(max_chunk),
+                                          _ptr(q_chunk), _ptr(chunk_lens), _ptr(k_pool),
+                                          _ptr(block_table), _ptr(seq_lens), _ptr(logits),
+                                          _ptr(head_stats), _ptr(vote), _ptr(sel_idx),
+                                          _ptr(sel_count), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def chunk_attn(shape, sel, max_chunk, q_chunk, chunk_lens, k_pool, v_pool, block_table, seq_lens,
+               sel_idx, sel_count, out, ws, stream=None):
+    lib = load_library()
+    _check(lib.tokenselect_chunk_attn(ctypes.byref(shape), ctypes.byref(sel), int(max_chunk),
+                                      _ptr(q_chunk), _ptr(chunk_lens), _ptr(k_pool), _ptr(v_pool),
+                                      _ptr(block_table), _ptr(seq_lens), _ptr(sel_idx),
+                                      _ptr(sel_count), _ptr(out), _ptr(ws), ws.numel(),
+                                      _stream(stream)))
+
+
+def prefill_chunk(shape, sel, max_chunk, q_chunk, chunk_lens, k_pool, v_pool, block_table, seq_lens,
+                  sel_idx, sel_count, out, ws, stream=None):
+    lib = load_library()
+    _check(lib.tokenselect_prefill_chunk(ctypes.byref(shape), ctypes.byref(sel), int(max_chunk),
+                                         _ptr(q_chunk), _ptr(chunk_lens), _ptr(k_pool), _ptr(v_pool),
+                                         _ptr(block_table), _ptr(seq_lens), _ptr(sel_idx),
+                                         _ptr(sel_count), _ptr(out), _ptr(ws), ws.numel(),
+                                         _stream(stream)))

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <stdint.h>
+
 #include <algorithm>
 #include <string>
 
@@ -202,7 +204,161 @@ ts::AttnParams attn_params(const ts_shape& s, const ts_select& sel, const void* 
   return p;
 }
 
+// ---------------------------------------------------------------- prefill
+struct PrefillLayout {
+  Layout dec;                  // the decode regions, used by the selection over the past
+  size_t qbar, past, cpart, total;
+};
+
+int chunk_splits_for(const ts_shape& s, const ts_select& sel, int max_chunk) {
+  return ts::chunk_splits(eff_top_k(s, sel), eff_local(s, sel), max_chunk);
+}
+
+PrefillLayout prefill_layout(const ts_shape& s, const ts_select& sel, int max_chunk) {
+  PrefillLayout L;
+  L.dec = layout(s, sel);
+  size_t off = L.dec.total;
+  const size_t bH = (size_t)s.batch * s.num_q_heads;
+  L.qbar = off;  off += align_up(sizeof(float) * bH * ts::kHeadDim);
+  L.past = off;  off += align_up(sizeof(int32_t) * (size_t)s.batch);
+  L.cpart = off; off += align_up(sizeof(float) * bH * (size_t)max_chunk *
+                                 chunk_splits_for(s, sel, max_chunk) * ts::kChunkPartStride);
+  L.total = off;
+  return L;
+}
+
+ts_status check_chunk(const ts_shape& s, const ts_select& sel, int max_chunk) {
+  if (max_chunk < 1) return fail(TS_ERR_INVALID_ARG, "max_chunk %d < 1", max_chunk);
+  if ((int64_t)max_chunk > s.max_total_tokens)
+    return fail(TS_ERR_INVALID_ARG, "max_chunk %d > max_total_tokens %lld", max_chunk,
+                (long long)s.max_total_tokens);
+  const int G = s.num_q_heads / s.num_kv_heads;
+  const int64_t tiles = cdiv((int64_t)max_chunk * G, ts::kChunkRows) * s.num_kv_heads * s.batch;
+  if (tiles > INT32_MAX || (int64_t)s.batch * max_chunk > INT32_MAX)
+    return fail(TS_ERR_UNSUPPORTED, "batch x max_chunk %lld too large", (long long)s.batch * max_chunk);
+  if (chunk_splits_for(s, sel, max_chunk) > 65535)
+    return fail(TS_ERR_UNSUPPORTED, "top_k + n_local + max_chunk too large for the split grid");
+  return TS_OK;
+}
+
+ts_status check_prefill_ws(const ts_shape& s, const ts_select& sel, int max_chunk, const void* ws,
+                           size_t ws_bytes) {
+  const size_t need = prefill_layout(s, sel, max_chunk).total;
+  if (!ws) return fail(TS_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws_bytes < need)
+    return fail(TS_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(TS_ERR_INVALID_ARG, "workspace must be %zu-byte aligned", kAlign);
+  return TS_OK;
+}
+
+ts::ChunkParams chunk_params(const ts_shape& s, const ts_select& sel, int max_chunk, const void* q,
+                             const int32_t* chunk_lens, const int32_t* seq, const void* k_pool,
+                             const void* v_pool, const int32_t* bt, const int32_t* sel_idx,
+                             const int32_t* sel_count, void* out, void* ws) {
+  const PrefillLayout L = prefill_layout(s, sel, max_chunk);
+  ts::ChunkParams p{};
+  p.q = q; p.chunk_lens = chunk_lens; p.seq_lens = seq; p.k_pool = k_pool; p.v_pool = v_pool;
+  p.block_table = bt; p.sel_idx = sel_idx; p.sel_count = sel_count;
+  p.qbar = at<float>(ws, L.qbar); p.past_lens = at<int32_t>(ws, L.past);
+  p.partials = at<float>(ws, L.cpart); p.out = out;
+  p.H = s.num_q_heads; p.Hkv = s.num_kv_heads; p.b = s.batch; p.stride = s.block_table_stride;
+  p.max_chunk = max_chunk; p.sel_stride = sel.top_k; p.n_local = sel.n_local;
+  p.splits = chunk_splits_for(s, sel, max_chunk);
+  p.attn_scale = sel.attn_scale;
+  p.bf16 = s.dtype == TS_BF16;
+  return p;
+}
+
+// Mean query, then the decode selection over the past positions.
+ts_status prefill_select_launch(const ts_shape& s, const ts_select& sel, int max_chunk,
+                                const void* q_chunk, const int32_t* chunk_lens,
+                                const void* k_pool, const int32_t* bt, const int32_t* seq,
+                                float* logits, float* stats, float* vote, int32_t* sel_idx,
+                                int32_t* sel_count, void* ws, hipStream_t stream) {
+  const PrefillLayout L = prefill_layout(s, sel, max_chunk);
+  const ts::ChunkParams cp = chunk_params(s, sel, max_chunk, q_chunk, chunk_lens, seq, k_pool,
+                                          nullptr, bt, nullptr, nullptr, nullptr, ws);
+  ts_status st = device_status(ts::launch_chunk_mean(cp, stream), "chunk mean launch");
+  if (st != TS_OK) return st;
+  const int32_t* past = cp.past_lens;
+  if (!logits) logits = at<float>(ws, L.dec.logits);
+  if (!stats) stats = at<float>(ws, L.dec.stats);
+  ts::ScoreParams sp = score_params(s, sel, cp.qbar, k_pool, bt, past, nullptr, logits, stats, ws);
+  sp.q_f32 = 1;
+  if ((st = device_status(ts::launch_score(sp, stream), "score launch")) != TS_OK) return st;
+  const ts::VoteParams vp = vote_params(s, sel, logits, stats, past, nullptr, vote, sel_idx,
+                                        sel_count, ws);
+  return device_status(ts::launch_vote_topk(vp, stream, true), "vote/top-k launch");
+}
+
 }  // namespace
+
+extern "C" {
+
+size_t tokenselect_prefill_workspace_size(const ts_shape* shape, const ts_select* sel,
+                                          int32_t max_chunk) {
+  if (check_shape(shape, sel) != TS_OK) return 0;
+  if (check_chunk(*shape, *sel, max_chunk) != TS_OK) return 0;
+  return prefill_layout(*shape, *sel, max_chunk).total;
+}
+
+ts_status tokenselect_prefill_select(const ts_shape* shape, const ts_select* sel, int32_t max_chunk,
+                                     const void* q_chunk, const int32_t* chunk_lens,
+                                     const void* k_pool, const int32_t* block_table,
+                                     const int32_t* seq_lens, float* logits, float* head_stats,
+                                     float* vote, int32_t* sel_idx, int32_t* sel_count, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  ts_status st = check_shape(shape, sel);
+  if (st != TS_OK) return st;
+  if ((st = check_chunk(*shape, *sel, max_chunk)) != TS_OK) return st;
+  TS_REQUIRE16(q_chunk); TS_REQUIRE(chunk_lens); TS_REQUIRE16(k_pool); TS_REQUIRE(block_table);
+  TS_REQUIRE(seq_lens); TS_REQUIRE(sel_idx); TS_REQUIRE(sel_count);
+  if ((st = check_prefill_ws(*shape, *sel, max_chunk, ws, ws_bytes)) != TS_OK) return st;
+  return prefill_select_launch(*shape, *sel, max_chunk, q_chunk, chunk_lens, k_pool, block_table,
+                               seq_lens, logits, head_stats, vote, sel_idx, sel_count, ws, stream);
+}
+
+ts_status tokenselect_chunk_attn(const ts_shape* shape, const ts_select* sel, int32_t max_chunk,
+                                 const void* q_chunk, const int32_t* chunk_lens,
+                                 const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* sel_idx, const int32_t* sel_count, void* out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  ts_status st = check_shape(shape, sel);
+  if (st != TS_OK) return st;
+  if ((st = check_chunk(*shape, *sel, max_chunk)) != TS_OK) return st;
+  TS_REQUIRE16(q_chunk); TS_REQUIRE(chunk_lens); TS_REQUIRE16(k_pool); TS_REQUIRE16(v_pool);
+  TS_REQUIRE(block_table); TS_REQUIRE(seq_lens); TS_REQUIRE(sel_idx); TS_REQUIRE(sel_count);
+  TS_REQUIRE(out);
+  if ((st = check_prefill_ws(*shape, *sel, max_chunk, ws, ws_bytes)) != TS_OK) return st;
+  const ts::ChunkParams cp = chunk_params(*shape, *sel, max_chunk, q_chunk, chunk_lens, seq_lens,
+                                          k_pool, v_pool, block_table, sel_idx, sel_count, out, ws);
+  return device_status(ts::launch_chunk_attn(cp, stream), "chunk attention launch");
+}
+
+ts_status tokenselect_prefill_chunk(const ts_shape* shape, const ts_select* sel, int32_t max_chunk,
+                                    const void* q_chunk, const int32_t* chunk_lens,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    int32_t* sel_idx, int32_t* sel_count, void* out, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  ts_status st = check_shape(shape, sel);
+  if (st != TS_OK) return st;
+  if ((st = check_chunk(*shape, *sel, max_chunk)) != TS_OK) return st;
+  TS_REQUIRE16(q_chunk); TS_REQUIRE(chunk_lens); TS_REQUIRE16(k_pool); TS_REQUIRE16(v_pool);
+  TS_REQUIRE(block_table); TS_REQUIRE(seq_lens); TS_REQUIRE(sel_idx); TS_REQUIRE(sel_count);
+  TS_REQUIRE(out);
+  if ((st = check_prefill_ws(*shape, *sel, max_chunk, ws, ws_bytes)) != TS_OK) return st;
+  st = prefill_select_launch(*shape, *sel, max_chunk, q_chunk, chunk_lens, k_pool, block_table,
+                             seq_lens, nullptr, nullptr, nullptr, sel_idx, sel_count, ws, stream);
+  if (st != TS_OK) return st;
+  const ts::ChunkParams cp = chunk_params(*shape, *sel, max_chunk, q_chunk, chunk_lens, seq_lens,
+                                          k_pool, v_pool, block_table, sel_idx, sel_count, out, ws);
+  return device_status(ts::launch_chunk_attn(cp, stream), "chunk attention launch");
+}
+
+}  // extern "C"
 
 extern "C" {
 

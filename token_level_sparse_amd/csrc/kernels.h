@@ -27,7 +27,8 @@ struct ScoreParams {
   int H, Hkv, b, stride;
   int chunk_pages;            // pages per work unit
   float score_scale;
-  int bf16;                   // element type of q / pool
+  int bf16;                   // element type of the pool (and of q unless q_f32)
+  int q_f32;                  // q is fp32 whatever the pool type (the chunk mean query)
   int grid;                   // workgroups of the score kernel
 };
 
@@ -74,6 +75,38 @@ struct CacheParams {
   int bf16;
 };
 
+// Chunk-wise prefill. A request's chunk of c_r queries sits at positions
+// [P_r, P_r + c_r) of its cache, P_r = N_r - c_r. The attention of chunk query j
+// runs over a gathered key list: the TopK positions below the window start
+// w0 = max(0, P_r - L) (n_sel of them), then the contiguous range
+// [w0, P_r + c_r); query j sees the first base + j + 1 entries, base = n_sel + P_r - w0.
+constexpr int kChunkRows = 64;        // (query, head) rows per attention workgroup
+constexpr int kChunkSplitKeys = 1024; // key-list entries per attention split
+constexpr int kChunkPartStride = 128 + 4;  // floats per split partial: o[128], m, l, pad
+
+struct ChunkParams {
+  const void* q;              // [b][max_chunk][H][d]
+  const int32_t* chunk_lens;  // [b]
+  const int32_t* seq_lens;    // [b] N_r, chunk included
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* sel_idx;     // [b][sel_stride] TopK over the past, ascending
+  const int32_t* sel_count;   // [b]
+  float* qbar;                // [b][H][d] fp32 mean query (output of the mean kernel)
+  int32_t* past_lens;         // [b] P_r (output of the mean kernel)
+  float* partials;            // [b][max_chunk][H][splits][d + 2]
+  void* out;                  // [b][max_chunk][H][d]
+  int H, Hkv, b, stride, max_chunk, sel_stride, n_local, splits;
+  float attn_scale;
+  int bf16;
+};
+
+__host__ __device__ inline int chunk_splits(int top_k, int n_local, int max_chunk) {
+  const long long keys = (long long)top_k + n_local + max_chunk;
+  return (int)((keys + kChunkSplitKeys - 1) / kChunkSplitKeys);
+}
+
 __host__ __device__ inline int attn_splits(int top_k, int n_local) {
   return (top_k + kAttnTile - 1) / kAttnTile + (n_local + kAttnTile - 1) / kAttnTile;
 }
@@ -82,5 +115,7 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t s);
 hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 hipError_t launch_cache_check(const CacheParams& p, hipStream_t s);
+hipError_t launch_chunk_mean(const ChunkParams& p, hipStream_t s);
+hipError_t launch_chunk_attn(const ChunkParams& p, hipStream_t s);
 
 }  // namespace ts

@@ -1,0 +1,440 @@
+// Chunk-wise prefill: the mean query of a chunk, and the attention of every chunk
+// query over the chunk's shared selection plus the causal part of the chunk.
+//
+// Source: TokenSelect deepnotes page, selection frequency of the prefill stage (the
+// c queries of a chunk are averaged into one query that goes through the selection
+// function, and the chunk shares the result), and the selective sparse attention
+// formalisation; blog review of the same paper, section 3.2 (chunk-wise selection
+// in prefill) and section 3.3 (Fig. 5: the chunk-prefill step with chunk 512).
+//
+// Selection reuses the decode kernels: the mean query (fp64 sum of the chunk's
+// queries, one division, rounded to fp32) is scored against the past positions
+// [0, P) with the fp32-query score mode, then voted and TopK'd as in decode.
+//
+// Attention. Chunk query j of request r sees the gathered key list
+//   x < n_sel:  the TopK positions below the window start w0 = max(0, P - L),
+//   x >= n_sel: positions w0 + (x - n_sel), i.e. the window and the chunk,
+// truncated at x <= base + j with base = n_sel + P - w0 (causal inside the chunk).
+// That is a causal attention with a key offset over an index-mapped paged pool, a
+// dense contraction of c*G rows by ~k+L+c keys, so it runs on the matrix cores.
+//
+// gfx950 design. A workgroup owns 64 (query, head) rows of one (request, KV head):
+// row = j * G + head-in-group, so one staged key block serves all G heads of the
+// group. Each of the 4 waves owns 16 rows. Per block of keys:
+//   * the workgroup stages K as [key][d] and V transposed as [d][key] in LDS (the
+//     next block's loads are issued into registers before the current block's
+//     products, so the gather latency overlaps the matrix work);
+//   * S^T = K Q^T on MFMA (A = 16 keys x 32 dims from LDS, B = the wave's queries
+//     held in registers), so a lane ends with 4 keys of one row: row = lane % 16;
+//   * online softmax in base 2 per row (row max across the 4 lane groups);
+//   * O^T += V^T P^T on MFMA: the lane's probabilities are already the B operand
+//     (row = lane % 16, 8 keys), with the key order of the A operand (V^T rows from
+//     LDS) permuted to match, so P never leaves registers.
+// bf16 uses v_mfma_f32_16x16x32_bf16 on 64-key blocks; fp32 uses
+// v_mfma_f32_16x16x4_f32 on 32-key blocks with the same index and mask logic.
+// Key splits of kChunkSplitKeys list entries give more workgroups; a combine kernel
+// merges the per-split (o, m, l) rows.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace ts {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kPartStride = kChunkPartStride;   // o[128], m, l, 2 pad: 16-byte aligned rows
+static_assert(kChunkPartStride == kHeadDim + 4, "partial row layout");
+
+// Geometry of request r's chunk. Out-of-contract lengths are clamped so that no
+// access leaves the request's pages (results are then unspecified).
+struct ChunkGeom {
+  int c, P, w0, n_sel, base, N;
+};
+
+__device__ int lower_bound_i32(const int32_t* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ ChunkGeom chunk_geom(const ChunkParams& p, int r, bool with_sel) {
+  ChunkGeom gm;
+  gm.N = max(0, p.seq_lens[r]);
+  gm.c = min(max(p.chunk_lens[r], 0), min(p.max_chunk, gm.N));
+  gm.P = gm.N - gm.c;
+  gm.w0 = max(0, gm.P - p.n_local);
+  gm.n_sel = 0;
+  if (with_sel) {
+    const int cnt = min(max(p.sel_count[r], 0), min(p.sel_stride, gm.P));
+    gm.n_sel = lower_bound_i32(p.sel_idx + (int64_t)r * p.sel_stride, cnt, gm.w0);
+  }
+  gm.base = gm.n_sel + gm.P - gm.w0;
+  return gm;
+}
+
+// ---------------------------------------------------------------- mean query
+// One workgroup per (request, head): qbar = (sum_j q_j) / c with the sum in fp64
+// (exact for bf16 queries of ordinary range), rounded once to fp32.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void chunk_mean_kernel(ChunkParams p) {
+  __shared__ double s_acc[kHeadDim];
+  const int r = blockIdx.x / p.H, h = blockIdx.x - (blockIdx.x / p.H) * p.H;
+  const ChunkGeom gm = chunk_geom(p, r, false);
+  const int d = threadIdx.x & (kHeadDim - 1), half = threadIdx.x >> 7;
+  double acc = 0.0;
+  for (int j = half; j < gm.c; j += 2) {
+    const int64_t idx = (((int64_t)r * p.max_chunk + j) * p.H + h) * kHeadDim + d;
+    const float x = kBf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(p.q)[idx] << 16)
+                          : static_cast<const float*>(p.q)[idx];
+    acc += (double)x;
+  }
+  if (half == 1) s_acc[d] = acc;
+  __syncthreads();
+  if (half == 0) {
+    acc += s_acc[d];
+    p.qbar[((int64_t)r * p.H + h) * kHeadDim + d] = (float)(acc / (double)max(gm.c, 1));
+  }
+  if (h == 0 && threadIdx.x == 0) p.past_lens[r] = gm.P;
+}
+
+// ---------------------------------------------------------------- attention
+template <bool kBf16> struct Tile;
+template <> struct Tile<true> {
+  static constexpr int kKeys = 64;                 // keys per staged block
+  static constexpr int kKStride = kHeadDim + 8;    // bf16 elements per K row in LDS
+  static constexpr int kVStride = 64 + 8;          // bf16 elements per V^T row in LDS
+  static constexpr int kLds = kKeys * kKStride * 2 + kHeadDim * kVStride * 2;
+  uint4 k[4], v[4];                                // staging registers: 4 keys x 8 dims
+};
+template <> struct Tile<false> {
+  static constexpr int kKeys = 32;
+  static constexpr int kStride = kHeadDim + 4;     // floats per K / V row in LDS
+  static constexpr int kLds = 2 * kKeys * kStride * 4;
+  float4 k[4], v[4];                               // staging registers: 1 key x 16 dims
+};
+constexpr int kChunkLds = Tile<true>::kLds > Tile<false>::kLds ? Tile<true>::kLds : Tile<false>::kLds;
+
+struct KeyMap {
+  const int32_t* sel;      // request's TopK row
+  const int32_t* bt;       // request's block-table row
+  int n_sel, w0, N, g, Hkv, x_end;
+  __device__ int64_t row(int x) const {          // element offset of key-list entry x
+    const int xc = min(x, x_end - 1);
+    int pos = xc < n_sel ? sel[xc] : w0 + (xc - n_sel);
+    pos = min(max(pos, 0), N - 1);
+    const int64_t page = bt[pos >> 4];
+    return ((page * Hkv + g) * kPage + (pos & (kPage - 1))) * kHeadDim;
+  }
+};
+
+__device__ __forceinline__ void stage_load(Tile<true>& t, const uint16_t* kp, const uint16_t* vp,
+                                           const KeyMap& km, int x0) {
+  const int kq = threadIdx.x >> 4, dc = threadIdx.x & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t off = km.row(x0 + 4 * kq + i) + 8 * dc;
+    t.k[i] = *reinterpret_cast<const uint4*>(kp + off);
+    t.v[i] = *reinterpret_cast<const uint4*>(vp + off);
+  }
+}
+__device__ __forceinline__ void stage_store(const Tile<true>& t, char* lds) {
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* Vt = Ks + Tile<true>::kKeys * Tile<true>::kKStride;
+  const int kq = threadIdx.x >> 4, dc = threadIdx.x & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint4*>(Ks + (4 * kq + i) * Tile<true>::kKStride + 8 * dc) = t.k[i];
+  // V^T[d][key]: for each of the 8 dims, the 4 keys' values packed into 8 bytes
+  const uint32_t w[4][4] = {{t.v[0].x, t.v[0].y, t.v[0].z, t.v[0].w},
+                            {t.v[1].x, t.v[1].y, t.v[1].z, t.v[1].w},
+                            {t.v[2].x, t.v[2].y, t.v[2].z, t.v[2].w},
+                            {t.v[3].x, t.v[3].y, t.v[3].z, t.v[3].w}};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int sh = (e & 1) ? 16 : 0;
+    const uint32_t b0 = (w[0][e >> 1] >> sh) & 0xffffu, b1 = (w[1][e >> 1] >> sh) & 0xffffu;
+    const uint32_t b2 = (w[2][e >> 1] >> sh) & 0xffffu, b3 = (w[3][e >> 1] >> sh) & 0xffffu;
+    *reinterpret_cast<uint2*>(Vt + (8 * dc + e) * Tile<true>::kVStride + 4 * kq) =
+        make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+  }
+}
+__device__ __forceinline__ void stage_load(Tile<false>& t, const float* kp, const float* vp,
+                                           const KeyMap& km, int x0) {
+  const int key = threadIdx.x >> 3, dq = threadIdx.x & 7;
+  const int64_t off = km.row(x0 + key) + 16 * dq;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    t.k[m] = *reinterpret_cast<const float4*>(kp + off + 4 * m);
+    t.v[m] = *reinterpret_cast<const float4*>(vp + off + 4 * m);
+  }
+}
+__device__ __forceinline__ void stage_store(const Tile<false>& t, char* lds) {
+  float* Ks = reinterpret_cast<float*>(lds);
+  float* Vs = Ks + Tile<false>::kKeys * Tile<false>::kStride;
+  const int key = threadIdx.x >> 3, dq = threadIdx.x & 7;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    *reinterpret_cast<float4*>(Ks + key * Tile<false>::kStride + 16 * dq + 4 * m) = t.k[m];
+    *reinterpret_cast<float4*>(Vs + key * Tile<false>::kStride + 16 * dq + 4 * m) = t.v[m];
+  }
+}
+
+// Query operand (B of S^T = K Q^T): bf16 lane holds dims 32 ks + 8 a + [0, 8) of its
+// row; fp32 lane holds dims 4 ks + a.
+struct QOpBf16 { bf16x8_t v[4]; };
+struct QOpF32 { float v[32]; };
+
+__device__ __forceinline__ void load_qop(QOpBf16& q, const uint16_t* qrow, bool ok, int a) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (ok) w = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * a);
+    q.v[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{w.x, w.y, w.z, w.w});
+  }
+}
+__device__ __forceinline__ void load_qop(QOpF32& q, const float* qrow, bool ok, int a) {
+#pragma unroll
+  for (int ks = 0; ks < 32; ++ks) q.v[ks] = ok ? qrow[4 * ks + a] : 0.f;
+}
+
+// S^T tiles of one staged block: s[t][i] = <q_row, k_{16 t + 4 a + i}>.
+__device__ __forceinline__ void qk_block(const char* lds, const QOpBf16& q, int l16, int a,
+                                         f32x4_t (&s)[4]) {
+  const uint16_t* Ks = reinterpret_cast<const uint16_t*>(lds);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(
+          Ks + (16 * t + l16) * Tile<true>::kKStride + 32 * ks + 8 * a);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, q.v[ks], acc, 0, 0, 0);
+    }
+    s[t] = acc;
+  }
+}
+__device__ __forceinline__ void qk_block(const char* lds, const QOpF32& q, int l16, int a,
+                                         f32x4_t (&s)[2]) {
+  const float* Ks = reinterpret_cast<const float*>(lds);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[(16 * t + l16) * Tile<false>::kStride + 4 * ks + a],
+                                                 q.v[ks], acc, 0, 0, 0);
+    s[t] = acc;
+  }
+}
+
+// O^T += V^T P^T over one staged block. o[dt][i] = O[row][16 dt + 4 a + i].
+__device__ __forceinline__ void pv_block(const char* lds, const float (&pv)[4][4], int l16, int a,
+                                         f32x4_t (&o)[8]) {
+  const uint16_t* Vt = reinterpret_cast<const uint16_t*>(lds) + Tile<true>::kKeys * Tile<true>::kKStride;
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    // B operand: keys 32 k2 + 4 a + [0, 4) then 32 k2 + 16 + 4 a + [0, 4)
+    const u32x4_t pw = {
+        (uint32_t)f32_to_bf16(pv[2 * k2][0]) | ((uint32_t)f32_to_bf16(pv[2 * k2][1]) << 16),
+        (uint32_t)f32_to_bf16(pv[2 * k2][2]) | ((uint32_t)f32_to_bf16(pv[2 * k2][3]) << 16),
+        (uint32_t)f32_to_bf16(pv[2 * k2 + 1][0]) | ((uint32_t)f32_to_bf16(pv[2 * k2 + 1][1]) << 16),
+        (uint32_t)f32_to_bf16(pv[2 * k2 + 1][2]) | ((uint32_t)f32_to_bf16(pv[2 * k2 + 1][3]) << 16)};
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint16_t* vr = Vt + (16 * dt + l16) * Tile<true>::kVStride + 32 * k2 + 4 * a;
+      const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[dt], 0, 0, 0);
+    }
+  }
+}
+__device__ __forceinline__ void pv_block(const char* lds, const float (&pv)[2][4], int l16, int a,
+                                         f32x4_t (&o)[8]) {
+  const float* Vs = reinterpret_cast<const float*>(lds) + Tile<false>::kKeys * Tile<false>::kStride;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+            Vs[(16 * t + 4 * a + i) * Tile<false>::kStride + 16 * dt + l16], pv[t][i], o[dt], 0, 0, 0);
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void chunk_attn_kernel(ChunkParams p) {
+  using T = typename std::conditional<kBf16, uint16_t, float>::type;
+  using QOp = typename std::conditional<kBf16, QOpBf16, QOpF32>::type;
+  constexpr int KB = Tile<kBf16>::kKeys;
+  constexpr int NT = KB / 16;
+  __shared__ __align__(16) char s_lds[kChunkLds];
+  __shared__ int s_geom[6];
+
+  const int H = p.H, Hkv = p.Hkv, G = H / Hkv;
+  const int rt = (p.max_chunk * G + kChunkRows - 1) / kChunkRows;
+  const int tile = blockIdx.x % rt;
+  const int g = (blockIdx.x / rt) % Hkv;
+  const int r = blockIdx.x / (rt * Hkv);
+  const int split = blockIdx.y;
+  if (threadIdx.x == 0) {
+    const ChunkGeom gm = chunk_geom(p, r, true);
+    s_geom[0] = gm.c; s_geom[1] = gm.P; s_geom[2] = gm.w0;
+    s_geom[3] = gm.n_sel; s_geom[4] = gm.base; s_geom[5] = gm.N;
+  }
+  __syncthreads();
+  const int c = s_geom[0], w0 = s_geom[2], n_sel = s_geom[3], base = s_geom[4], N = s_geom[5];
+  const int rows = c * G;
+  const int row0 = tile * kChunkRows;
+  if (row0 >= rows) return;                                   // uniform over the workgroup
+  const int jmax = (min(row0 + kChunkRows, rows) - 1) / G;
+  const int n_vis = base + jmax + 1;                          // entries the last query sees
+  const int x_begin = split * kChunkSplitKeys;
+  if (x_begin >= n_vis) return;                               // uniform
+  const int x_end = min(x_begin + kChunkSplitKeys, n_vis);
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, a = lane >> 4;
+  const int rho = row0 + 16 * wave + l16;
+  const bool row_ok = rho < rows;
+  const int j = row_ok ? rho / G : 0;
+  const int h = g * G + (row_ok ? rho - (rho / G) * G : 0);
+  const int lim = row_ok ? base + j : -1;                     // last visible key-list entry
+
+  const T* qrow = static_cast<const T*>(p.q) + (((int64_t)r * p.max_chunk + j) * H + h) * kHeadDim;
+  QOp q;
+  load_qop(q, qrow, row_ok, a);
+
+  KeyMap km;
+  km.sel = p.sel_idx + (int64_t)r * p.sel_stride;
+  km.bt = p.block_table + (int64_t)r * p.stride;
+  km.n_sel = n_sel; km.w0 = w0; km.N = N; km.g = g; km.Hkv = Hkv; km.x_end = x_end;
+  const T* kp = static_cast<const T*>(p.k_pool);
+  const T* vp = static_cast<const T*>(p.v_pool);
+
+  const float sl2 = p.attn_scale * kLog2e;
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4_t o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  Tile<kBf16> st;
+  stage_load(st, kp, vp, km, x_begin);
+  for (int x0 = x_begin; x0 < x_end; x0 += KB) {
+    __syncthreads();                      // the previous block's reads of LDS are done
+    stage_store(st, s_lds);
+    __syncthreads();
+    if (x0 + KB < x_end) stage_load(st, kp, vp, km, x0 + KB);   // overlaps the products below
+
+    f32x4_t s[NT];
+    qk_block(s_lds, q, l16, a, s);
+    float pv[NT][4];
+    float mloc = kNegInf;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int x = x0 + 16 * t + 4 * a + i;
+        pv[t][i] = (x < x_end && x <= lim) ? s[t][i] * sl2 : kNegInf;
+        mloc = fmaxf(mloc, pv[t][i]);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc);
+    float alpha = 1.f, psum = 0.f;
+    if (m_new != kNegInf) {
+      alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[t][i] = fast_exp2(pv[t][i] - m_new);
+          psum += pv[t][i];
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[t][i] = 0.f;
+    }
+    l_run = fmaf(l_run, alpha, psum);
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    pv_block(s_lds, pv, l16, a, o);
+  }
+
+  float lt = l_run + __shfl_xor(l_run, 16);
+  lt += __shfl_xor(lt, 32);
+  if (row_ok) {
+    float* dst = p.partials +
+                 ((((int64_t)r * p.max_chunk + j) * H + h) * p.splits + split) * kPartStride;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(dst + 16 * dt + 4 * a) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (a == 0) { dst[kHeadDim] = m_run; dst[kHeadDim + 1] = lt; }
+  }
+}
+
+// One workgroup per (request, chunk query): merge the splits of every head.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkParams p) {
+  __shared__ int s_geom[2];
+  const int r = blockIdx.x / p.max_chunk, j = blockIdx.x - (blockIdx.x / p.max_chunk) * p.max_chunk;
+  if (threadIdx.x == 0) {
+    const ChunkGeom gm = chunk_geom(p, r, true);
+    s_geom[0] = gm.c; s_geom[1] = gm.base;
+  }
+  __syncthreads();
+  const int c = s_geom[0], base = s_geom[1];
+  if (j >= c) return;
+  const int S = min(p.splits, (base + j + kChunkSplitKeys) / kChunkSplitKeys);
+  const int d = threadIdx.x & (kHeadDim - 1);
+  for (int h = threadIdx.x >> 7; h < p.H; h += 2) {
+    const float* src = p.partials + (((int64_t)r * p.max_chunk + j) * p.H + h) * p.splits * kPartStride;
+    float M = kNegInf;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, src[s * kPartStride + kHeadDim]);
+    float L = 0.f, acc = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float ms = src[s * kPartStride + kHeadDim];
+      const float w = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
+      L = fmaf(w, src[s * kPartStride + kHeadDim + 1], L);
+      acc = fmaf(w, src[s * kPartStride + d], acc);
+    }
+    const float res = acc / L;
+    const int64_t oi = (((int64_t)r * p.max_chunk + j) * p.H + h) * kHeadDim + d;
+    if (kBf16) static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(res);
+    else static_cast<float*>(p.out)[oi] = res;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_mean(const ChunkParams& p, hipStream_t s) {
+  const dim3 grid(p.b * p.H), block(256);
+  if (p.bf16) hipLaunchKernelGGL(chunk_mean_kernel<true>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(chunk_mean_kernel<false>, grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_attn(const ChunkParams& p, hipStream_t s) {
+  const int G = p.H / p.Hkv;
+  const int rt = (p.max_chunk * G + kChunkRows - 1) / kChunkRows;
+  const dim3 grid(p.b * p.Hkv * rt, p.splits), block(256);
+  if (p.bf16) hipLaunchKernelGGL(chunk_attn_kernel<true>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(chunk_attn_kernel<false>, grid, block, 0, s, p);
+  const dim3 cgrid(p.b * p.max_chunk);
+  if (p.bf16) hipLaunchKernelGGL(chunk_combine_kernel<true>, cgrid, block, 0, s, p);
+  else hipLaunchKernelGGL(chunk_combine_kernel<false>, cgrid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace ts

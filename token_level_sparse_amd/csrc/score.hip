@@ -47,6 +47,18 @@ __device__ __forceinline__ int slot_head(int col, int s) {
 template <bool kBf16, int S> struct QRegs;
 template <int S> struct QRegs<true, S> { uint32_t w[S][4]; };
 template <int S> struct QRegs<false, S> { float w[S][8]; };
+// fp32 query against bf16 keys (the mean query of a prefill chunk): dims
+// [8 col, 8 col + 8) as floats.
+template <int S> struct QRegsMixed { float w[S][8]; };
+
+template <bool kBf16, bool kQ32, int S> struct QSel {
+  using type = QRegs<kBf16, S>;
+  using elem = typename std::conditional<kBf16, uint16_t, float>::type;
+};
+template <int S> struct QSel<true, true, S> {
+  using type = QRegsMixed<S>;
+  using elem = float;
+};
 
 template <bool kBf16> struct PageRegs;
 template <> struct PageRegs<true> { uint4 w[4]; };
@@ -114,6 +126,21 @@ __device__ __forceinline__ void load_q(QRegs<false, S>& qr, const float* qb, int
   }
 }
 
+template <int G, int S>
+__device__ __forceinline__ void load_q(QRegsMixed<S>& qr, const float* qb, int col) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int h = slot_head(col, s);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
+    if (h < G) {
+      a = *reinterpret_cast<const float4*>(qb + h * kHeadDim + 8 * col);
+      c = *reinterpret_cast<const float4*>(qb + h * kHeadDim + 8 * col + 4);
+    }
+    qr.w[s][0] = a.x; qr.w[s][1] = a.y; qr.w[s][2] = a.z; qr.w[s][3] = a.w;
+    qr.w[s][4] = c.x; qr.w[s][5] = c.y; qr.w[s][6] = c.z; qr.w[s][7] = c.w;
+  }
+}
+
 __device__ __forceinline__ void load_page(PageRegs<true>& pr, const uint16_t* base, int row, int col) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -166,6 +193,29 @@ __device__ __forceinline__ void lane_dots(const PageRegs<false>& pr, const QRegs
   }
 }
 
+// bf16 keys widened to fp32 (exact), then fp32 FMAs with the fp32 query.
+template <int S>
+__device__ __forceinline__ void lane_dots(const PageRegs<true>& pr, const QRegsMixed<S>& qr,
+                                          float (&acc)[4][S]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w[4] = {pr.w[j].x, pr.w[j].y, pr.w[j].z, pr.w[j].w};
+    float k[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      k[2 * t] = __uint_as_float(w[t] << 16);
+      k[2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      float a = k[0] * qr.w[s][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) a = fmaf(k[e], qr.w[s][e], a);
+      acc[j][s] = a;
+    }
+  }
+}
+
 constexpr int kDppXor3 = 0x1B;        // quad_perm [3,2,1,0]
 
 // Reduce-scatter over the 16 lanes of a row: 4 tokens x S slots in, S/4 values
@@ -198,10 +248,12 @@ __device__ __forceinline__ void row_reduce_scatter(const float (&acc)[4][S], int
   }
 }
 
-template <bool kBf16, int G>
+template <bool kBf16, bool kQ32, int G>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
   using T = typename std::conditional<kBf16, uint16_t, float>::type;
   constexpr int S = Slots<G>::kN;
+  using QR = typename QSel<kBf16, kQ32, S>::type;
+  using TQ = typename QSel<kBf16, kQ32, S>::elem;
   constexpr int C = S / 4;                     // values a lane owns per page
   __shared__ int64_t s_tok[kMaxBatch + 1];
   __shared__ int32_t s_chunk[kMaxBatch + 1];
@@ -218,7 +270,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
   const int row = lane >> 4, col = lane & 15;
   const int H = p.H, Hkv = p.Hkv;
   const int total_units = s_chunk[b] * Hkv;
-  const T* qall = static_cast<const T*>(p.q);
+  const TQ* qall = static_cast<const TQ*>(p.q);
   const T* pool = static_cast<const T*>(p.k_pool);
   // this lane's outputs: token 4 (col & 3) + row of each page, heads hd[c]
   const int tok_in_page = 4 * (col & 3) + row;
@@ -249,7 +301,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     const int pg0 = c0 * p.chunk_pages;
     const int pg1 = min(n_pages, pg0 + p.chunk_pages);
 
-    QRegs<kBf16, S> q;
+    QR q;
     load_q<G>(q, qall + ((int64_t)r * H + g * G) * kHeadDim, col);
     const int32_t* bt = p.block_table + (int64_t)r * p.stride;
     // logits of KV head g: [N][G] (token-major, the group's heads adjacent)
@@ -360,19 +412,19 @@ __global__ __launch_bounds__(256) void stats_kernel(ScoreParams p) {
   }
 }
 
-template <bool kBf16>
+template <bool kBf16, bool kQ32>
 hipError_t launch_score_t(const ScoreParams& p, hipStream_t st) {
   const int G = p.H / p.Hkv;
   dim3 grid(p.grid), block(256);
   switch (G) {
-    case 1: hipLaunchKernelGGL((score_kernel<kBf16, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((score_kernel<kBf16, 2>), grid, block, 0, st, p); break;
-    case 3: hipLaunchKernelGGL((score_kernel<kBf16, 3>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((score_kernel<kBf16, 4>), grid, block, 0, st, p); break;
-    case 5: hipLaunchKernelGGL((score_kernel<kBf16, 5>), grid, block, 0, st, p); break;
-    case 6: hipLaunchKernelGGL((score_kernel<kBf16, 6>), grid, block, 0, st, p); break;
-    case 7: hipLaunchKernelGGL((score_kernel<kBf16, 7>), grid, block, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((score_kernel<kBf16, 8>), grid, block, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((score_kernel<kBf16, kQ32, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((score_kernel<kBf16, kQ32, 2>), grid, block, 0, st, p); break;
+    case 3: hipLaunchKernelGGL((score_kernel<kBf16, kQ32, 3>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((score_kernel<kBf16, kQ32, 4>), grid, block, 0, st, p); break;
+    case 5: hipLaunchKernelGGL((score_kernel<kBf16, kQ32, 5>), grid, block, 0, st, p); break;
+    case 6: hipLaunchKernelGGL((score_kernel<kBf16, kQ32, 6>), grid, block, 0, st, p); break;
+    case 7: hipLaunchKernelGGL((score_kernel<kBf16, kQ32, 7>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((score_kernel<kBf16, kQ32, 8>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -381,7 +433,9 @@ hipError_t launch_score_t(const ScoreParams& p, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_score(const ScoreParams& p, hipStream_t st) {
-  hipError_t e = p.bf16 ? launch_score_t<true>(p, st) : launch_score_t<false>(p, st);
+  hipError_t e = !p.bf16  ? launch_score_t<false, false>(p, st)
+                 : p.q_f32 ? launch_score_t<true, true>(p, st)
+                           : launch_score_t<true, false>(p, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(stats_kernel, dim3(p.b * p.H), dim3(256), 0, st, p);
   return hipGetLastError();

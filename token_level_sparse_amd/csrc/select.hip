@@ -332,6 +332,10 @@ __device__ void count_phase(const VoteParams& p, SelectShared& sh) {
 // Ascending positions through a prefix over the request's tiles.
 __device__ void write_phase(const VoteParams& p, SelectShared& sh) {
   const int total = sh.tb.tile[p.b];
+  // a request with no positions (a first prefill chunk) has no tile to do it
+  if (blockIdx.x == 0)
+    for (int r = threadIdx.x; r < p.b; r += kThreads)
+      if (p.seq_lens[r] == 0 && !(p.skip && p.skip[r])) p.sel_count[r] = 0;
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int r = find_segment(sh.tb.tile, p.b, tile);
     const int t = tile - sh.tb.tile[r];
