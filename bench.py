@@ -13,7 +13,9 @@ Prints one JSON line: decode steps/s (value), the scoring kernel's achieved HBM
 bandwidth against the 8 TB/s peak (roofline), the same metric at N = 131072
 (secondary), the 16-request ragged batch (ragged_batch), the 256-step
 Selection Cache sequence on Qwen2-7B shapes (selection_cache: steps/s, hit rate,
-hit vector), and the fp64 oracle timed on host cores (cpu_baseline).
+hit vector), chunk-wise prefill at 128K and 1M cached tokens with 512-token chunks
+(prefill: chunks/s, selection GB/s, chunk-attention TFLOP/s against the bf16
+matrix-core peak), and the fp64 oracle timed on host cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -28,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0     # dense bf16 matrix-core peak of MI355X
 
 
 def log(msg):
@@ -253,6 +256,93 @@ def time_cache_sequence(geo, dev):
     return res
 
 
+def time_prefill(geo, n_layers, steps, warmup, dev):
+    """Chunk-wise prefill: one chunk of c queries per step over rotating layers
+    (tokenselect_prefill_chunk: mean query, selection over the past, chunk attention).
+    The chunk attention and the selection are also timed per launch on the same
+    stream; the attention's algorithmic FLOPs are 4 d H sum_j |S_j| (two products of
+    d multiply-adds per attended key, query and head)."""
+    import torch
+    import token_level_sparse_amd as ts
+    from synth import workloads as wl
+    t0 = time.time()
+    KC, VC = kv_cache(geo, n_layers, dev)
+    cbs = [wl.make_chunk_batch(geo, dev, layer=l, pools=(KC[l], VC[l])) for l in range(n_layers)]
+    torch.cuda.synchronize()
+    log(f"[{geo.name}] generated {n_layers} layers in {time.time() - t0:.1f}s")
+    H, d, c = geo.num_q_heads, geo.head_dim, geo.chunk
+    N = geo.seq_len
+    P = N - c
+    shape = ts.make_shape(H, geo.num_kv_heads, 1, cbs[0].paged.block_table.shape[1], N, geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, 2.0)
+    ws = ts.alloc_prefill_workspace(shape, sel, c, dev)
+    sel_idx = [torch.empty(1, geo.top_k, dtype=torch.int32, device=dev) for _ in range(n_layers)]
+    sel_count = [torch.empty(1, dtype=torch.int32, device=dev) for _ in range(n_layers)]
+    out = torch.empty(1, c, H, d, dtype=geo.torch_dtype, device=dev)
+
+    def chunk(s):
+        cb, l = cbs[s % n_layers], s % n_layers
+        ts.prefill_chunk(shape, sel, c, cb.q_chunk, cb.chunk_lens, cb.paged.k_pool, cb.paged.v_pool,
+                         cb.paged.block_table, cb.seq_lens, sel_idx[l], sel_count[l], out, ws)
+
+    def timed(fn, n):
+        evs = []
+        for s in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(s)
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / n
+
+    for s in range(max(warmup, n_layers)):
+        chunk(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        chunk(s)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+
+    def attn(s):
+        cb, l = cbs[s % n_layers], s % n_layers
+        ts.chunk_attn(shape, sel, c, cb.q_chunk, cb.chunk_lens, cb.paged.k_pool, cb.paged.v_pool,
+                      cb.paged.block_table, cb.seq_lens, sel_idx[l], sel_count[l], out, ws)
+
+    def select(s):
+        cb, l = cbs[s % n_layers], s % n_layers
+        ts.prefill_select(shape, sel, c, cb.q_chunk, cb.chunk_lens, cb.paged.k_pool, cb.paged.block_table,
+                          cb.seq_lens, None, None, None, sel_idx[l], sel_count[l], ws)
+
+    attn_ms = timed(attn, steps)
+    select_ms = timed(select, steps)
+    # attended keys of every chunk query: base + j + 1, base = |T below the window| + (P - w0)
+    w0 = max(0, P - geo.n_local)
+    flops = 0.0
+    for l in range(n_layers):
+        T = sel_idx[l][0, : int(sel_count[l][0])].cpu()
+        base = int((T < w0).sum()) + (P - w0)
+        flops += 4.0 * d * H * (c * base + c * (c + 1) / 2)
+    flops /= n_layers
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    sel_bytes = score_bytes_per_token(geo) * P
+    log(f"[{geo.name}] chunk of {c}: {ms:.4f} ms ({c * 1e3 / ms:.0f} prefill tokens/s); "
+        f"selection {select_ms:.4f} ms ({sel_bytes / (select_ms * 1e-3) / 1e9:.0f} GB/s), "
+        f"chunk attention {attn_ms:.4f} ms ({attn_tflops:.1f} TFLOP/s)")
+    res = {"workload": geo.name, "N": N, "chunk": c, "top_k": geo.top_k, "n_local": geo.n_local,
+           "layers": n_layers, "ms_per_chunk": ms, "chunks_per_s": 1e3 / ms,
+           "prefill_tokens_per_s": c * 1e3 / ms, "select_ms": select_ms,
+           "select_gbps": sel_bytes / (select_ms * 1e-3) / 1e9, "attn_ms": attn_ms,
+           "attn_flops": flops, "attn_tflops": attn_tflops,
+           "attn_mfma_frac": attn_tflops * 1e3 / PEAK_BF16_TFLOPS}
+    del cbs, ws, KC, VC
+    torch.cuda.empty_cache()
+    return res
+
+
 def counter_run(geo, dev, launches=4, layers=4):
     """Short program for rocprofv3 --pmc passes: a few scoring launches on the 1M
     workload, then a plain device copy of 1 GiB (the calibration kernel whose true
@@ -338,10 +428,12 @@ def main():
         secondary = {"workload": g1.name, "N": g1.seq_len, "decode_steps_per_s": 1e3 / r1["ms_per_step"],
                      "ms_per_step": r1["ms_per_step"], "score_ms": r1["score_ms"],
                      "score_gbps": r1["score_gbps"], "k_gbps": r1["k_gbps"], "rotating_layers": 8}
-    ragged = cache_seq = None
+    ragged = cache_seq = prefill = None
     if not args.no_secondary:
         ragged = time_ragged(wl.workload("llama3-8b-ragged16"), max(8, args.steps // 4), 2, dev)
         cache_seq = time_cache_sequence(wl.workload("qwen2-7b-cache256"), dev)
+        prefill = [time_prefill(wl.workload("prefill-llama3-128k"), 8, max(16, args.steps // 2), 4, dev),
+                   time_prefill(wl.workload("prefill-llama3-1m"), 4, max(8, args.steps // 8), 2, dev)]
     cpu = cpu_baseline(geo, host) if host is not None else None
 
     ms = main_res["ms_per_step"]
@@ -372,6 +464,7 @@ def main():
         "secondary": secondary,
         "ragged_batch": ragged,
         "selection_cache": cache_seq,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -207,11 +207,15 @@ ts::AttnParams attn_params(const ts_shape& s, const ts_select& sel, const void* 
 // ---------------------------------------------------------------- prefill
 struct PrefillLayout {
   Layout dec;                  // the decode regions, used by the selection over the past
-  size_t qbar, past, cpart, total;
+  size_t qbar, past, cpart, keytab, total;
 };
 
 int chunk_splits_for(const ts_shape& s, const ts_select& sel, int max_chunk) {
   return ts::chunk_splits(eff_top_k(s, sel), eff_local(s, sel), max_chunk);
+}
+
+int64_t chunk_max_keys_for(const ts_shape& s, const ts_select& sel, int max_chunk) {
+  return ts::chunk_max_keys(eff_top_k(s, sel), eff_local(s, sel), max_chunk);
 }
 
 PrefillLayout prefill_layout(const ts_shape& s, const ts_select& sel, int max_chunk) {
@@ -223,6 +227,7 @@ PrefillLayout prefill_layout(const ts_shape& s, const ts_select& sel, int max_ch
   L.past = off;  off += align_up(sizeof(int32_t) * (size_t)s.batch);
   L.cpart = off; off += align_up(sizeof(float) * bH * (size_t)max_chunk *
                                  chunk_splits_for(s, sel, max_chunk) * ts::kChunkPartStride);
+  L.keytab = off; off += align_up(sizeof(int32_t) * (size_t)s.batch * chunk_max_keys_for(s, sel, max_chunk));
   L.total = off;
   return L;
 }
@@ -234,8 +239,12 @@ ts_status check_chunk(const ts_shape& s, const ts_select& sel, int max_chunk) {
                 (long long)s.max_total_tokens);
   const int G = s.num_q_heads / s.num_kv_heads;
   const int64_t tiles = cdiv((int64_t)max_chunk * G, ts::kChunkRows) * s.num_kv_heads * s.batch;
-  if (tiles > INT32_MAX || (int64_t)s.batch * max_chunk > INT32_MAX)
+  if (tiles * (chunk_splits_for(s, sel, max_chunk) + ts::kXcds) > INT32_MAX ||
+      (int64_t)s.batch * max_chunk * s.num_q_heads / 8 > INT32_MAX)
     return fail(TS_ERR_UNSUPPORTED, "batch x max_chunk %lld too large", (long long)s.batch * max_chunk);
+  if (chunk_max_keys_for(s, sel, max_chunk) > INT32_MAX / 2 ||
+      (int64_t)s.batch * chunk_max_keys_for(s, sel, max_chunk) > INT32_MAX)
+    return fail(TS_ERR_UNSUPPORTED, "top_k + n_local + max_chunk too large");
   if (chunk_splits_for(s, sel, max_chunk) > 65535)
     return fail(TS_ERR_UNSUPPORTED, "top_k + n_local + max_chunk too large for the split grid");
   return TS_OK;
@@ -262,6 +271,8 @@ ts::ChunkParams chunk_params(const ts_shape& s, const ts_select& sel, int max_ch
   p.block_table = bt; p.sel_idx = sel_idx; p.sel_count = sel_count;
   p.qbar = at<float>(ws, L.qbar); p.past_lens = at<int32_t>(ws, L.past);
   p.partials = at<float>(ws, L.cpart); p.out = out;
+  p.keytab = at<int32_t>(ws, L.keytab);
+  p.max_keys = (int)chunk_max_keys_for(s, sel, max_chunk);
   p.H = s.num_q_heads; p.Hkv = s.num_kv_heads; p.b = s.batch; p.stride = s.block_table_stride;
   p.max_chunk = max_chunk; p.sel_stride = sel.top_k; p.n_local = sel.n_local;
   p.splits = chunk_splits_for(s, sel, max_chunk);

@@ -81,7 +81,10 @@ struct CacheParams {
 // w0 = max(0, P_r - L) (n_sel of them), then the contiguous range
 // [w0, P_r + c_r); query j sees the first base + j + 1 entries, base = n_sel + P_r - w0.
 constexpr int kChunkRows = 64;        // (query, head) rows per attention workgroup
-constexpr int kChunkSplitKeys = 1024; // key-list entries per attention split
+#ifndef TS_CHUNK_SPLIT_KEYS
+#define TS_CHUNK_SPLIT_KEYS 1024
+#endif
+constexpr int kChunkSplitKeys = TS_CHUNK_SPLIT_KEYS;  // key-list entries per attention split
 constexpr int kChunkPartStride = 128 + 4;  // floats per split partial: o[128], m, l, pad
 
 struct ChunkParams {
@@ -95,16 +98,20 @@ struct ChunkParams {
   const int32_t* sel_count;   // [b]
   float* qbar;                // [b][H][d] fp32 mean query (output of the mean kernel)
   int32_t* past_lens;         // [b] P_r (output of the mean kernel)
-  float* partials;            // [b][max_chunk][H][splits][d + 2]
+  float* partials;            // [b][max_chunk][H][splits][kChunkPartStride]
+  int32_t* keytab;            // [b][max_keys] page * 16 + slot of each key-list entry
   void* out;                  // [b][max_chunk][H][d]
-  int H, Hkv, b, stride, max_chunk, sel_stride, n_local, splits;
+  int H, Hkv, b, stride, max_chunk, sel_stride, n_local, splits, max_keys;
   float attn_scale;
   int bf16;
 };
 
+// Upper bound of a chunk's key-list length: TopK below the window, window, chunk.
+__host__ __device__ inline long long chunk_max_keys(int top_k, int n_local, int max_chunk) {
+  return (long long)top_k + n_local + max_chunk;
+}
 __host__ __device__ inline int chunk_splits(int top_k, int n_local, int max_chunk) {
-  const long long keys = (long long)top_k + n_local + max_chunk;
-  return (int)((keys + kChunkSplitKeys - 1) / kChunkSplitKeys);
+  return (int)((chunk_max_keys(top_k, n_local, max_chunk) + kChunkSplitKeys - 1) / kChunkSplitKeys);
 }
 
 __host__ __device__ inline int attn_splits(int top_k, int n_local) {

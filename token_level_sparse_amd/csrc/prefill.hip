@@ -46,6 +46,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+constexpr float kRescaleSlack = 8.f;
 constexpr int kPartStride = kChunkPartStride;   // o[128], m, l, 2 pad: 16-byte aligned rows
 static_assert(kChunkPartStride == kHeadDim + 4, "partial row layout");
 
@@ -81,27 +82,67 @@ __device__ ChunkGeom chunk_geom(const ChunkParams& p, int r, bool with_sel) {
 
 // ---------------------------------------------------------------- mean query
 // One workgroup per (request, head): qbar = (sum_j q_j) / c with the sum in fp64
-// (exact for bf16 queries of ordinary range), rounded once to fp32.
+// (exact for bf16 queries of ordinary range), rounded once to fp32. Thread t owns
+// dims 8 (t % 16) + [0, 8) of rows j = t / 16 (mod 16): 16-byte loads, 16 rows in
+// flight per pass, then an LDS sum over the 16 row groups.
 template <bool kBf16>
 __global__ __launch_bounds__(256) void chunk_mean_kernel(ChunkParams p) {
-  __shared__ double s_acc[kHeadDim];
+  __shared__ double s_acc[16][kHeadDim];
   const int r = blockIdx.x / p.H, h = blockIdx.x - (blockIdx.x / p.H) * p.H;
   const ChunkGeom gm = chunk_geom(p, r, false);
-  const int d = threadIdx.x & (kHeadDim - 1), half = threadIdx.x >> 7;
-  double acc = 0.0;
-  for (int j = half; j < gm.c; j += 2) {
-    const int64_t idx = (((int64_t)r * p.max_chunk + j) * p.H + h) * kHeadDim + d;
-    const float x = kBf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(p.q)[idx] << 16)
-                          : static_cast<const float*>(p.q)[idx];
-    acc += (double)x;
+  const int dc = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  const int64_t row_stride = (int64_t)p.H * kHeadDim;
+  const int64_t base = ((int64_t)r * p.max_chunk * p.H + h) * kHeadDim + 8 * dc;
+#pragma unroll 4
+  for (int j = rg; j < gm.c; j += 16) {
+    if (kBf16) {
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + base + j * row_stride);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)bf16_lo(ws[e]);
+        acc[2 * e + 1] += (double)bf16_hi(ws[e]);
+      }
+    } else {
+      const float* src = static_cast<const float*>(p.q) + base + j * row_stride;
+      const float4 x0 = *reinterpret_cast<const float4*>(src);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      acc[0] += (double)x0.x; acc[1] += (double)x0.y; acc[2] += (double)x0.z; acc[3] += (double)x0.w;
+      acc[4] += (double)x1.x; acc[5] += (double)x1.y; acc[6] += (double)x1.z; acc[7] += (double)x1.w;
+    }
   }
-  if (half == 1) s_acc[d] = acc;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_acc[rg][8 * dc + e] = acc[e];
   __syncthreads();
-  if (half == 0) {
-    acc += s_acc[d];
-    p.qbar[((int64_t)r * p.H + h) * kHeadDim + d] = (float)(acc / (double)max(gm.c, 1));
+  if (threadIdx.x < kHeadDim) {
+    double t = 0.0;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) t += s_acc[g][threadIdx.x];
+    p.qbar[((int64_t)r * p.H + h) * kHeadDim + threadIdx.x] = (float)(t / (double)max(gm.c, 1));
   }
   if (h == 0 && threadIdx.x == 0) p.past_lens[r] = gm.P;
+}
+
+// ---------------------------------------------------------------- key list
+// keytab[r][x] = page * 16 + slot of key-list entry x of request r (x < base + c),
+// built once per request so the attention's K/V loads wait on one LDS read.
+__global__ __launch_bounds__(256) void chunk_keys_kernel(ChunkParams p) {
+  __shared__ int s_geom[5];
+  const int per = (p.max_keys + 255) / 256;
+  const int r = blockIdx.x / per, blk = blockIdx.x - (blockIdx.x / per) * per;
+  if (threadIdx.x == 0) {
+    const ChunkGeom gm = chunk_geom(p, r, true);
+    s_geom[0] = gm.c; s_geom[1] = gm.w0; s_geom[2] = gm.n_sel; s_geom[3] = gm.base; s_geom[4] = gm.N;
+  }
+  __syncthreads();
+  const int c = s_geom[0], w0 = s_geom[1], n_sel = s_geom[2], base = s_geom[3], N = s_geom[4];
+  const int x = blk * 256 + threadIdx.x;
+  if (x >= base + c || x >= p.max_keys) return;
+  int pos = x < n_sel ? p.sel_idx[(int64_t)r * p.sel_stride + x] : w0 + (x - n_sel);
+  pos = min(max(pos, 0), N - 1);
+  const int page = p.block_table[(int64_t)r * p.stride + (pos >> 4)];
+  p.keytab[(int64_t)r * p.max_keys + x] = page * kPage + (pos & (kPage - 1));
 }
 
 // ---------------------------------------------------------------- attention
@@ -122,32 +163,29 @@ template <> struct Tile<false> {
 constexpr int kChunkLds = Tile<true>::kLds > Tile<false>::kLds ? Tile<true>::kLds : Tile<false>::kLds;
 
 struct KeyMap {
-  const int32_t* sel;      // request's TopK row
-  const int32_t* bt;       // request's block-table row
-  int n_sel, w0, N, g, Hkv, x_end;
-  __device__ int64_t row(int x) const {          // element offset of key-list entry x
-    const int xc = min(x, x_end - 1);
-    int pos = xc < n_sel ? sel[xc] : w0 + (xc - n_sel);
-    pos = min(max(pos, 0), N - 1);
-    const int64_t page = bt[pos >> 4];
-    return ((page * Hkv + g) * kPage + (pos & (kPage - 1))) * kHeadDim;
-  }
+  const int64_t* off;      // LDS: element offset of the split's key-list entries (this KV head)
+  int x_begin, x_end;
+  __device__ int64_t row(int x) const { return off[min(x, x_end - 1) - x_begin]; }
 };
 
+// K: thread t stages dims 8 (t % 16) + [0, 8) of keys 4 (t / 16) + [0, 4).
+// V: thread t stages dims 8 (t / 16) + [0, 8) of keys 4 (t % 16) + [0, 4), so that
+// the transposed writes of a 32-lane group fill two whole V^T rows (no bank conflict).
 __device__ __forceinline__ void stage_load(Tile<true>& t, const uint16_t* kp, const uint16_t* vp,
                                            const KeyMap& km, int x0) {
   const int kq = threadIdx.x >> 4, dc = threadIdx.x & 15;
+  const int vq = threadIdx.x & 15, vc = threadIdx.x >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t off = km.row(x0 + 4 * kq + i) + 8 * dc;
-    t.k[i] = *reinterpret_cast<const uint4*>(kp + off);
-    t.v[i] = *reinterpret_cast<const uint4*>(vp + off);
+    t.k[i] = *reinterpret_cast<const uint4*>(kp + km.row(x0 + 4 * kq + i) + 8 * dc);
+    t.v[i] = *reinterpret_cast<const uint4*>(vp + km.row(x0 + 4 * vq + i) + 8 * vc);
   }
 }
 __device__ __forceinline__ void stage_store(const Tile<true>& t, char* lds) {
   uint16_t* Ks = reinterpret_cast<uint16_t*>(lds);
   uint16_t* Vt = Ks + Tile<true>::kKeys * Tile<true>::kKStride;
   const int kq = threadIdx.x >> 4, dc = threadIdx.x & 15;
+  const int vq = threadIdx.x & 15, vc = threadIdx.x >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     *reinterpret_cast<uint4*>(Ks + (4 * kq + i) * Tile<true>::kKStride + 8 * dc) = t.k[i];
@@ -161,7 +199,7 @@ __device__ __forceinline__ void stage_store(const Tile<true>& t, char* lds) {
     const int sh = (e & 1) ? 16 : 0;
     const uint32_t b0 = (w[0][e >> 1] >> sh) & 0xffffu, b1 = (w[1][e >> 1] >> sh) & 0xffffu;
     const uint32_t b2 = (w[2][e >> 1] >> sh) & 0xffffu, b3 = (w[3][e >> 1] >> sh) & 0xffffu;
-    *reinterpret_cast<uint2*>(Vt + (8 * dc + e) * Tile<true>::kVStride + 4 * kq) =
+    *reinterpret_cast<uint2*>(Vt + (8 * vc + e) * Tile<true>::kVStride + 4 * vq) =
         make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
   }
 }
@@ -241,12 +279,10 @@ __device__ __forceinline__ void pv_block(const char* lds, const float (&pv)[4][4
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2) {
     // B operand: keys 32 k2 + 4 a + [0, 4) then 32 k2 + 16 + 4 a + [0, 4)
-    const u32x4_t pw = {
-        (uint32_t)f32_to_bf16(pv[2 * k2][0]) | ((uint32_t)f32_to_bf16(pv[2 * k2][1]) << 16),
-        (uint32_t)f32_to_bf16(pv[2 * k2][2]) | ((uint32_t)f32_to_bf16(pv[2 * k2][3]) << 16),
-        (uint32_t)f32_to_bf16(pv[2 * k2 + 1][0]) | ((uint32_t)f32_to_bf16(pv[2 * k2 + 1][1]) << 16),
-        (uint32_t)f32_to_bf16(pv[2 * k2 + 1][2]) | ((uint32_t)f32_to_bf16(pv[2 * k2 + 1][3]) << 16)};
-    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+    // probabilities in [0, 1] to bf16 (round to nearest even, two per instruction)
+    const bf16x8_t pb = {(__bf16)pv[2 * k2][0], (__bf16)pv[2 * k2][1], (__bf16)pv[2 * k2][2],
+                         (__bf16)pv[2 * k2][3], (__bf16)pv[2 * k2 + 1][0], (__bf16)pv[2 * k2 + 1][1],
+                         (__bf16)pv[2 * k2 + 1][2], (__bf16)pv[2 * k2 + 1][3]};
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const uint16_t* vr = Vt + (16 * dt + l16) * Tile<true>::kVStride + 32 * k2 + 4 * a;
@@ -277,21 +313,29 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(ChunkParams p) {
   constexpr int KB = Tile<kBf16>::kKeys;
   constexpr int NT = KB / 16;
   __shared__ __align__(16) char s_lds[kChunkLds];
+  __shared__ int64_t s_keys[kChunkSplitKeys];
   __shared__ int s_geom[6];
 
   const int H = p.H, Hkv = p.Hkv, G = H / Hkv;
   const int rt = (p.max_chunk * G + kChunkRows - 1) / kChunkRows;
-  const int tile = blockIdx.x % rt;
-  const int g = (blockIdx.x / rt) % Hkv;
-  const int r = blockIdx.x / (rt * Hkv);
-  const int split = blockIdx.y;
+  // XCD-aware order: workgroup i runs on XCD i % 8. All row tiles of one unit
+  // (request, KV head, split) go to the same XCD, one after another, so the unit's
+  // staged K/V rows come from that XCD's L2 after the first tile.
+  const int units = p.b * Hkv * p.splits;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = (slot / rt) * kXcds + xcd;
+  if (u >= units) return;
+  const int tile = slot % rt;
+  const int split = u % p.splits;
+  const int g = (u / p.splits) % Hkv;
+  const int r = u / (p.splits * Hkv);
   if (threadIdx.x == 0) {
     const ChunkGeom gm = chunk_geom(p, r, true);
     s_geom[0] = gm.c; s_geom[1] = gm.P; s_geom[2] = gm.w0;
     s_geom[3] = gm.n_sel; s_geom[4] = gm.base; s_geom[5] = gm.N;
   }
   __syncthreads();
-  const int c = s_geom[0], w0 = s_geom[2], n_sel = s_geom[3], base = s_geom[4], N = s_geom[5];
+  const int c = s_geom[0], base = s_geom[4];
   const int rows = c * G;
   const int row0 = tile * kChunkRows;
   if (row0 >= rows) return;                                   // uniform over the workgroup
@@ -308,15 +352,22 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(ChunkParams p) {
   const int j = row_ok ? rho / G : 0;
   const int h = g * G + (row_ok ? rho - (rho / G) * G : 0);
   const int lim = row_ok ? base + j : -1;                     // last visible key-list entry
+  // smallest limit over the wave's rows (rows past the chunk count as fully visible)
+  const int wave_j0 = min(row0 + 16 * wave, rows - 1) / G;
+  const int wave_lim = base + wave_j0;
 
   const T* qrow = static_cast<const T*>(p.q) + (((int64_t)r * p.max_chunk + j) * H + h) * kHeadDim;
   QOp q;
   load_qop(q, qrow, row_ok, a);
 
+  const int32_t* kt = p.keytab + (int64_t)r * p.max_keys;
+  for (int x = x_begin + (int)threadIdx.x; x < x_end; x += 256) {
+    const int v = kt[x];                                       // page * 16 + slot
+    s_keys[x - x_begin] = (((int64_t)(v >> 4) * Hkv + g) * kPage + (v & (kPage - 1))) * kHeadDim;
+  }
+  __syncthreads();
   KeyMap km;
-  km.sel = p.sel_idx + (int64_t)r * p.sel_stride;
-  km.bt = p.block_table + (int64_t)r * p.stride;
-  km.n_sel = n_sel; km.w0 = w0; km.N = N; km.g = g; km.Hkv = Hkv; km.x_end = x_end;
+  km.off = s_keys; km.x_begin = x_begin; km.x_end = x_end;
   const T* kp = static_cast<const T*>(p.k_pool);
   const T* vp = static_cast<const T*>(p.v_pool);
 
@@ -338,37 +389,46 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(ChunkParams p) {
     qk_block(s_lds, q, l16, a, s);
     float pv[NT][4];
     float mloc = kNegInf;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int x = x0 + 16 * t + 4 * a + i;
-        pv[t][i] = (x < x_end && x <= lim) ? s[t][i] * sl2 : kNegInf;
-        mloc = fmaxf(mloc, pv[t][i]);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    float alpha = 1.f, psum = 0.f;
-    if (m_new != kNegInf) {
-      alpha = fast_exp2(m_run - m_new);
+    if (x0 + KB <= x_end && x0 + KB - 1 <= wave_lim) {   // wave-uniform: no key of a valid row masked
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv[t][i] = fast_exp2(pv[t][i] - m_new);
-          psum += pv[t][i];
+          pv[t][i] = s[t][i] * sl2;
+          mloc = fmaxf(mloc, pv[t][i]);
         }
     } else {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[t][i] = 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int x = x0 + 16 * t + 4 * a + i;
+          pv[t][i] = (x < x_end && x <= lim) ? s[t][i] * sl2 : kNegInf;
+          mloc = fmaxf(mloc, pv[t][i]);
+        }
     }
-    l_run = fmaf(l_run, alpha, psum);
-    m_run = m_new;
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    // Rescale only when some row's block maximum exceeds its running maximum by more
+    // than kRescaleSlack (base 2): o and l stay relative to the same m_run, so the
+    // result is unchanged, and probabilities stay below 2^kRescaleSlack.
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[t][i] = (pv[t][i] == kNegInf) ? 0.f : fast_exp2(pv[t][i] - m_run);
+        psum += pv[t][i];
+      }
+    l_run += psum;
     pv_block(s_lds, pv, l16, a, o);
   }
 
@@ -384,35 +444,43 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(ChunkParams p) {
   }
 }
 
-// One workgroup per (request, chunk query): merge the splits of every head.
+// Merge the splits of each (request, chunk query, head) row: 32 threads per row,
+// 4 dims each, 8 rows per workgroup.
 template <bool kBf16>
 __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkParams p) {
-  __shared__ int s_geom[2];
-  const int r = blockIdx.x / p.max_chunk, j = blockIdx.x - (blockIdx.x / p.max_chunk) * p.max_chunk;
-  if (threadIdx.x == 0) {
-    const ChunkGeom gm = chunk_geom(p, r, true);
-    s_geom[0] = gm.c; s_geom[1] = gm.base;
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int64_t rows = (int64_t)p.b * p.max_chunk * p.H;
+  if (row >= rows) return;
+  const int h = (int)(row % p.H);
+  const int j = (int)((row / p.H) % p.max_chunk);
+  const int r = (int)(row / ((int64_t)p.H * p.max_chunk));
+  const ChunkGeom gm = chunk_geom(p, r, true);
+  if (j >= gm.c) return;
+  const int S = min(p.splits, (gm.base + j + kChunkSplitKeys) / kChunkSplitKeys);
+  const int d4 = 4 * (threadIdx.x & 31);
+  const float* src = p.partials + row * p.splits * kPartStride;
+  float M = kNegInf;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, src[s * kPartStride + kHeadDim]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < S; ++s) {
+    const float ms = src[s * kPartStride + kHeadDim];
+    const float w = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
+    L = fmaf(w, src[s * kPartStride + kHeadDim + 1], L);
+    const float4 o = *reinterpret_cast<const float4*>(src + s * kPartStride + d4);
+    acc.x = fmaf(w, o.x, acc.x); acc.y = fmaf(w, o.y, acc.y);
+    acc.z = fmaf(w, o.z, acc.z); acc.w = fmaf(w, o.w, acc.w);
   }
-  __syncthreads();
-  const int c = s_geom[0], base = s_geom[1];
-  if (j >= c) return;
-  const int S = min(p.splits, (base + j + kChunkSplitKeys) / kChunkSplitKeys);
-  const int d = threadIdx.x & (kHeadDim - 1);
-  for (int h = threadIdx.x >> 7; h < p.H; h += 2) {
-    const float* src = p.partials + (((int64_t)r * p.max_chunk + j) * p.H + h) * p.splits * kPartStride;
-    float M = kNegInf;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, src[s * kPartStride + kHeadDim]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float ms = src[s * kPartStride + kHeadDim];
-      const float w = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
-      L = fmaf(w, src[s * kPartStride + kHeadDim + 1], L);
-      acc = fmaf(w, src[s * kPartStride + d], acc);
-    }
-    const float res = acc / L;
-    const int64_t oi = (((int64_t)r * p.max_chunk + j) * p.H + h) * kHeadDim + d;
-    if (kBf16) static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(res);
-    else static_cast<float*>(p.out)[oi] = res;
+  const float inv = 1.f / L;
+  const int64_t oi = row * kHeadDim + d4;
+  if (kBf16) {
+    uint2 v;
+    v.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
+    v.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + oi) = v;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + oi) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
 }
 
@@ -428,10 +496,13 @@ hipError_t launch_chunk_mean(const ChunkParams& p, hipStream_t s) {
 hipError_t launch_chunk_attn(const ChunkParams& p, hipStream_t s) {
   const int G = p.H / p.Hkv;
   const int rt = (p.max_chunk * G + kChunkRows - 1) / kChunkRows;
-  const dim3 grid(p.b * p.Hkv * rt, p.splits), block(256);
+  const dim3 block(256);
+  hipLaunchKernelGGL(chunk_keys_kernel, dim3(p.b * ((p.max_keys + 255) / 256)), block, 0, s, p);
+  const int units = p.b * p.Hkv * p.splits;
+  const dim3 grid(kXcds * rt * ((units + kXcds - 1) / kXcds));
   if (p.bf16) hipLaunchKernelGGL(chunk_attn_kernel<true>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(chunk_attn_kernel<false>, grid, block, 0, s, p);
-  const dim3 cgrid(p.b * p.max_chunk);
+  const dim3 cgrid((unsigned)(((int64_t)p.b * p.max_chunk * p.H + 7) / 8));
   if (p.bf16) hipLaunchKernelGGL(chunk_combine_kernel<true>, cgrid, block, 0, s, p);
   else hipLaunchKernelGGL(chunk_combine_kernel<false>, cgrid, block, 0, s, p);
   return hipGetLastError();
