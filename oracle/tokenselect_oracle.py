@@ -247,3 +247,30 @@ def decode_sequence(qs, K, V, lens, k: int, n_local: int, theta: float,
             outs.append(sparse_attention(qs[t], Kt, Vt, union_local(T, N, n_local), attn_scale))
     return {"hit": np.array(hits), "cos": np.array(coss), "T": Ts,
             "out": np.array(outs) if want_outputs else None}
+
+
+# ---------------------------------------------------------------- dynamic top-p budget
+def topp_count(v, p: float, k_max: int) -> int:
+    """Budget of the dynamic top-p selection: the smallest m such that the m largest
+    votes (ties to the lower position) hold at least p of the total vote mass,
+    capped at k_max and at N.
+
+    RTPurbo team post, dynamic token selection: keep the tokens whose cumulative
+    score mass reaches p instead of a fixed top-k; UniPrefill page: keep the minimal
+    set whose importance sum reaches 99% of the total. Applied to the head soft vote
+    (total mass H). 0 < p <= 1.
+    """
+    v = _f64(v)
+    N = v.shape[0]
+    if N == 0:
+        return 0
+    order = np.lexsort((np.arange(N), -v))
+    csum = np.cumsum(v[order])
+    target = p * csum[-1]
+    m = int(np.searchsorted(csum, target, side="left")) + 1
+    return min(m, k_max, N)
+
+
+def topp_indices(v, p: float, k_max: int) -> np.ndarray:
+    """The dynamic top-p set: the topp_count(v, p, k_max) largest votes, ascending."""
+    return topk_indices(v, topp_count(v, p, k_max))

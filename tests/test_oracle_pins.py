@@ -327,3 +327,57 @@ def test_soft_vote_recalls_every_heads_top_planted_token_naive_does_not():
     naive = ora.naive_topk(q, K, geo.top_k)
     # the naive TopK over raw logits is dominated by the large-scale KV head
     assert not np.all(np.isin(best, naive))
+
+
+# ------------------------------------------------------------------ dynamic top-p budget
+def test_topp_hand_cases():
+    gx = _load("topp_hand.json")
+    for cs in gx["cases"]:
+        m = ora.topp_count(cs["v"], cs["p"], cs["k_max"])
+        assert m == cs["m"], cs
+        assert ora.topp_indices(cs["v"], cs["p"], cs["k_max"]).tolist() == cs["T"], cs
+
+
+def test_topp_brute_force_small():
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        N = int(rng.integers(1, 7))
+        v = rng.integers(0, 5, N).astype(np.float64)   # integer masses: ties and exact sums
+        if v.sum() == 0:
+            v[0] = 1.0
+        p = float(rng.choice([0.2, 0.5, 0.75, 0.9, 1.0]))
+        kmax = int(rng.integers(1, N + 2))
+        # brute force: the smallest m whose best m-subset (by mass) reaches p of the total
+        best = None
+        for m in range(1, N + 1):
+            top = max(sum(v[list(c)]) for c in itertools.combinations(range(N), m))
+            if top >= p * v.sum():
+                best = m
+                break
+        assert ora.topp_count(v, p, kmax) == min(best, kmax, N), (v, p, kmax)
+        T = ora.topp_indices(v, p, kmax)
+        # the chosen positions are the largest votes, lower positions first among equals
+        m = len(T)
+        key = sorted(range(N), key=lambda i: (-v[i], i))[:m]
+        assert sorted(key) == T.tolist()
+
+
+def test_topp_full_mass_and_cap_reduce_to_topk():
+    rng = np.random.default_rng(12)
+    v = rng.random(500)
+    assert np.array_equal(ora.topp_indices(v, 1.0, 40), ora.topk_indices(v, 40))
+    # a tiny p keeps the single largest vote
+    assert ora.topp_indices(v, 1e-9, 40).tolist() == [int(np.argmax(v))]
+
+
+def test_topp_peaked_vote_selects_few_planted_tokens():
+    # a needle-like distribution: most vote mass on the planted tokens (no scale
+    # spread, so every head's softmax concentrates on its planted keys)
+    geo = wl.workload("llama3-8b-128k", seq_len=4096, n_planted=16)
+    b = wl.make_batch(geo, scale_spread=False)
+    r = b.requests[0]
+    sel = ora.select(_np(r.q), _np(r.k), 256)
+    T = ora.topp_indices(sel["vote"], 0.9, 4096)
+    planted = np.unique(r.planted_pos.numpy())
+    assert len(T) <= 2 * len(planted)
+    assert np.isin(T, planted).mean() > 0.5
