@@ -54,7 +54,8 @@
  *   vote       fp32 log2 of the head soft vote, log2 v_i: request r, token i at
  *              off_r + i (finite where the linear vote would underflow fp32).
  *   sel_idx    int32 [batch][top_k]: the TopK positions of request r, ascending,
- *              in the first sel_count[r] = min(top_k, N_r) entries.
+ *              in the first sel_count[r] = min(top_k, N_r) entries (the top-p
+ *              budget instead when ts_select.top_p > 0).
  *   out        [batch][H][d] element type `dtype` (bf16 results are rounded to
  *              nearest even from fp32 accumulators).
  */
@@ -99,6 +100,14 @@ typedef struct {
                                  1.0 is the printed vote equation (raw logits)  */
   float attn_scale;           /* SDPA scale, normally 1/sqrt(d)                  */
   double cos_threshold;       /* theta: reuse the cached selection iff cos >= theta */
+  double top_p;               /* 0: fixed TopK budget. 0 < p <= 1: dynamic top-p budget,
+                                 the fewest largest votes holding at least p of the
+                                 vote mass, capped at top_k (RTPurbo post, dynamic
+                                 token selection and its histogram top-p kernel;
+                                 UniPrefill page, minimal set holding 99% of the
+                                 importance). Vote masses are taken as the integers
+                                 rint(v * 2^40), so the budget is exact and
+                                 deterministic; sel_count[r] receives it. */
 } ts_select;
 
 /* Selection Cache state, caller-owned device buffers kept across steps
@@ -131,7 +140,8 @@ ts_status tokenselect_score(const ts_shape* shape, const ts_select* sel,
    (deepnotes head soft vote equation), computed as lv_i = log2 v_i by a
    log-sum-exp over the heads, and TopK over all N_r positions: the k largest
    votes (largest lv), ties to the lower position, written ascending to
-   sel_idx[r][0 .. sel_count[r]) with sel_count[r] = min(top_k, N_r). `vote`
+   sel_idx[r][0 .. sel_count[r]) with sel_count[r] = min(top_k, N_r) (with top_p > 0:
+   the top-p budget, at most min(top_k, N_r)). `vote`
    (max_total_tokens floats) receives lv and may be NULL; then lv stays in the
    workspace. The local window is not written: step 5 adds it. */
 ts_status tokenselect_vote_topk(const ts_shape* shape, const ts_select* sel,

@@ -181,3 +181,18 @@ def test_prefill_validation_before_launch(lib):
     st = lib.tokenselect_prefill_chunk(ctypes.byref(shape), ctypes.byref(sel), 512, misaligned, FAKE,
                                        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
     assert st == ts.TS_ERR_INVALID_ARG and "16-byte" in lib.tokenselect_last_error().decode()
+
+
+@pytest.mark.parametrize("p", [-0.1, 1.5, float("nan")])
+def test_invalid_top_p_rejected(lib, p):
+    shape, sel = _shape(), _sel(top_p=p)
+    assert ts.workspace_size(shape, sel) == 0
+    st = lib.tokenselect_vote_topk(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE, None,
+                                   FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == ts.TS_ERR_INVALID_ARG and "top_p" in lib.tokenselect_last_error().decode()
+
+
+def test_top_p_field_layout(lib):
+    # the binding's struct matches the header's field order and size
+    assert ctypes.sizeof(ts.Select) == 4 * 4 + 8 + 8
+    assert ts.Select.top_p.offset == 24

@@ -63,6 +63,7 @@ class Select(ctypes.Structure):
         ("score_scale", ctypes.c_float),
         ("attn_scale", ctypes.c_float),
         ("cos_threshold", ctypes.c_double),
+        ("top_p", ctypes.c_double),
     ]
 
 
@@ -150,8 +151,8 @@ def make_shape(num_q_heads, num_kv_heads, batch, block_table_stride, max_total_t
 
 
 def make_select(top_k, n_local, score_scale=1.0, attn_scale=1.0 / 128 ** 0.5,
-                cos_threshold=0.9) -> Select:
-    return Select(top_k, n_local, score_scale, attn_scale, cos_threshold)
+                cos_threshold=0.9, top_p=0.0) -> Select:
+    return Select(top_k, n_local, score_scale, attn_scale, cos_threshold, top_p)
 
 
 def workspace_size(shape: Shape, sel: Select) -> int:

@@ -58,7 +58,7 @@ constexpr int kMaxGrid = 2048;
 
 // Byte offsets of the workspace regions.
 struct Layout {
-  size_t logits, partials, stats, vote, hist, state, tiles, attn, total;
+  size_t logits, partials, stats, vote, hist, mass, mstate, state, tiles, attn, total;
 };
 
 int64_t max_chunks(const ts_shape& s) {
@@ -85,6 +85,8 @@ Layout layout(const ts_shape& s, const ts_select& sel) {
   L.stats = off;    off += align_up(sizeof(float) * 2 * (size_t)H * s.batch);
   L.vote = off;     off += align_up(sizeof(float) * (size_t)T);
   L.hist = off;     off += align_up(sizeof(uint32_t) * 3 * ts::kHistBins * (size_t)s.batch);
+  L.mass = off;     off += align_up(sizeof(uint64_t) * 3 * ts::kHistBins * (size_t)s.batch);
+  L.mstate = off;   off += align_up(sizeof(uint64_t) * 4 * (size_t)s.batch);
   L.state = off;    off += align_up(sizeof(int32_t) * 8 * (size_t)s.batch);
   L.tiles = off;    off += align_up(sizeof(int32_t) * 2 * (size_t)max_tiles(s));
   const int S = ts::attn_splits(eff_top_k(s, sel), eff_local(s, sel));
@@ -117,6 +119,8 @@ ts_status check_shape(const ts_shape* s, const ts_select* sel) {
     return fail(TS_ERR_UNSUPPORTED, "dtype %d is neither TS_F32 nor TS_BF16", s->dtype);
   if (sel->top_k < 1) return fail(TS_ERR_INVALID_ARG, "top_k %d < 1", sel->top_k);
   if (sel->n_local < 0) return fail(TS_ERR_INVALID_ARG, "n_local %d < 0", sel->n_local);
+  if (!(sel->top_p >= 0.0 && sel->top_p <= 1.0))
+    return fail(TS_ERR_INVALID_ARG, "top_p %g outside [0, 1] (0 turns the top-p budget off)", sel->top_p);
   return TS_OK;
 }
 
@@ -178,6 +182,10 @@ ts::VoteParams vote_params(const ts_shape& s, const ts_select& sel, const float*
   p.logits = logits; p.head_stats = stats; p.seq_lens = seq; p.skip = skip;
   p.vote = vote ? vote : at<float>(ws, L.vote);
   p.hist = at<uint32_t>(ws, L.hist);
+  p.mass = at<unsigned long long>(ws, L.mass);
+  p.mstate = at<unsigned long long>(ws, L.mstate);
+  p.topp = sel.top_p > 0.0;
+  p.top_p = sel.top_p;
   p.state = at<int32_t>(ws, L.state);
   p.tile_counts = at<int32_t>(ws, L.tiles);
   p.sel_idx = sel_idx; p.sel_count = sel_count;
@@ -440,6 +448,7 @@ ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel, c
   ts::CacheParams cp{};
   cp.q = q; cp.cached_q = cache->cached_q; cp.valid = cache->valid; cp.hit = hit;
   cp.hist = at<uint32_t>(ws, L.hist);
+  cp.mass = sel->top_p > 0.0 ? at<unsigned long long>(ws, L.mass) : nullptr;
   cp.H = shape->num_q_heads; cp.d = shape->head_dim; cp.b = shape->batch;
   cp.theta = sel->cos_threshold; cp.bf16 = shape->dtype == TS_BF16;
   if ((st = device_status(ts::launch_cache_check(cp, stream), "cache check launch")) != TS_OK) return st;

@@ -85,6 +85,10 @@ __global__ __launch_bounds__(256) void cache_check_kernel(CacheParams p) {
   for (int64_t j = threadIdx.x; j < nchunks; j += blockDim.x) dst[j] = src[j];
   uint32_t* h = p.hist + (int64_t)r * 3 * kHistBins;
   for (int i = threadIdx.x; i < 3 * kHistBins; i += blockDim.x) h[i] = 0u;
+  if (p.mass) {
+    unsigned long long* m = p.mass + (int64_t)r * 3 * kHistBins;
+    for (int i = threadIdx.x; i < 3 * kHistBins; i += blockDim.x) m[i] = 0ull;
+  }
   if (threadIdx.x == 0) p.valid[r] = 1;
 }
 

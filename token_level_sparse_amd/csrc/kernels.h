@@ -39,13 +39,22 @@ struct VoteParams {
   const int32_t* skip;
   float* vote;                // ragged [N_r]
   uint32_t* hist;             // [b][3][kHistBins]
+  unsigned long long* mass;   // [b][3][kHistBins] integer vote mass per bin (top-p)
+  unsigned long long* mstate; // [b][4] top-p state (target, mass left after digits 0, 1)
   int32_t* state;             // [b][8] select state (digits found, counts left)
   int32_t* tile_counts;       // [tiles][2] (greater, equal) per tile
   int32_t* sel_idx;           // [b][top_k]
   int32_t* sel_count;         // [b]
   int H, G, b, top_k;
+  int topp;                   // nonzero: dynamic top-p budget with fraction top_p, capped at top_k
+  double top_p;
   int grid;                   // workgroups of the tile kernels
 };
+
+// Integer vote mass of the top-p budget: rint(v * 2^kMassBits) with v = 2^lv. Votes
+// are at most H <= 256, so a request's total stays below 2^48 + N; integer sums are
+// exact and independent of the order of the atomics.
+constexpr int kMassBits = 40;
 
 struct AttnParams {
   const void* q;
@@ -70,6 +79,7 @@ struct CacheParams {
   int32_t* valid;
   int32_t* hit;
   uint32_t* hist;             // zeroed for the requests that reselect
+  unsigned long long* mass;   // zeroed too when non-null (top-p)
   int H, d, b;
   double theta;
   int bf16;

@@ -25,6 +25,15 @@
 //   tile, keys above the exact threshold and keys equal to it, and write
 //   positions through a prefix over tiles; equal keys are taken in position
 //   order until k is reached, so the result is deterministic.
+// * Dynamic top-p budget (RTPurbo team post: dynamic token selection and its
+//   histogram-based top-p decode kernel; UniPrefill page: the minimal set holding
+//   99% of the importance). Each vote also carries an integer mass
+//   q = rint(v * 2^40), v = 2^lv, and every histogram pass accumulates per-bin masses
+//   beside the counts (64-bit integer atomics: exact and order-independent, so the
+//   budget is deterministic). At each digit the walk from the top stops at the
+//   first bin where either k keys or the target mass ceil(p * sum q) is reached, so
+//   one radix walk gives min(top-p budget, k); the keys equal to the final threshold
+//   are taken in position order up to that count.
 #include <algorithm>
 
 #include "common.h"
@@ -46,10 +55,21 @@ constexpr int kRefineMaxGrid = TS_REFINE_MAX_GRID;
 constexpr int kPerThread = kVoteTile / kThreads;   // positions per thread
 constexpr float kLog2eF = 1.4426950408889634f;
 
+typedef unsigned long long u64;
+
 // Order-preserving map of an fp32 value to uint32 (larger value, larger key).
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+  const uint32_t u = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+  return __uint_as_float(u);
+}
+
+// Integer mass of a log2 vote: rint(2^(lv + kMassBits)).
+__device__ __forceinline__ u64 vote_mass(float lv) {
+  return (u64)rint(exp2((double)lv + (double)kMassBits));
 }
 
 struct Tables {
@@ -79,6 +99,74 @@ __device__ uint32_t block_excl_scan(uint32_t x, uint32_t* s_w) {
   for (int w = 0; w < wave; ++w) base += s_w[w];
   __syncthreads();
   return base + inc - x;
+}
+
+__device__ u64 block_excl_scan64(u64 x, u64* s_w) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  u64 inc = x;
+  for (int o = 1; o < 64; o <<= 1) {
+    const u64 t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) s_w[wave] = inc;
+  __syncthreads();
+  u64 base = 0;
+  for (int w = 0; w < wave; ++w) base += s_w[w];
+  __syncthreads();
+  return base + inc - x;
+}
+
+// Digit of the top-p walk: walking the bins from the top, the first bin where the
+// cumulative count reaches kk or the cumulative mass reaches mm. s_out = {bin,
+// kk - count above}, *s_mres = mm - mass above.
+template <int kBins>
+__device__ void find_digit_pk(const uint32_t* hist, const u64* mhist, int kk, u64 mm, int* s_out,
+                              u64* s_mres, uint32_t* s_w, u64* s_w64, int* s_bin) {
+  constexpr int kPer = kBins / kThreads;
+  const int hi = kBins - kPer * threadIdx.x;
+  uint32_t c[kPer];
+  u64 m[kPer];
+  uint32_t sc = 0;
+  u64 sm = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    c[e] = hist[hi - 1 - e]; m[e] = mhist[hi - 1 - e];
+    sc += c[e]; sm += m[e];
+  }
+  if (threadIdx.x == 0) { s_bin[0] = -1; s_bin[1] = -1; }
+  const uint32_t ac = block_excl_scan(sc, s_w);
+  const u64 am = block_excl_scan64(sm, s_w64);
+  if (ac < (uint32_t)kk && (uint32_t)kk <= ac + sc) {
+    uint32_t acc = ac;
+    bool done = false;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (!done && acc + c[e] >= (uint32_t)kk) { s_bin[0] = hi - 1 - e; done = true; }
+      acc += c[e];
+    }
+  }
+  if (am < mm && mm <= am + sm) {
+    u64 acc = am;
+    bool done = false;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (!done && acc + m[e] >= mm) { s_bin[1] = hi - 1 - e; done = true; }
+      acc += m[e];
+    }
+  }
+  __syncthreads();
+  const int bin = max(max(s_bin[0], s_bin[1]), 0);
+  if (threadIdx.x == (kBins - 1 - bin) / kPer) {
+    uint32_t acc = ac;
+    u64 accm = am;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (hi - 1 - e > bin) { acc += c[e]; accm += m[e]; }
+    s_out[0] = bin;
+    s_out[1] = kk - (int)acc;
+    *s_mres = mm - accm;
+  }
+  __syncthreads();
 }
 
 // Digit holding the kk-th largest key among the counts in hist[0..kBins) (bins in
@@ -137,10 +225,11 @@ __device__ __forceinline__ void load_group(const float* zg, int i, float (&x)[G]
   }
 }
 
-template <int G>
+template <int G, bool kTopP>
 __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
   __shared__ Tables tb;
   __shared__ uint32_t s_hist[kHistBins];
+  __shared__ u64 s_mass[kTopP ? kHistBins : 1];
   __shared__ float s_m[256], s_l[256];
   build_tables(tb, p);
   const int H = p.H, Hkv = H / G;
@@ -154,6 +243,11 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
     uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
     for (int i = threadIdx.x; i < kHistBins; i += kThreads)
       if (s_hist[i]) atomicAdd(&gh[i], s_hist[i]);
+    if (kTopP) {
+      u64* gm = p.mass + (int64_t)r * 3 * kHistBins;
+      for (int i = threadIdx.x; i < kHistBins; i += kThreads)
+        if (s_mass[i]) atomicAdd(&gm[i], s_mass[i]);
+    }
   };
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int r = find_segment(tb.tile, p.b, tile);
@@ -163,6 +257,8 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
       if (cur_r >= 0) flush(cur_r);
       __syncthreads();
       for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_hist[i] = 0;
+      if (kTopP)
+        for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_mass[i] = 0;
       // x_hi = (z_hi - M_h) log2e - log2 Z_h; z - M is exact near the head maximum
       for (int h = threadIdx.x; h < H; h += kThreads) {
         s_m[h] = p.head_stats[((int64_t)r * H + h) * 2 + 0];
@@ -206,7 +302,9 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
       if (i < N) {
         const float lv = m[e] + __builtin_amdgcn_logf(s[e]);
         vout[i] = lv;
-        atomicAdd(&s_hist[order_key(lv) >> (32 - kDigitBits0)], 1u);
+        const uint32_t bin = order_key(lv) >> (32 - kDigitBits0);
+        atomicAdd(&s_hist[bin], 1u);
+        if (kTopP) atomicAdd(&s_mass[bin], vote_mass(lv));
       }
     }
   }
@@ -217,20 +315,26 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
 // Four kernels, one per phase; every workgroup loops over its share of the tiles.
 // (A single cooperative kernel with grid barriers between the phases was measured
 // on MI355X at 321 us per 1M-token step against 26 us for the four launches.)
+template <bool kTopP>
 struct SelectShared {
   Tables tb;
   uint32_t hist[kHistBins];
+  u64 mass[kTopP ? kHistBins : 1];
   uint32_t w[4];
+  u64 w64[4];
+  u64 mres;
   int dig[2];
+  int bin[2];
   int cnt[2][4];
 };
 
 // kPass 1: find digit 0 from hist[0], histogram digit 1 of matching keys into hist[1].
 // kPass 2: read digit 0 from state, find digit 1 from hist[1], histogram digit 2 into hist[2].
 // A workgroup finds a request's digit once, accumulates its LDS histogram over all
-// its tiles of that request and flushes it once.
-template <int kPass>
-__device__ void refine_phase(const VoteParams& p, SelectShared& sh) {
+// its tiles of that request and flushes it once. With kTopP the masses go along and
+// each digit comes from the count-or-mass walk.
+template <int kPass, bool kTopP>
+__device__ void refine_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
   const int total = sh.tb.tile[p.b];
   constexpr int kShift = (kPass == 1) ? (32 - kDigitBits0) : (32 - kDigitBits0 - kDigitBits1);
   constexpr int kNextBits = (kPass == 1) ? kDigitBits1 : kDigitBits2;
@@ -242,12 +346,23 @@ __device__ void refine_phase(const VoteParams& p, SelectShared& sh) {
     uint32_t* gn = p.hist + ((int64_t)r * 3 + kPass) * kHistBins;
     for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads)
       if (sh.hist[i]) atomicAdd(&gn[i], sh.hist[i]);
+    if (kTopP) {
+      u64* gm = p.mass + ((int64_t)r * 3 + kPass) * kHistBins;
+      for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads)
+        if (sh.mass[i]) atomicAdd(&gm[i], sh.mass[i]);
+    }
+  };
+  auto record = [&](int r) {
+    int32_t* st = p.state + r * 8;
+    if (kPass == 1) { st[0] = sh.dig[0]; st[1] = sh.dig[1]; }
+    else { st[2] = sh.dig[0]; st[3] = sh.dig[1]; }
+    if (kTopP) p.mstate[r * 4 + kPass] = sh.mres;
   };
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int r = find_segment(sh.tb.tile, p.b, tile);
     const int t = tile - sh.tb.tile[r];
     const int N = p.seq_lens[r];
-    if (p.top_k >= N) continue;                       // whole request selected: no radix work
+    if (!kTopP && p.top_k >= N) continue;             // whole request selected: no radix work
     const int i0 = t * kVoteTile + threadIdx.x;
     uint32_t key[kPerThread];
     load_keys(p.vote + sh.tb.tok[r], i0, N, key);
@@ -256,60 +371,103 @@ __device__ void refine_phase(const VoteParams& p, SelectShared& sh) {
       __syncthreads();
       int32_t* st = p.state + r * 8;
       const uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
+      const u64* gm = p.mass + (int64_t)r * 3 * kHistBins;
       if (kPass == 1) {
-        find_digit<1 << kDigitBits0>(gh, p.top_k, sh.dig, sh.w);
+        if (kTopP) {
+          // target mass: ceil(p * total mass of the request)
+          u64 part = 0;
+          for (int i = threadIdx.x; i < kHistBins; i += kThreads) part += gm[i];
+          const u64 Q = block_excl_scan64(part, sh.w64) + part;    // inclusive: thread 255 holds the total
+          if (threadIdx.x == kThreads - 1) sh.mres = Q;
+          __syncthreads();
+          const u64 total_mass = sh.mres;
+          __syncthreads();
+          u64 target = (u64)ceil(p.top_p * (double)total_mass);
+          if (target < 1) target = 1;
+          if (t == 0 && threadIdx.x == 0) p.mstate[r * 4 + 0] = target;
+          find_digit_pk<1 << kDigitBits0>(gh, gm, min(p.top_k, N), target, sh.dig, &sh.mres, sh.w,
+                                          sh.w64, sh.bin);
+        } else {
+          find_digit<1 << kDigitBits0>(gh, p.top_k, sh.dig, sh.w);
+        }
         prefix = (uint32_t)sh.dig[0];
-        if (t == 0 && threadIdx.x == 0) { st[0] = sh.dig[0]; st[1] = sh.dig[1]; }
       } else {
         const int d0 = st[0], k0 = st[1];
-        find_digit<1 << kDigitBits1>(gh + kHistBins, k0, sh.dig, sh.w);
+        if (kTopP)
+          find_digit_pk<1 << kDigitBits1>(gh + kHistBins, gm + kHistBins, k0, p.mstate[r * 4 + 1],
+                                          sh.dig, &sh.mres, sh.w, sh.w64, sh.bin);
+        else
+          find_digit<1 << kDigitBits1>(gh + kHistBins, k0, sh.dig, sh.w);
         prefix = ((uint32_t)d0 << kDigitBits1) | (uint32_t)sh.dig[0];
-        if (t == 0 && threadIdx.x == 0) { st[2] = sh.dig[0]; st[3] = sh.dig[1]; }
       }
+      if (t == 0 && threadIdx.x == 0) record(r);
       for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads) sh.hist[i] = 0;
+      if (kTopP)
+        for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads) sh.mass[i] = 0;
       __syncthreads();
       cur_r = r;
     } else if (t == 0 && threadIdx.x == 0) {
-      int32_t* st = p.state + r * 8;
-      if (kPass == 1) { st[0] = sh.dig[0]; st[1] = sh.dig[1]; }
-      else { st[2] = sh.dig[0]; st[3] = sh.dig[1]; }
+      record(r);
     }
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      if (i0 + e * kThreads < N && (key[e] >> kShift) == prefix)
-        atomicAdd(&sh.hist[(key[e] >> kNextShift) & ((1u << kNextBits) - 1)], 1u);
+      if (i0 + e * kThreads < N && (key[e] >> kShift) == prefix) {
+        const uint32_t bin = (key[e] >> kNextShift) & ((1u << kNextBits) - 1);
+        atomicAdd(&sh.hist[bin], 1u);
+        if (kTopP) atomicAdd(&sh.mass[bin], vote_mass(key_value(key[e])));
+      }
     }
   }
   if (cur_r >= 0) flush(cur_r);
 }
 
-// Exact threshold key of request r and how many keys equal to it are taken.
-__device__ void threshold(const VoteParams& p, int r, uint32_t& key_t, int& take_eq,
-                          SelectShared& sh, bool record) {
+// Exact threshold key of request r, how many keys equal to it are taken, and the
+// size of the selection (top_k, or the top-p budget capped at min(top_k, N)).
+template <bool kTopP>
+__device__ void threshold(const VoteParams& p, int r, int N, uint32_t& key_t, int& take_eq, int& m_sel,
+                          SelectShared<kTopP>& sh, bool record) {
   int32_t* st = p.state + r * 8;
   const int d0 = st[0], d1 = st[2], k1 = st[3];
-  find_digit<1 << kDigitBits2>(p.hist + ((int64_t)r * 3 + 2) * kHistBins, k1, sh.dig, sh.w);
+  const uint32_t* h2 = p.hist + ((int64_t)r * 3 + 2) * kHistBins;
+  if (kTopP) {
+    find_digit_pk<1 << kDigitBits2>(h2, p.mass + ((int64_t)r * 3 + 2) * kHistBins, k1,
+                                    p.mstate[r * 4 + 2], sh.dig, &sh.mres, sh.w, sh.w64, sh.bin);
+  } else {
+    find_digit<1 << kDigitBits2>(h2, k1, sh.dig, sh.w);
+  }
   key_t = ((uint32_t)d0 << (kDigitBits1 + kDigitBits2)) | ((uint32_t)d1 << kDigitBits2) |
           (uint32_t)sh.dig[0];
-  take_eq = sh.dig[1];
-  if (record && threadIdx.x == 0) { st[4] = sh.dig[0]; st[5] = sh.dig[1]; }
+  const int kres = sh.dig[1];
+  if (kTopP) {
+    // keys equal to key_t all carry the same mass q; take just enough of them
+    const u64 q = vote_mass(key_value(key_t));
+    const u64 mres = sh.mres;
+    const u64 need = q ? (mres + q - 1) / q : (u64)kres;
+    take_eq = (int)min((u64)kres, need);
+    m_sel = min(p.top_k, N) - kres + take_eq;
+  } else {
+    take_eq = kres;
+    m_sel = p.top_k;
+  }
+  if (record && threadIdx.x == 0) { st[4] = sh.dig[0]; st[5] = take_eq; st[6] = m_sel; }
 }
 
 // Per tile: keys above the exact threshold and keys equal to it.
-__device__ void count_phase(const VoteParams& p, SelectShared& sh) {
+template <bool kTopP>
+__device__ void count_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
   const int total = sh.tb.tile[p.b];
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int r = find_segment(sh.tb.tile, p.b, tile);
     const int t = tile - sh.tb.tile[r];
     const int N = p.seq_lens[r];
-    if (p.top_k >= N) continue;
+    if (!kTopP && p.top_k >= N) continue;
     const int i0 = t * kVoteTile + threadIdx.x;
     uint32_t key[kPerThread];
     load_keys(p.vote + sh.tb.tok[r], i0, N, key);
     __syncthreads();
     uint32_t key_t;
-    int take_eq;
-    threshold(p, r, key_t, take_eq, sh, t == 0);
+    int take_eq, m_sel;
+    threshold<kTopP>(p, r, N, key_t, take_eq, m_sel, sh, t == 0);
     int gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -330,7 +488,8 @@ __device__ void count_phase(const VoteParams& p, SelectShared& sh) {
 }
 
 // Ascending positions through a prefix over the request's tiles.
-__device__ void write_phase(const VoteParams& p, SelectShared& sh) {
+template <bool kTopP>
+__device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
   const int total = sh.tb.tile[p.b];
   // a request with no positions (a first prefill chunk) has no tile to do it
   if (blockIdx.x == 0)
@@ -342,13 +501,15 @@ __device__ void write_phase(const VoteParams& p, SelectShared& sh) {
     const int N = p.seq_lens[r];
     const int k = p.top_k;
     int32_t* out = p.sel_idx + (int64_t)r * k;
-    if (t == 0 && threadIdx.x == 0) p.sel_count[r] = min(k, N);
     // this thread owns kPerThread consecutive positions
     const int i0 = t * kVoteTile + threadIdx.x * kPerThread;
-    if (k >= N) {
-      for (int e = 0; e < kPerThread; ++e)
-        if (i0 + e < N) out[i0 + e] = i0 + e;
-      continue;
+    if (!kTopP) {
+      if (t == 0 && threadIdx.x == 0) p.sel_count[r] = min(k, N);
+      if (k >= N) {
+        for (int e = 0; e < kPerThread; ++e)
+          if (i0 + e < N) out[i0 + e] = i0 + e;
+        continue;
+      }
     }
     const float* lv = p.vote + sh.tb.tok[r];
     float x[kPerThread];
@@ -363,8 +524,9 @@ __device__ void write_phase(const VoteParams& p, SelectShared& sh) {
     }
     __syncthreads();
     uint32_t key_t;
-    int take_eq;
-    threshold(p, r, key_t, take_eq, sh, false);
+    int take_eq, m_sel;
+    threshold<kTopP>(p, r, N, key_t, take_eq, m_sel, sh, false);
+    if (kTopP && t == 0 && threadIdx.x == 0) p.sel_count[r] = m_sel;
     gtb = wave_sum_i(gtb);
     eqb = wave_sum_i(eqb);
     const int wave = threadIdx.x >> 6;
@@ -397,14 +559,14 @@ __device__ void write_phase(const VoteParams& p, SelectShared& sh) {
   }
 }
 
-template <int kPhase>
+template <int kPhase, bool kTopP>
 __global__ __launch_bounds__(kThreads) void select_phase_kernel(VoteParams p) {
-  __shared__ SelectShared sh;
+  __shared__ SelectShared<kTopP> sh;
   build_tables(sh.tb, p);
-  if (kPhase == 1) refine_phase<1>(p, sh);
-  if (kPhase == 2) refine_phase<2>(p, sh);
-  if (kPhase == 3) count_phase(p, sh);
-  if (kPhase == 4) write_phase(p, sh);
+  if (kPhase == 1) refine_phase<1, kTopP>(p, sh);
+  if (kPhase == 2) refine_phase<2, kTopP>(p, sh);
+  if (kPhase == 3) count_phase<kTopP>(p, sh);
+  if (kPhase == 4) write_phase<kTopP>(p, sh);
 }
 
 __global__ void zero_u32(uint32_t* x, int64_t n) {
@@ -412,32 +574,40 @@ __global__ void zero_u32(uint32_t* x, int64_t n) {
     x[i] = 0u;
 }
 
-}  // namespace
-
-hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist) {
+template <bool kTopP>
+hipError_t launch_vote_topk_t(const VoteParams& p, hipStream_t s, bool zero_hist) {
   if (zero_hist) {
     const int64_t n = (int64_t)p.b * 3 * kHistBins;
     hipLaunchKernelGGL(zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.hist, n);
+    if (kTopP)
+      hipLaunchKernelGGL(zero_u32, dim3((unsigned)((2 * n + 255) / 256)), dim3(256), 0, s,
+                         reinterpret_cast<uint32_t*>(p.mass), 2 * n);
   }
   const dim3 grid(p.grid), block(kThreads);
   const dim3 vgrid(std::min(p.grid, kVoteMaxGrid));
   switch (p.G) {
-    case 1: hipLaunchKernelGGL(vote_kernel<1>, vgrid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL(vote_kernel<2>, vgrid, block, 0, s, p); break;
-    case 3: hipLaunchKernelGGL(vote_kernel<3>, vgrid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL(vote_kernel<4>, vgrid, block, 0, s, p); break;
-    case 5: hipLaunchKernelGGL(vote_kernel<5>, vgrid, block, 0, s, p); break;
-    case 6: hipLaunchKernelGGL(vote_kernel<6>, vgrid, block, 0, s, p); break;
-    case 7: hipLaunchKernelGGL(vote_kernel<7>, vgrid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL(vote_kernel<8>, vgrid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((vote_kernel<1, kTopP>), vgrid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((vote_kernel<2, kTopP>), vgrid, block, 0, s, p); break;
+    case 3: hipLaunchKernelGGL((vote_kernel<3, kTopP>), vgrid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((vote_kernel<4, kTopP>), vgrid, block, 0, s, p); break;
+    case 5: hipLaunchKernelGGL((vote_kernel<5, kTopP>), vgrid, block, 0, s, p); break;
+    case 6: hipLaunchKernelGGL((vote_kernel<6, kTopP>), vgrid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL((vote_kernel<7, kTopP>), vgrid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((vote_kernel<8, kTopP>), vgrid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   const dim3 rgrid(std::min(p.grid, kRefineMaxGrid));
-  hipLaunchKernelGGL(select_phase_kernel<1>, rgrid, block, 0, s, p);
-  hipLaunchKernelGGL(select_phase_kernel<2>, grid, block, 0, s, p);
-  hipLaunchKernelGGL(select_phase_kernel<3>, grid, block, 0, s, p);
-  hipLaunchKernelGGL(select_phase_kernel<4>, grid, block, 0, s, p);
+  hipLaunchKernelGGL((select_phase_kernel<1, kTopP>), rgrid, block, 0, s, p);
+  hipLaunchKernelGGL((select_phase_kernel<2, kTopP>), grid, block, 0, s, p);
+  hipLaunchKernelGGL((select_phase_kernel<3, kTopP>), grid, block, 0, s, p);
+  hipLaunchKernelGGL((select_phase_kernel<4, kTopP>), grid, block, 0, s, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist) {
+  return p.topp ? launch_vote_topk_t<true>(p, s, zero_hist) : launch_vote_topk_t<false>(p, s, zero_hist);
 }
 
 }  // namespace ts
