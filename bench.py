@@ -15,7 +15,8 @@ bandwidth against the 8 TB/s peak (roofline), the same metric at N = 131072
 Selection Cache sequence on Qwen2-7B shapes (selection_cache: steps/s, hit rate,
 hit vector), chunk-wise prefill at 128K and 1M cached tokens with 512-token chunks
 (prefill: chunks/s, selection GB/s, chunk-attention TFLOP/s against the bf16
-matrix-core peak), and the fp64 oracle timed on host cores (cpu_baseline).
+matrix-core peak), the 1M decode step with the dynamic top-p budget (top_p: p = 0.9,
+capped at k), and the fp64 oracle timed on host cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -169,6 +170,44 @@ def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False):
     del layers, ws, logits, KC, VC
     torch.cuda.empty_cache()
     return res, host
+
+
+def time_topp(geo, n_layers, steps, warmup, dev, top_p=0.9):
+    """Decode steps with the dynamic top-p budget (ts_select.top_p) instead of the
+    fixed TopK, every step reselecting; reports steps/s and the mean budget."""
+    import torch
+    import token_level_sparse_amd as ts
+    KC, VC = kv_cache(geo, n_layers, dev)
+    layers = [Layer(geo, l, dev, False, (KC[l], VC[l])) for l in range(n_layers)]
+    L0 = layers[0]
+    shape = ts.make_shape(geo.num_q_heads, geo.num_kv_heads, 1, L0.block_table.shape[1], L0.total,
+                          geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, 2.0, top_p)
+    ws = ts.alloc_workspace(shape, sel, dev)
+
+    def step(s):
+        L = layers[s % n_layers]
+        ts.decode_step(shape, sel, L.q, L.k_pool, L.v_pool, L.block_table, L.seq_lens, L.cache,
+                       L.hit, L.out, ws)
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        step(s)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    budgets = [int(L.cache.cached_count[0]) for L in layers]
+    log(f"[{geo.name}] top-p {top_p}: decode step {ms:.4f} ms, mean budget {sum(budgets) / len(budgets):.1f}")
+    res = {"workload": geo.name, "top_p": top_p, "top_k_cap": geo.top_k, "layers": n_layers,
+           "decode_steps_per_s": 1e3 / ms, "ms_per_step": ms,
+           "mean_budget": sum(budgets) / len(budgets), "budgets": budgets}
+    del layers, ws, KC, VC
+    torch.cuda.empty_cache()
+    return res
 
 
 def time_ragged(geo, steps, warmup, dev):
@@ -428,10 +467,11 @@ def main():
         secondary = {"workload": g1.name, "N": g1.seq_len, "decode_steps_per_s": 1e3 / r1["ms_per_step"],
                      "ms_per_step": r1["ms_per_step"], "score_ms": r1["score_ms"],
                      "score_gbps": r1["score_gbps"], "k_gbps": r1["k_gbps"], "rotating_layers": 8}
-    ragged = cache_seq = prefill = None
+    ragged = cache_seq = prefill = topp = None
     if not args.no_secondary:
         ragged = time_ragged(wl.workload("llama3-8b-ragged16"), max(8, args.steps // 4), 2, dev)
         cache_seq = time_cache_sequence(wl.workload("qwen2-7b-cache256"), dev)
+        topp = time_topp(geo, 8, max(16, args.steps // 2), 4, dev)
         prefill = [time_prefill(wl.workload("prefill-llama3-128k"), 8, max(16, args.steps // 2), 4, dev),
                    time_prefill(wl.workload("prefill-llama3-1m"), 4, max(8, args.steps // 8), 2, dev)]
     cpu = cpu_baseline(geo, host) if host is not None else None
@@ -465,6 +505,7 @@ def main():
         "ragged_batch": ragged,
         "selection_cache": cache_seq,
         "prefill": prefill,
+        "top_p": topp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
