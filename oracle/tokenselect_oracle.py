@@ -274,3 +274,57 @@ def topp_count(v, p: float, k_max: int) -> int:
 def topp_indices(v, p: float, k_max: int) -> np.ndarray:
     """The dynamic top-p set: the topp_count(v, p, k_max) largest votes, ascending."""
     return topk_indices(v, topp_count(v, p, k_max))
+
+
+# ---------------------------------------------------------------- selection-function ablations
+def hard_vote_topk(z, k: int) -> np.ndarray:
+    """Head hard vote: every head takes its own TopK of its raw logits, a position
+    scores the number of heads that picked it, and the TopK of those counts is the
+    selection (ties to the lower position, ascending).
+
+    [DN] selection-function design: T_head-vote = TopK(sum_h I(i in TopK(Q^h K^h^T))),
+    the improvement over the naive TopK that keeps the heads independent.
+    """
+    z = _f64(z)
+    H, N = z.shape
+    counts = np.zeros(N, dtype=np.float64)
+    for h in range(H):
+        counts[topk_indices(z[h], k)] += 1.0
+    return topk_indices(counts, k)
+
+
+def block_scores(v, block: int) -> np.ndarray:
+    """Block criticality for block-level selection: the sum of the head soft votes of
+    the block's positions (blocks of ``block`` consecutive positions, the last one
+    possibly shorter)."""
+    v = _f64(v)
+    N = v.shape[0]
+    nb = -(-N // block)
+    pad = np.zeros(nb * block)
+    pad[:N] = v
+    return pad.reshape(nb, block).sum(axis=1)
+
+
+def block_topk(v, k: int, block: int) -> np.ndarray:
+    """Block-level selection with a budget of k tokens: the max(1, k // block) blocks
+    of largest summed vote (ties to the lower block), expanded to their positions,
+    ascending. block = 1 is the token-level TopK.
+
+    [DN] token-level motivation (Fig. 2b) and [BL] section 2: prior methods split
+    the cache into non-overlapping blocks and select blocks by an estimated
+    criticality; a block with one critical token is kept whole and a critical token
+    in a low-scoring block is lost.
+    """
+    N = len(v)
+    nb_sel = max(1, k // block)
+    blocks = topk_indices(block_scores(v, block), nb_sel)
+    pos = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    return pos[pos < N].astype(np.int64)
+
+
+def recall(selected, reference) -> float:
+    """Fraction of the reference positions that the selection contains."""
+    reference = np.asarray(reference)
+    if reference.size == 0:
+        return 1.0
+    return float(np.isin(reference, np.asarray(selected)).mean())

@@ -381,3 +381,72 @@ def test_topp_peaked_vote_selects_few_planted_tokens():
     planted = np.unique(r.planted_pos.numpy())
     assert len(T) <= 2 * len(planted)
     assert np.isin(T, planted).mean() > 0.5
+
+
+# ------------------------------------------------------------------ selection-function ablations
+def test_ablation_hand_cases():
+    gx = _load("ablation_hand.json")
+    hv = gx["hard_vote"]
+    z = np.array(hv["z"])
+    assert ora.hard_vote_topk(z, hv["k"]).tolist() == hv["T"]
+    assert ora.topk_indices(z.max(axis=0), hv["k"]).tolist() == hv["naive_T"]
+    bl = gx["block"]
+    v = np.array(bl["v"])
+    assert ora.topk_indices(v, bl["k"]).tolist() == bl["token_T"]
+    for cs in bl["cases"]:
+        if "sums" in cs:
+            np.testing.assert_allclose(ora.block_scores(v, cs["block"]), cs["sums"], rtol=1e-15)
+        T = ora.block_topk(v, bl["k"], cs["block"])
+        assert T.tolist() == cs["T"]
+        assert ora.recall(T, bl["token_T"]) == cs["recall"]
+
+
+def test_hard_vote_single_head_is_per_head_topk():
+    rng = np.random.default_rng(13)
+    z = rng.standard_normal((1, 300))
+    for k in (1, 7, 64):
+        assert np.array_equal(ora.hard_vote_topk(z, k), np.sort(np.argsort(-z[0], kind="stable")[:k]))
+
+
+def test_hard_vote_brute_force_counts():
+    rng = np.random.default_rng(14)
+    for _ in range(50):
+        H, N, k = int(rng.integers(1, 5)), int(rng.integers(2, 9)), int(rng.integers(1, 5))
+        z = rng.integers(-3, 4, (H, N)).astype(np.float64)
+        counts = np.zeros(N)
+        for h in range(H):
+            # this head's k best positions, lower position first among equal logits
+            best = sorted(range(N), key=lambda i: (-z[h, i], i))[:k]
+            counts[best] += 1
+        exp = sorted(sorted(range(N), key=lambda i: (-counts[i], i))[:k])
+        assert ora.hard_vote_topk(z, k).tolist() == exp
+
+
+def test_block_selection_reduces_to_token_level_and_covers_blocks():
+    rng = np.random.default_rng(15)
+    v = rng.random(1000) ** 8
+    assert np.array_equal(ora.block_topk(v, 64, 1), ora.topk_indices(v, 64))
+    for B in (2, 8, 32, 128):
+        T = ora.block_topk(v, 256, B)
+        assert len(T) == (256 // B) * B
+        blocks = np.unique(T // B)
+        assert len(blocks) == 256 // B and np.all(np.isin(blocks * B, T))
+        # brute force: no unselected block has a larger sum than a selected one
+        sums = ora.block_scores(v, B)
+        rest = np.setdiff1d(np.arange(len(sums)), blocks)
+        assert sums[blocks].min() >= sums[rest].max()
+
+
+def test_block_recall_falls_with_granularity_on_scattered_tokens():
+    # scattered critical tokens (planted at uniform positions): token-level selection
+    # recalls all of the token-level TopK, block-level selection loses more of it as
+    # blocks grow (the deepnotes page's Fig. 2b trend, on synthetic data)
+    geo = wl.workload("llama3-8b-128k", seq_len=16384, n_planted=32, top_k=512)
+    b = wl.make_batch(geo, scale_spread=False)
+    r = b.requests[0]
+    v = ora.select(_np(r.q), _np(r.k), geo.top_k)["vote"]
+    ref = ora.topk_indices(v, geo.top_k)
+    rec = [ora.recall(ora.block_topk(v, geo.top_k, B), ref) for B in (1, 4, 16, 64, 128)]
+    assert rec[0] == 1.0
+    assert all(x >= y for x, y in zip(rec, rec[1:]))
+    assert rec[-1] < 0.6
