@@ -450,3 +450,13 @@ def test_block_recall_falls_with_granularity_on_scattered_tokens():
     assert rec[0] == 1.0
     assert all(x >= y for x, y in zip(rec, rec[1:]))
     assert rec[-1] < 0.6
+
+
+def test_block_budget_rounds_down_and_recall_is_over_the_reference():
+    v = np.array([0.1, 0.9, 0.0, 0.0, 0.3, 0.3, 0.3, 0.0, 0.05, 0.05])
+    # budget 5 with blocks of 2: two whole blocks (4 tokens), never more than k
+    T = ora.block_topk(v, 5, 2)
+    assert T.tolist() == [0, 1, 4, 5]
+    # recall is the covered fraction of the reference set
+    assert ora.recall([1, 2, 3], [1]) == 1.0
+    assert ora.recall([1], [1, 2, 3, 4]) == 0.25
