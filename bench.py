@@ -16,7 +16,9 @@ Selection Cache sequence on Qwen2-7B shapes (selection_cache: steps/s, hit rate,
 hit vector), chunk-wise prefill at 128K and 1M cached tokens with 512-token chunks
 (prefill: chunks/s, selection GB/s, chunk-attention TFLOP/s against the bf16
 matrix-core peak), the 1M decode step with the dynamic top-p budget (top_p: p = 0.9,
-capped at k), and the fp64 oracle timed on host cores (cpu_baseline).
+capped at k), the selection-function ablations at 128K (ablations: time from logits
+to TopK and recall for the soft vote, naive TopK, head hard vote and block selection
+at block sizes 2-128), and the fp64 oracle timed on host cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -208,6 +210,52 @@ def time_topp(geo, n_layers, steps, warmup, dev, top_p=0.9):
     del layers, ws, KC, VC
     torch.cuda.empty_cache()
     return res
+
+
+def time_ablations(geo, dev, reps=10):
+    """Selection-function ablations on one layer: time from logits to TopK for the
+    head soft vote, the naive TopK, the head hard vote and block selection; recall of
+    the planted critical tokens and of the soft-vote TopK (recall vs granularity)."""
+    import numpy as np
+    import torch
+    import token_level_sparse_amd as ts
+    from synth import workloads as wl
+    batch = wl.make_batch(geo, device=dev)
+    H, total = geo.num_q_heads, batch.total_tokens
+    shape = ts.make_shape(H, geo.num_kv_heads, 1, batch.block_table.shape[1], total, geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale)
+    ws = ts.alloc_workspace(shape, sel, dev)
+    logits = torch.empty(H * total, dtype=torch.float32, device=dev)
+    stats = torch.empty(H * 2, dtype=torch.float32, device=dev)
+    ts.score(shape, sel, batch.q, batch.k_pool, batch.block_table, batch.seq_lens, logits, stats, ws)
+    planted = np.unique(batch.requests[0].planted_pos.cpu().numpy())
+    si = torch.empty(1, geo.top_k, dtype=torch.int32, device=dev)
+    sc = torch.empty(1, dtype=torch.int32, device=dev)
+    runs = [("soft_vote", ts.SELECT_SOFT_VOTE, 1), ("naive_topk", ts.SELECT_NAIVE_TOPK, 1),
+            ("hard_vote", ts.SELECT_HARD_VOTE, 1)] + [(f"block_{B}", ts.SELECT_BLOCK, B) for B in (2, 4, 8, 16, 32, 64, 128)]
+    res, soft = {}, None
+    for name, fn, B in runs:
+        aws = ts.alloc_ablation_workspace(shape, sel, fn, B, dev)
+        call = lambda: ts.select_ablation(shape, sel, fn, B, logits, stats, batch.seq_lens, None, si, sc, aws)
+        call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(); call(); b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+        T = si[0, : int(sc[0])].cpu().numpy()
+        if soft is None:
+            soft = T
+        res[name] = {"ms": ms, "selected": int(len(T)),
+                     "planted_recall": float(np.isin(planted, T).mean()),
+                     "recall_of_soft_vote_topk": float(np.isin(soft, T).mean())}
+        del aws
+    log(f"[{geo.name}] ablations: " + ", ".join(f"{k} {v['ms']:.3f} ms planted {v['planted_recall']:.3f} "
+                                                 f"soft-recall {v['recall_of_soft_vote_topk']:.3f}" for k, v in res.items()))
+    del batch, ws, logits
+    torch.cuda.empty_cache()
+    return {"workload": geo.name, "N": total, "top_k": geo.top_k, "selectors": res}
 
 
 def time_ragged(geo, steps, warmup, dev):
@@ -467,11 +515,12 @@ def main():
         secondary = {"workload": g1.name, "N": g1.seq_len, "decode_steps_per_s": 1e3 / r1["ms_per_step"],
                      "ms_per_step": r1["ms_per_step"], "score_ms": r1["score_ms"],
                      "score_gbps": r1["score_gbps"], "k_gbps": r1["k_gbps"], "rotating_layers": 8}
-    ragged = cache_seq = prefill = topp = None
+    ragged = cache_seq = prefill = topp = ablations = None
     if not args.no_secondary:
         ragged = time_ragged(wl.workload("llama3-8b-ragged16"), max(8, args.steps // 4), 2, dev)
         cache_seq = time_cache_sequence(wl.workload("qwen2-7b-cache256"), dev)
         topp = time_topp(geo, 8, max(16, args.steps // 2), 4, dev)
+        ablations = time_ablations(wl.workload("llama3-8b-128k"), dev)
         prefill = [time_prefill(wl.workload("prefill-llama3-128k"), 8, max(16, args.steps // 2), 4, dev),
                    time_prefill(wl.workload("prefill-llama3-1m"), 4, max(8, args.steps // 8), 2, dev)]
     cpu = cpu_baseline(geo, host) if host is not None else None
@@ -506,6 +555,7 @@ def main():
         "selection_cache": cache_seq,
         "prefill": prefill,
         "top_p": topp,
+        "ablations": ablations,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -231,6 +231,41 @@ ts_status tokenselect_prefill_chunk(const ts_shape* shape, const ts_select* sel,
                                     int32_t* sel_idx, int32_t* sel_count, void* out, void* ws,
                                     size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- selection-function ablations
+   Alternatives to the head soft vote, over the decode logits and head statistics
+   of tokenselect_score (deepnotes page, selection-function design and the token-level
+   motivation, Fig. 2b; blog review section 2). Each writes a TopK in the decode
+   sel_idx / sel_count layout (ascending, ties to the lower position):
+     TS_SELECT_SOFT_VOTE  the head soft vote (same result as tokenselect_vote_topk);
+     TS_SELECT_NAIVE_TOPK a position scores its largest raw logit over the H heads;
+     TS_SELECT_HARD_VOTE  every head takes its own TopK(top_k) of its logits, a position
+                          scores the number of heads that picked it, then TopK of the
+                          counts; needs batch * H <= 1024;
+     TS_SELECT_BLOCK      blocks of `block` positions score the sum of their tokens'
+                          votes, as log2 sum 2^lv (fp64 in position order, rounded once
+                          to fp32); the max(1, top_k / block) best blocks are expanded
+                          to their positions (sel_count counts them; a request's last
+                          block may be short).
+   `score` (optional, may be NULL) receives what the final TopK ran on: log2 votes,
+   max logits, or head counts ([sum N_r] floats), or block scores ([sum ceil(N_r / block)]).
+   top_p must be 0. */
+typedef enum {
+  TS_SELECT_SOFT_VOTE = 0,
+  TS_SELECT_NAIVE_TOPK = 1,
+  TS_SELECT_HARD_VOTE = 2,
+  TS_SELECT_BLOCK = 3
+} ts_select_fn;
+
+/* Workspace bytes of tokenselect_select_ablation; 0 if the arguments are invalid. */
+size_t tokenselect_ablation_workspace_size(const ts_shape* shape, const ts_select* sel, int32_t fn,
+                                           int32_t block);
+
+ts_status tokenselect_select_ablation(const ts_shape* shape, const ts_select* sel, int32_t fn,
+                                      int32_t block, const float* logits, const float* head_stats,
+                                      const int32_t* seq_lens, float* score, int32_t* sel_idx,
+                                      int32_t* sel_count, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
+
 /* Static text for a status code. */
 const char* tokenselect_status_string(ts_status status);
 

@@ -132,8 +132,13 @@ def naive_topk(q, K, k: int, score_scale: float = 1.0) -> np.ndarray:
     score is its largest raw logit over the H heads (the concatenated logits
     reduced to positions). Ascending output.
     """
-    z = score_logits(q, K, score_scale)
-    return topk_indices(z.max(axis=0), k)
+    return naive_topk_from_logits(score_logits(q, K, score_scale), k)
+
+
+def naive_topk_from_logits(z, k: int) -> np.ndarray:
+    """The naive TopK's selection step on given logits [H][N]: each position scores
+    its largest logit over the heads."""
+    return topk_indices(_f64(z).max(axis=0), k)
 
 
 # ---------------------------------------------------------------- step 5

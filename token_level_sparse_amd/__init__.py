@@ -32,6 +32,8 @@ ENTRY_POINTS = (
     "tokenselect_prefill_select",
     "tokenselect_chunk_attn",
     "tokenselect_prefill_chunk",
+    "tokenselect_ablation_workspace_size",
+    "tokenselect_select_ablation",
     "tokenselect_status_string",
     "tokenselect_last_error",
 )
@@ -112,6 +114,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tokenselect_prefill_chunk.argtypes = [sp, selp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                               sz, vp]
     lib.tokenselect_prefill_chunk.restype = ctypes.c_int
+    lib.tokenselect_ablation_workspace_size.argtypes = [sp, selp, i32, i32]
+    lib.tokenselect_ablation_workspace_size.restype = sz
+    lib.tokenselect_select_ablation.argtypes = [sp, selp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.tokenselect_select_ablation.restype = ctypes.c_int
     lib.tokenselect_status_string.argtypes = [ctypes.c_int]
     lib.tokenselect_status_string.restype = ctypes.c_char_p
     lib.tokenselect_last_error.argtypes = []
@@ -263,3 +269,28 @@ def prefill_chunk(shape, sel, max_chunk, q_chunk, chunk_lens, k_pool, v_pool, bl
                                          _ptr(block_table), _ptr(seq_lens), _ptr(sel_idx),
                                          _ptr(sel_count), _ptr(out), _ptr(ws), ws.numel(),
                                          _stream(stream)))
+
+
+# ---------------------------------------------------------------- selection-function ablations
+SELECT_SOFT_VOTE, SELECT_NAIVE_TOPK, SELECT_HARD_VOTE, SELECT_BLOCK = range(4)
+
+
+def ablation_workspace_size(shape: Shape, sel: Select, fn: int, block: int = 1) -> int:
+    return int(load_library().tokenselect_ablation_workspace_size(ctypes.byref(shape), ctypes.byref(sel),
+                                                                  int(fn), int(block)))
+
+
+def alloc_ablation_workspace(shape: Shape, sel: Select, fn: int, block: int = 1, device="cuda") -> torch.Tensor:
+    n = ablation_workspace_size(shape, sel, fn, block)
+    if n == 0:
+        raise TokenSelectError(TS_ERR_INVALID_ARG, load_library().tokenselect_last_error().decode())
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def select_ablation(shape, sel, fn, block, logits, head_stats, seq_lens, score, sel_idx, sel_count, ws,
+                    stream=None):
+    lib = load_library()
+    _check(lib.tokenselect_select_ablation(ctypes.byref(shape), ctypes.byref(sel), int(fn), int(block),
+                                           _ptr(logits), _ptr(head_stats), _ptr(seq_lens), _ptr(score),
+                                           _ptr(sel_idx), _ptr(sel_count), _ptr(ws), ws.numel(),
+                                           _stream(stream)))

@@ -311,9 +311,130 @@ ts_status prefill_select_launch(const ts_shape& s, const ts_select& sel, int max
   return device_status(ts::launch_vote_topk(vp, stream, true), "vote/top-k launch");
 }
 
+// ---------------------------------------------------------------- ablations
+struct AblLayout {
+  size_t vote, score, head_scores, head_sel, head_cnt, seg_lens, hist, mstate, state, tiles, total;
+  int segs, stride;
+  int64_t positions;           // positions the radix select may see in one call
+};
+
+AblLayout abl_layout(const ts_shape& s, const ts_select& sel, int fn, int block) {
+  AblLayout L;
+  const int64_t T = s.max_total_tokens;
+  const int H = s.num_q_heads;
+  const bool hard = fn == ts::kAblHardVote, blk = fn == ts::kAblBlock;
+  L.segs = hard ? s.batch * H : s.batch;
+  L.stride = blk ? std::max(1, sel.top_k / block) : sel.top_k;
+  L.positions = hard ? (int64_t)H * T : T;
+  size_t off = 0;
+  L.vote = off;        off += align_up(sizeof(float) * (size_t)T);
+  L.score = off;       off += align_up(sizeof(float) * (size_t)(T + s.batch));
+  L.head_scores = off; off += hard ? align_up(sizeof(float) * (size_t)H * T) : 0;
+  L.head_sel = off;    off += align_up(sizeof(int32_t) * (size_t)L.segs * L.stride);
+  L.head_cnt = off;    off += align_up(sizeof(int32_t) * (size_t)L.segs);
+  L.seg_lens = off;    off += align_up(sizeof(int32_t) * (size_t)L.segs);
+  L.hist = off;        off += align_up(sizeof(uint32_t) * 3 * ts::kHistBins * (size_t)L.segs);
+  L.mstate = off;      off += align_up(sizeof(uint64_t) * 4 * (size_t)L.segs);
+  L.state = off;       off += align_up(sizeof(int32_t) * 8 * (size_t)L.segs);
+  L.tiles = off;       off += align_up(sizeof(int32_t) * 2 * (size_t)(cdiv(L.positions, ts::kVoteTile) + L.segs));
+  L.total = off;
+  return L;
+}
+
+ts_status check_ablation(const ts_shape& s, const ts_select& sel, int fn, int block) {
+  if (fn < ts::kAblSoftVote || fn > ts::kAblBlock)
+    return fail(TS_ERR_INVALID_ARG, "selection function %d is not a ts_select_fn", fn);
+  if (fn == ts::kAblBlock && (block < 1 || block > 4096))
+    return fail(TS_ERR_INVALID_ARG, "block %d outside [1, 4096]", block);
+  if (fn == ts::kAblHardVote && (int64_t)s.batch * s.num_q_heads > ts::kMaxBatch)
+    return fail(TS_ERR_UNSUPPORTED, "hard vote needs batch x num_q_heads <= %d (one TopK segment per head)",
+                ts::kMaxBatch);
+  if (fn == ts::kAblHardVote && (int64_t)s.num_q_heads * s.max_total_tokens > INT32_MAX)
+    return fail(TS_ERR_UNSUPPORTED, "hard vote needs num_q_heads x max_total_tokens < 2^31");
+  if (sel.top_p != 0.0) return fail(TS_ERR_UNSUPPORTED, "the ablations use a fixed top_k (top_p must be 0)");
+  return TS_OK;
+}
+
+ts::VoteParams abl_vote_params(const AblLayout& L, void* ws, const float* score, const int32_t* lens,
+                               int segs, int top_k, int32_t* sel_idx, int32_t* sel_count) {
+  ts::VoteParams p{};
+  p.vote = const_cast<float*>(score);
+  p.seq_lens = lens;
+  p.hist = at<uint32_t>(ws, L.hist);
+  p.mstate = at<unsigned long long>(ws, L.mstate);
+  p.state = at<int32_t>(ws, L.state);
+  p.tile_counts = at<int32_t>(ws, L.tiles);
+  p.sel_idx = sel_idx; p.sel_count = sel_count;
+  p.b = segs; p.top_k = top_k;
+  p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxGrid, cdiv(L.positions, ts::kVoteTile) + segs));
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t tokenselect_ablation_workspace_size(const ts_shape* shape, const ts_select* sel, int32_t fn,
+                                           int32_t block) {
+  if (check_shape(shape, sel) != TS_OK || check_ablation(*shape, *sel, fn, block) != TS_OK) return 0;
+  return abl_layout(*shape, *sel, fn, block).total;
+}
+
+ts_status tokenselect_select_ablation(const ts_shape* shape, const ts_select* sel, int32_t fn,
+                                      int32_t block, const float* logits, const float* head_stats,
+                                      const int32_t* seq_lens, float* score, int32_t* sel_idx,
+                                      int32_t* sel_count, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  ts_status st = check_shape(shape, sel);
+  if (st != TS_OK) return st;
+  if ((st = check_ablation(*shape, *sel, fn, block)) != TS_OK) return st;
+  TS_REQUIRE(logits); TS_REQUIRE(seq_lens); TS_REQUIRE(sel_idx); TS_REQUIRE(sel_count);
+  if (fn == ts::kAblSoftVote || fn == ts::kAblBlock) TS_REQUIRE(head_stats);
+  const AblLayout L = abl_layout(*shape, *sel, fn, block);
+  if (!ws) return fail(TS_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws_bytes < L.total) return fail(TS_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(TS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int b = shape->batch, H = shape->num_q_heads, k = sel->top_k;
+  float* sc = score ? score : at<float>(ws, L.score);
+  ts::AblationParams ap{};
+  ap.logits = logits; ap.seq_lens = seq_lens; ap.seg_lens = at<int32_t>(ws, L.seg_lens);
+  ap.score = sc; ap.head_scores = at<float>(ws, L.head_scores);
+  ap.head_sel = at<int32_t>(ws, L.head_sel); ap.head_cnt = at<int32_t>(ws, L.head_cnt);
+  ap.head_stride = L.stride; ap.vote = at<float>(ws, L.vote);
+  ap.sel_idx = sel_idx; ap.sel_count = sel_count;
+  ap.H = H; ap.Hkv = shape->num_kv_heads; ap.b = b; ap.top_k = k; ap.block = block;
+  auto soft_votes = [&](float* dst) {
+    ts::VoteParams vp = abl_vote_params(L, ws, dst, seq_lens, b, k, sel_idx, sel_count);
+    vp.logits = logits; vp.head_stats = head_stats; vp.H = H; vp.G = H / shape->num_kv_heads;
+    return vp;
+  };
+  switch (fn) {
+    case ts::kAblSoftVote:
+      return device_status(ts::launch_vote_topk(soft_votes(sc), stream, true), "vote/top-k launch");
+    case ts::kAblNaive: {
+      if ((st = device_status(ts::launch_naive_scores(ap, stream), "naive score launch")) != TS_OK) return st;
+      return device_status(ts::launch_score_select(abl_vote_params(L, ws, sc, seq_lens, b, k, sel_idx, sel_count),
+                                                   stream), "top-k launch");
+    }
+    case ts::kAblHardVote: {
+      if ((st = device_status(ts::launch_head_scores(ap, stream), "head score launch")) != TS_OK) return st;
+      const ts::VoteParams hp = abl_vote_params(L, ws, ap.head_scores, ap.seg_lens, b * H, k, ap.head_sel,
+                                                ap.head_cnt);
+      if ((st = device_status(ts::launch_score_select(hp, stream), "per-head top-k launch")) != TS_OK) return st;
+      if ((st = device_status(ts::launch_count_votes(ap, stream), "vote count launch")) != TS_OK) return st;
+      return device_status(ts::launch_score_select(abl_vote_params(L, ws, sc, seq_lens, b, k, sel_idx, sel_count),
+                                                   stream), "top-k launch");
+    }
+    default: {  // block
+      ts::VoteParams vp = soft_votes(at<float>(ws, L.vote));
+      if ((st = device_status(ts::launch_vote_only(vp, stream), "vote launch")) != TS_OK) return st;
+      if ((st = device_status(ts::launch_block_scores(ap, stream), "block score launch")) != TS_OK) return st;
+      const ts::VoteParams bp = abl_vote_params(L, ws, sc, ap.seg_lens, b, L.stride, ap.head_sel, ap.head_cnt);
+      if ((st = device_status(ts::launch_score_select(bp, stream), "block top-k launch")) != TS_OK) return st;
+      return device_status(ts::launch_expand_blocks(ap, stream), "block expand launch");
+    }
+  }
+}
 
 size_t tokenselect_prefill_workspace_size(const ts_shape* shape, const ts_select* sel,
                                           int32_t max_chunk) {

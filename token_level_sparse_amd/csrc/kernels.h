@@ -55,6 +55,9 @@ struct VoteParams {
 // are at most H <= 256, so a request's total stays below 2^48 + N; integer sums are
 // exact and independent of the order of the atomics.
 constexpr int kMassBits = 40;
+__device__ __forceinline__ unsigned long long vote_mass(float lv) {
+  return (unsigned long long)rint(exp2((double)lv + (double)kMassBits));
+}
 
 struct AttnParams {
   const void* q;
@@ -132,6 +135,33 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t s);
 hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 hipError_t launch_cache_check(const CacheParams& p, hipStream_t s);
+// Soft vote only (log2 votes into p.vote and the digit-0 histogram).
+hipError_t launch_vote_only(const VoteParams& p, hipStream_t s);
+// Radix TopK over any fp32 score array p.vote (segments p.seq_lens): histogram + phases.
+hipError_t launch_score_select(const VoteParams& p, hipStream_t s);
+
+// Selection-function ablations over the decode logits.
+enum AblationFn { kAblSoftVote = 0, kAblNaive = 1, kAblHardVote = 2, kAblBlock = 3 };
+struct AblationParams {
+  const float* logits;        // decode layout [H_kv][N_r][G] per request
+  const int32_t* seq_lens;    // [b]
+  int32_t* seg_lens;          // [b * H] (hard vote) or [b] (block) segment lengths
+  float* score;               // the per-position (or per-block) score the final TopK runs on
+  float* head_scores;         // hard vote: [b][H][N_r] logits, one segment per (request, head)
+  int32_t* head_sel;          // hard vote: [b * H][top_k] per-head TopK; block: [b][top_k] blocks
+  int32_t* head_cnt;          // [b * H]
+  int head_stride;            // int32 entries per head_sel row
+  const float* vote;          // block: log2 votes [sum N_r]
+  int32_t* sel_idx;           // [b][top_k]
+  int32_t* sel_count;         // [b]
+  int H, Hkv, b, top_k, block;
+};
+hipError_t launch_naive_scores(const AblationParams& p, hipStream_t s);
+hipError_t launch_head_scores(const AblationParams& p, hipStream_t s);
+hipError_t launch_count_votes(const AblationParams& p, hipStream_t s);
+hipError_t launch_block_scores(const AblationParams& p, hipStream_t s);
+hipError_t launch_expand_blocks(const AblationParams& p, hipStream_t s);
+
 hipError_t launch_chunk_mean(const ChunkParams& p, hipStream_t s);
 hipError_t launch_chunk_attn(const ChunkParams& p, hipStream_t s);
 

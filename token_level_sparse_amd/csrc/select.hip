@@ -67,10 +67,7 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float(u);
 }
 
-// Integer mass of a log2 vote: rint(2^(lv + kMassBits)).
-__device__ __forceinline__ u64 vote_mass(float lv) {
-  return (u64)rint(exp2((double)lv + (double)kMassBits));
-}
+
 
 struct Tables {
   int64_t tok[kMaxBatch + 1];
@@ -569,6 +566,41 @@ __global__ __launch_bounds__(kThreads) void select_phase_kernel(VoteParams p) {
   if (kPhase == 4) write_phase<kTopP>(p, sh);
 }
 
+// Digit-0 histogram of any score array (the selection-function ablations run the
+// TopK phases on scores other than the soft vote): same tiles as the vote kernel.
+__global__ __launch_bounds__(kThreads) void hist0_kernel(VoteParams p) {
+  __shared__ Tables tb;
+  __shared__ uint32_t s_hist[kHistBins];
+  build_tables(tb, p);
+  const int total = tb.tile[p.b];
+  int cur_r = -1;
+  auto flush = [&](int r) {
+    __syncthreads();
+    uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads)
+      if (s_hist[i]) atomicAdd(&gh[i], s_hist[i]);
+  };
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int r = find_segment(tb.tile, p.b, tile);
+    const int t = tile - tb.tile[r];
+    const int N = p.seq_lens[r];
+    if (r != cur_r) {
+      if (cur_r >= 0) flush(cur_r);
+      __syncthreads();
+      for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_hist[i] = 0;
+      __syncthreads();
+      cur_r = r;
+    }
+    const int i0 = t * kVoteTile + threadIdx.x;
+    uint32_t key[kPerThread];
+    load_keys(p.vote + tb.tok[r], i0, N, key);
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      if (i0 + e * kThreads < N) atomicAdd(&s_hist[key[e] >> (32 - kDigitBits0)], 1u);
+  }
+  if (cur_r >= 0) flush(cur_r);
+}
+
 __global__ void zero_u32(uint32_t* x, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     x[i] = 0u;
@@ -608,6 +640,36 @@ hipError_t launch_vote_topk_t(const VoteParams& p, hipStream_t s, bool zero_hist
 
 hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist) {
   return p.topp ? launch_vote_topk_t<true>(p, s, zero_hist) : launch_vote_topk_t<false>(p, s, zero_hist);
+}
+
+hipError_t launch_vote_only(const VoteParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.b * 3 * kHistBins;
+  hipLaunchKernelGGL(zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.hist, n);
+  const dim3 vgrid(std::min(p.grid, kVoteMaxGrid)), block(kThreads);
+  switch (p.G) {
+    case 1: hipLaunchKernelGGL((vote_kernel<1, false>), vgrid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((vote_kernel<2, false>), vgrid, block, 0, s, p); break;
+    case 3: hipLaunchKernelGGL((vote_kernel<3, false>), vgrid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((vote_kernel<4, false>), vgrid, block, 0, s, p); break;
+    case 5: hipLaunchKernelGGL((vote_kernel<5, false>), vgrid, block, 0, s, p); break;
+    case 6: hipLaunchKernelGGL((vote_kernel<6, false>), vgrid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL((vote_kernel<7, false>), vgrid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((vote_kernel<8, false>), vgrid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_select(const VoteParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.b * 3 * kHistBins;
+  hipLaunchKernelGGL(zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.hist, n);
+  const dim3 grid(p.grid), block(kThreads);
+  hipLaunchKernelGGL(hist0_kernel, dim3(std::min(p.grid, kVoteMaxGrid)), block, 0, s, p);
+  hipLaunchKernelGGL((select_phase_kernel<1, false>), dim3(std::min(p.grid, kRefineMaxGrid)), block, 0, s, p);
+  hipLaunchKernelGGL((select_phase_kernel<2, false>), grid, block, 0, s, p);
+  hipLaunchKernelGGL((select_phase_kernel<3, false>), grid, block, 0, s, p);
+  hipLaunchKernelGGL((select_phase_kernel<4, false>), grid, block, 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace ts
