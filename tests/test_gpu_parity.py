@@ -173,3 +173,27 @@ def test_attention_given_oracle_selection():
     po = gh.run_path(batch, geo, sel_override=(sel_idx, sel_count))
     ref = ora.sparse_attention(q, K, V, ora.union_local(T, 6000, geo.n_local), geo.attn_scale)
     assert np.max(np.abs(po.out[0] - ref)) <= 2e-2
+
+
+# ------------------------------------------------------------------ head groupings and batch limits
+@pytest.mark.parametrize("H,Hkv,dtype", [(8, 8, "bf16"), (16, 8, "f32"), (12, 4, "bf16"), (40, 8, "bf16"),
+                                         (48, 8, "f32"), (64, 8, "bf16")])
+def test_every_group_size(H, Hkv, dtype):
+    # G = 1, 2, 3, 5, 6, 8 (4 and 7 are covered above): every score, vote and
+    # attention instantiation
+    geo = wl.workload("llama3-8b-128k", num_q_heads=H, num_kv_heads=Hkv, dtype=dtype, seq_len=3000,
+                      top_k=96, n_local=40, n_planted=8, seed=7100 + H)
+    gh.log(f"[group {H // Hkv}] H={H} H_kv={Hkv} {dtype}")
+    _check_all(wl.make_batch(geo, device=DEV), geo)
+
+
+def test_max_batch_of_1024_requests():
+    # the LDS prefix tables of every kernel hold up to 1024 requests
+    geo = wl.workload("llama3-8b-ragged16", batch=1024, min_len=40, max_len=400, top_k=24, n_local=8,
+                      n_planted=4, seed=7300)
+    gh.log("[batch 1024] N_r in [40, 400]")
+    batch = wl.make_batch(geo, device=DEV)
+    po = gh.run_path(batch, geo)
+    rng = np.random.default_rng(0)
+    for r in sorted(set(rng.integers(0, 1024, 12).tolist()) | {0, 1023}):
+        gh.check_request(po, r, batch.requests[r], geo)
