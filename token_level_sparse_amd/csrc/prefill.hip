@@ -81,21 +81,23 @@ __device__ ChunkGeom chunk_geom(const ChunkParams& p, int r, bool with_sel) {
 }
 
 // ---------------------------------------------------------------- mean query
-// One workgroup per (request, head): qbar = (sum_j q_j) / c with the sum in fp64
-// (exact for bf16 queries of ordinary range), rounded once to fp32. Thread t owns
-// dims 8 (t % 16) + [0, 8) of rows j = t / 16 (mod 16): 16-byte loads, 16 rows in
-// flight per pass, then an LDS sum over the 16 row groups.
+// One workgroup of 1024 threads per (request, head): qbar = (sum_j q_j) / c with the
+// sum in fp64 (exact for bf16 queries of ordinary range), rounded once to fp32.
+// Thread t owns dims 8 (t % 16) + [0, 8) of rows j = t / 16 (mod 64): 16-byte loads,
+// 64 rows in flight per pass, then an LDS sum over the 64 row groups.
+constexpr int kMeanThreads = 1024;
+constexpr int kMeanGroups = kMeanThreads / 16;
 template <bool kBf16>
-__global__ __launch_bounds__(256) void chunk_mean_kernel(ChunkParams p) {
-  __shared__ double s_acc[16][kHeadDim];
+__global__ __launch_bounds__(kMeanThreads) void chunk_mean_kernel(ChunkParams p) {
+  __shared__ double s_acc[kMeanGroups][kHeadDim / 2];     // two passes of 64 dims
   const int r = blockIdx.x / p.H, h = blockIdx.x - (blockIdx.x / p.H) * p.H;
   const ChunkGeom gm = chunk_geom(p, r, false);
   const int dc = threadIdx.x & 15, rg = threadIdx.x >> 4;
   double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
   const int64_t row_stride = (int64_t)p.H * kHeadDim;
   const int64_t base = ((int64_t)r * p.max_chunk * p.H + h) * kHeadDim + 8 * dc;
-#pragma unroll 4
-  for (int j = rg; j < gm.c; j += 16) {
+#pragma unroll 2
+  for (int j = rg; j < gm.c; j += kMeanGroups) {
     if (kBf16) {
       const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + base + j * row_stride);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -112,14 +114,20 @@ __global__ __launch_bounds__(256) void chunk_mean_kernel(ChunkParams p) {
       acc[4] += (double)x1.x; acc[5] += (double)x1.y; acc[6] += (double)x1.z; acc[7] += (double)x1.w;
     }
   }
+  // dims [0, 64) then [64, 128): threads with dc < 8, then dc >= 8, publish
+  for (int half = 0; half < 2; ++half) {
+    if ((dc >> 3) == half) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s_acc[rg][8 * dc + e] = acc[e];
-  __syncthreads();
-  if (threadIdx.x < kHeadDim) {
-    double t = 0.0;
-#pragma unroll
-    for (int g = 0; g < 16; ++g) t += s_acc[g][threadIdx.x];
-    p.qbar[((int64_t)r * p.H + h) * kHeadDim + threadIdx.x] = (float)(t / (double)max(gm.c, 1));
+      for (int e = 0; e < 8; ++e) s_acc[rg][8 * (dc & 7) + e] = acc[e];
+    }
+    __syncthreads();
+    if (threadIdx.x < kHeadDim / 2) {
+      double t = 0.0;
+      for (int g = 0; g < kMeanGroups; ++g) t += s_acc[g][threadIdx.x];
+      p.qbar[((int64_t)r * p.H + h) * kHeadDim + 64 * half + threadIdx.x] =
+          (float)(t / (double)max(gm.c, 1));
+    }
+    __syncthreads();
   }
   if (h == 0 && threadIdx.x == 0) p.past_lens[r] = gm.P;
 }
@@ -487,7 +495,7 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkParams p) {
 }  // namespace
 
 hipError_t launch_chunk_mean(const ChunkParams& p, hipStream_t s) {
-  const dim3 grid(p.b * p.H), block(256);
+  const dim3 grid(p.b * p.H), block(kMeanThreads);
   if (p.bf16) hipLaunchKernelGGL(chunk_mean_kernel<true>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(chunk_mean_kernel<false>, grid, block, 0, s, p);
   return hipGetLastError();
