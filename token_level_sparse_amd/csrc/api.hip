@@ -42,7 +42,7 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // has about kScoreUnitsTarget units; the grid is capped at kScoreMaxGrid
 // workgroups of 4 waves that loop over the units.
 #ifndef TS_SCORE_UNITS_TARGET
-#define TS_SCORE_UNITS_TARGET 16384
+#define TS_SCORE_UNITS_TARGET 2048
 #endif
 #ifndef TS_SCORE_MAX_GRID
 #define TS_SCORE_MAX_GRID 2048
