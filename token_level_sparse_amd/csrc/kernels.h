@@ -12,7 +12,10 @@ constexpr int kVoteTile = 1024;
 constexpr int kDigitBits0 = 11, kDigitBits1 = 11, kDigitBits2 = 10;
 constexpr int kHistBins = 1 << 11;
 // Selected tokens per attention wavefront and per attention workgroup (4 waves).
-constexpr int kAttnSplit = 32;
+#ifndef TS_ATTN_SPLIT
+#define TS_ATTN_SPLIT 32
+#endif
+constexpr int kAttnSplit = TS_ATTN_SPLIT;
 constexpr int kAttnTile = 4 * kAttnSplit;
 
 struct ScoreParams {
@@ -93,7 +96,7 @@ struct CacheParams {
 // runs over a gathered key list: the TopK positions below the window start
 // w0 = max(0, P_r - L) (n_sel of them), then the contiguous range
 // [w0, P_r + c_r); query j sees the first base + j + 1 entries, base = n_sel + P_r - w0.
-constexpr int kChunkRows = 64;        // (query, head) rows per attention workgroup
+constexpr int kChunkRows = 64;        // fewest (query, head) rows per attention workgroup (fp32; bf16 128)
 #ifndef TS_CHUNK_SPLIT_KEYS
 #define TS_CHUNK_SPLIT_KEYS 1024
 #endif

@@ -18,20 +18,22 @@
 // That is a causal attention with a key offset over an index-mapped paged pool, a
 // dense contraction of c*G rows by ~k+L+c keys, so it runs on the matrix cores.
 //
-// gfx950 design. A workgroup owns 64 (query, head) rows of one (request, KV head):
-// row = j * G + head-in-group, so one staged key block serves all G heads of the
-// group. Each of the 4 waves owns 16 rows. Per block of keys:
+// gfx950 design. A workgroup owns 128 (query, head) rows of one (request, KV head)
+// (64 for fp32): row = j * G + head-in-group, so one staged key block serves all G
+// heads of the group. Each of the 4 waves owns 32 rows (16 for fp32), so every K and
+// V fragment a wave reads from LDS feeds 32 rows. Per block of keys:
 //   * the workgroup stages K as [key][d] and V transposed as [d][key] in LDS (the
 //     next block's loads are issued into registers before the current block's
 //     products, so the gather latency overlaps the matrix work);
-//   * S^T = K Q^T on MFMA (A = 16 keys x 32 dims from LDS, B = the wave's queries
-//     held in registers), so a lane ends with 4 keys of one row: row = lane % 16;
-//   * online softmax in base 2 per row (row max across the 4 lane groups);
+//   * S^T = K Q^T on MFMA (A = 32 keys x 16 dims from LDS, B = the wave's queries
+//     held in registers), so a lane ends with 16 keys of one row: row = lane % 32;
+//   * online softmax in base 2 per row (row max across the 2 lane halves);
 //   * O^T += V^T P^T on MFMA: the lane's probabilities are already the B operand
-//     (row = lane % 16, 8 keys), with the key order of the A operand (V^T rows from
-//     LDS) permuted to match, so P never leaves registers.
-// bf16 uses v_mfma_f32_16x16x32_bf16 on 64-key blocks; fp32 uses
-// v_mfma_f32_16x16x4_f32 on 32-key blocks with the same index and mask logic.
+//     (row = lane % 32, 8 keys per step), with the key order of the A operand (V^T
+//     rows from LDS) permuted to match, so P never leaves registers.
+// bf16 uses v_mfma_f32_32x32x16_bf16 on 64-key blocks (accumulators in VGPRs, two
+// waves per SIMD); fp32 uses v_mfma_f32_16x16x4_f32 on 32-key blocks with 16-row
+// waves and the same index and mask logic.
 // Key splits of kChunkSplitKeys list entries give more workgroups; a combine kernel
 // merges the per-split (o, m, l) rows.
 #include <type_traits>
@@ -45,6 +47,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kRescaleSlack = 8.f;
 constexpr int kPartStride = kChunkPartStride;   // o[128], m, l, 2 pad: 16-byte aligned rows
@@ -158,7 +161,7 @@ template <bool kBf16> struct Tile;
 template <> struct Tile<true> {
   static constexpr int kKeys = 64;                 // keys per staged block
   static constexpr int kKStride = kHeadDim + 8;    // bf16 elements per K row in LDS
-  static constexpr int kVStride = 64 + 8;          // bf16 elements per V^T row in LDS
+  static constexpr int kVStride = 64 + 4;          // bf16 elements per V^T row in LDS
   static constexpr int kLds = kKeys * kKStride * 2 + kHeadDim * kVStride * 2;
   uint4 k[4], v[4];                                // staging registers: 4 keys x 8 dims
 };
@@ -168,7 +171,6 @@ template <> struct Tile<false> {
   static constexpr int kLds = 2 * kKeys * kStride * 4;
   float4 k[4], v[4];                               // staging registers: 1 key x 16 dims
 };
-constexpr int kChunkLds = Tile<true>::kLds > Tile<false>::kLds ? Tile<true>::kLds : Tile<false>::kLds;
 
 struct KeyMap {
   const int64_t* off;      // LDS: element offset of the split's key-list entries (this KV head)
@@ -232,40 +234,70 @@ __device__ __forceinline__ void stage_store(const Tile<false>& t, char* lds) {
   }
 }
 
-// Query operand (B of S^T = K Q^T): bf16 lane holds dims 32 ks + 8 a + [0, 8) of its
-// row; fp32 lane holds dims 4 ks + a.
-struct QOpBf16 { bf16x8_t v[4]; };
+// Query operand (B of S^T = K Q^T). fp32 (16x16x4): the lane holds dims 4 ks + a of
+// its row. bf16 (32x32x16): the lane holds dims 16 ks + 8 lg + [0, 8).
 struct QOpF32 { float v[32]; };
+struct QOp32 { bf16x8_t v[8]; };
 
-__device__ __forceinline__ void load_qop(QOpBf16& q, const uint16_t* qrow, bool ok, int a) {
+__device__ __forceinline__ void load_qop32(QOp32& q, const uint16_t* qrow, bool ok, int lg) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < 8; ++ks) {
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (ok) w = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * a);
+    if (ok) w = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * lg);
     q.v[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{w.x, w.y, w.z, w.w});
   }
 }
+
+// bf16 S^T tiles of one staged block on v_mfma_f32_32x32x16_bf16: s[t][j] =
+// <q_row, k_{32 t + 8 (j / 4) + 4 lg + j % 4}> for the lane's row l32.
+__device__ __forceinline__ void qk_block32(const char* lds, const QOp32& q, int l32, int lg,
+                                           f32x16_t (&s)[2]) {
+  const uint16_t* Ks = reinterpret_cast<const uint16_t*>(lds);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x16_t acc = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(
+          Ks + (32 * t + l32) * Tile<true>::kKStride + 16 * ks + 8 * lg);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, q.v[ks], acc, 0, 0, 0);
+    }
+    s[t] = acc;
+  }
+}
+
+// bf16 O^T += V^T P^T: o[dt][j] = O[row][32 dt + 8 (j / 4) + 4 lg + j % 4]. The B operand
+// of the 16-key step (t, hh) is the lane's pv[t][8 hh .. 8 hh + 8) (keys 32 t + 16 hh +
+// 4 lg + [0, 4) and + 8), so the A operand's keys are read in that order from V^T.
+__device__ __forceinline__ void pv_block32(const char* lds, const f32x16_t (&pv)[2], int l32, int lg,
+                                           f32x16_t (&o)[4]) {
+  const uint16_t* Vt = reinterpret_cast<const uint16_t*>(lds) + Tile<true>::kKeys * Tile<true>::kKStride;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int b8 = 8 * hh;
+      // probabilities in [0, 2^8] to bf16 (round to nearest even, two per instruction)
+      const bf16x8_t pb = {(__bf16)pv[t][b8], (__bf16)pv[t][b8 + 1], (__bf16)pv[t][b8 + 2],
+                           (__bf16)pv[t][b8 + 3], (__bf16)pv[t][b8 + 4], (__bf16)pv[t][b8 + 5],
+                           (__bf16)pv[t][b8 + 6], (__bf16)pv[t][b8 + 7]};
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const uint16_t* vr = Vt + (32 * dt + l32) * Tile<true>::kVStride + 32 * t + 16 * hh + 4 * lg;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[dt], 0, 0, 0);
+      }
+    }
+}
+
 __device__ __forceinline__ void load_qop(QOpF32& q, const float* qrow, bool ok, int a) {
 #pragma unroll
   for (int ks = 0; ks < 32; ++ks) q.v[ks] = ok ? qrow[4 * ks + a] : 0.f;
 }
 
-// S^T tiles of one staged block: s[t][i] = <q_row, k_{16 t + 4 a + i}>.
-__device__ __forceinline__ void qk_block(const char* lds, const QOpBf16& q, int l16, int a,
-                                         f32x4_t (&s)[4]) {
-  const uint16_t* Ks = reinterpret_cast<const uint16_t*>(lds);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(
-          Ks + (16 * t + l16) * Tile<true>::kKStride + 32 * ks + 8 * a);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, q.v[ks], acc, 0, 0, 0);
-    }
-    s[t] = acc;
-  }
-}
+// fp32: S^T tiles of one staged block: s[t][i] = <q_row, k_{16 t + 4 a + i}>.
 __device__ __forceinline__ void qk_block(const char* lds, const QOpF32& q, int l16, int a,
                                          f32x4_t (&s)[2]) {
   const float* Ks = reinterpret_cast<const float*>(lds);
@@ -280,27 +312,7 @@ __device__ __forceinline__ void qk_block(const char* lds, const QOpF32& q, int l
   }
 }
 
-// O^T += V^T P^T over one staged block. o[dt][i] = O[row][16 dt + 4 a + i].
-__device__ __forceinline__ void pv_block(const char* lds, const float (&pv)[4][4], int l16, int a,
-                                         f32x4_t (&o)[8]) {
-  const uint16_t* Vt = reinterpret_cast<const uint16_t*>(lds) + Tile<true>::kKeys * Tile<true>::kKStride;
-#pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) {
-    // B operand: keys 32 k2 + 4 a + [0, 4) then 32 k2 + 16 + 4 a + [0, 4)
-    // probabilities in [0, 1] to bf16 (round to nearest even, two per instruction)
-    const bf16x8_t pb = {(__bf16)pv[2 * k2][0], (__bf16)pv[2 * k2][1], (__bf16)pv[2 * k2][2],
-                         (__bf16)pv[2 * k2][3], (__bf16)pv[2 * k2 + 1][0], (__bf16)pv[2 * k2 + 1][1],
-                         (__bf16)pv[2 * k2 + 1][2], (__bf16)pv[2 * k2 + 1][3]};
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint16_t* vr = Vt + (16 * dt + l16) * Tile<true>::kVStride + 32 * k2 + 4 * a;
-      const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[dt], 0, 0, 0);
-    }
-  }
-}
+// fp32: O^T += V^T P^T over one staged block. o[dt][i] = O[row][16 dt + 4 a + i].
 __device__ __forceinline__ void pv_block(const char* lds, const float (&pv)[2][4], int l16, int a,
                                          f32x4_t (&o)[8]) {
   const float* Vs = reinterpret_cast<const float*>(lds) + Tile<false>::kKeys * Tile<false>::kStride;
@@ -314,129 +326,230 @@ __device__ __forceinline__ void pv_block(const char* lds, const float (&pv)[2][4
             Vs[(16 * t + 4 * a + i) * Tile<false>::kStride + 16 * dt + l16], pv[t][i], o[dt], 0, 0, 0);
 }
 
-template <bool kBf16>
-__global__ __launch_bounds__(256) void chunk_attn_kernel(ChunkParams p) {
-  using T = typename std::conditional<kBf16, uint16_t, float>::type;
-  using QOp = typename std::conditional<kBf16, QOpBf16, QOpF32>::type;
-  constexpr int KB = Tile<kBf16>::kKeys;
-  constexpr int NT = KB / 16;
-  __shared__ __align__(16) char s_lds[kChunkLds];
-  __shared__ int64_t s_keys[kChunkSplitKeys];
-  __shared__ int s_geom[6];
+// Work of one attention workgroup: a unit (request, KV head, split) and a tile of
+// rows_per_wg (query, head) rows. The split's key-list entries are expanded into
+// element offsets of this KV head in LDS. Returns false (the same for every thread)
+// when the workgroup has nothing to do.
+struct UnitWork {
+  int r, g, split, G, rows, row0, base, x_begin, x_end;
+  KeyMap km;
+};
 
-  const int H = p.H, Hkv = p.Hkv, G = H / Hkv;
-  const int rt = (p.max_chunk * G + kChunkRows - 1) / kChunkRows;
+__device__ bool chunk_unit(const ChunkParams& p, int rows_per_wg, int* s_geom, int64_t* s_keys,
+                           UnitWork& w) {
+  const int H = p.H, Hkv = p.Hkv;
+  w.G = H / Hkv;
+  const int rt = (p.max_chunk * w.G + rows_per_wg - 1) / rows_per_wg;
   // XCD-aware order: workgroup i runs on XCD i % 8. All row tiles of one unit
   // (request, KV head, split) go to the same XCD, one after another, so the unit's
   // staged K/V rows come from that XCD's L2 after the first tile.
   const int units = p.b * Hkv * p.splits;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int u = (slot / rt) * kXcds + xcd;
-  if (u >= units) return;
+  if (u >= units) return false;
   const int tile = slot % rt;
-  const int split = u % p.splits;
-  const int g = (u / p.splits) % Hkv;
-  const int r = u / (p.splits * Hkv);
+  w.split = u % p.splits;
+  w.g = (u / p.splits) % Hkv;
+  w.r = u / (p.splits * Hkv);
   if (threadIdx.x == 0) {
-    const ChunkGeom gm = chunk_geom(p, r, true);
-    s_geom[0] = gm.c; s_geom[1] = gm.P; s_geom[2] = gm.w0;
-    s_geom[3] = gm.n_sel; s_geom[4] = gm.base; s_geom[5] = gm.N;
+    const ChunkGeom gm = chunk_geom(p, w.r, true);
+    s_geom[0] = gm.c; s_geom[1] = gm.base;
   }
   __syncthreads();
-  const int c = s_geom[0], base = s_geom[4];
-  const int rows = c * G;
-  const int row0 = tile * kChunkRows;
-  if (row0 >= rows) return;                                   // uniform over the workgroup
-  const int jmax = (min(row0 + kChunkRows, rows) - 1) / G;
-  const int n_vis = base + jmax + 1;                          // entries the last query sees
-  const int x_begin = split * kChunkSplitKeys;
-  if (x_begin >= n_vis) return;                               // uniform
-  const int x_end = min(x_begin + kChunkSplitKeys, n_vis);
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int l16 = lane & 15, a = lane >> 4;
-  const int rho = row0 + 16 * wave + l16;
-  const bool row_ok = rho < rows;
-  const int j = row_ok ? rho / G : 0;
-  const int h = g * G + (row_ok ? rho - (rho / G) * G : 0);
-  const int lim = row_ok ? base + j : -1;                     // last visible key-list entry
-  // smallest limit over the wave's rows (rows past the chunk count as fully visible)
-  const int wave_j0 = min(row0 + 16 * wave, rows - 1) / G;
-  const int wave_lim = base + wave_j0;
-
-  const T* qrow = static_cast<const T*>(p.q) + (((int64_t)r * p.max_chunk + j) * H + h) * kHeadDim;
-  QOp q;
-  load_qop(q, qrow, row_ok, a);
-
-  const int32_t* kt = p.keytab + (int64_t)r * p.max_keys;
-  for (int x = x_begin + (int)threadIdx.x; x < x_end; x += 256) {
+  const int c = s_geom[0];
+  w.base = s_geom[1];
+  w.rows = c * w.G;
+  w.row0 = tile * rows_per_wg;
+  if (w.row0 >= w.rows) return false;
+  const int jmax = (min(w.row0 + rows_per_wg, w.rows) - 1) / w.G;
+  const int n_vis = w.base + jmax + 1;                        // entries the last query sees
+  w.x_begin = w.split * kChunkSplitKeys;
+  if (w.x_begin >= n_vis) return false;
+  w.x_end = min(w.x_begin + kChunkSplitKeys, n_vis);
+  const int32_t* kt = p.keytab + (int64_t)w.r * p.max_keys;
+  for (int x = w.x_begin + (int)threadIdx.x; x < w.x_end; x += 256) {
     const int v = kt[x];                                       // page * 16 + slot
-    s_keys[x - x_begin] = (((int64_t)(v >> 4) * Hkv + g) * kPage + (v & (kPage - 1))) * kHeadDim;
+    s_keys[x - w.x_begin] = (((int64_t)(v >> 4) * Hkv + w.g) * kPage + (v & (kPage - 1))) * kHeadDim;
   }
   __syncthreads();
-  KeyMap km;
-  km.off = s_keys; km.x_begin = x_begin; km.x_end = x_end;
-  const T* kp = static_cast<const T*>(p.k_pool);
-  const T* vp = static_cast<const T*>(p.v_pool);
+  w.km.off = s_keys; w.km.x_begin = w.x_begin; w.km.x_end = w.x_end;
+  return true;
+}
 
+// Online softmax step shared by both kernels. Rescale only when some row's block
+// maximum exceeds its running maximum by more than kRescaleSlack (base 2): o and l stay
+// relative to the same m_run, so the result is unchanged, and probabilities stay below
+// 2^kRescaleSlack. pv holds scaled scores (-inf where masked) and returns probabilities.
+template <int kN, typename Rescale>
+__device__ __forceinline__ void softmax_step(float (&pv)[kN], float mloc, float& m_run, float& l_run,
+                                             Rescale rescale) {
+  if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack)) {
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+    l_run *= alpha;
+    m_run = m_new;
+    rescale(alpha);
+  }
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    pv[i] = (pv[i] == kNegInf) ? 0.f : fast_exp2(pv[i] - m_run);
+    psum += pv[i];
+  }
+  l_run += psum;
+}
+
+// bf16: 4 waves x 32 rows, v_mfma_f32_32x32x16_bf16. Lane l holds row l % 32 (lg = l / 32
+// picks which keys and dims of that row it carries).
+constexpr int kRows32 = 128;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void chunk_attn_bf16_kernel(ChunkParams p) {
+  constexpr int KB = Tile<true>::kKeys;
+  __shared__ __align__(16) char s_lds[Tile<true>::kLds];
+  __shared__ int64_t s_keys[kChunkSplitKeys];
+  __shared__ int s_geom[2];
+  UnitWork w;
+  if (!chunk_unit(p, kRows32, s_geom, s_keys, w)) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l32 = lane & 31, lg = lane >> 5;
+  const int rho = w.row0 + 32 * wave + l32;
+  const bool row_ok = rho < w.rows;
+  const int j = row_ok ? rho / w.G : 0;
+  const int h = w.g * w.G + (row_ok ? rho - (rho / w.G) * w.G : 0);
+  const int lim = row_ok ? w.base + j : -1;                   // last visible key-list entry
+  const int wave_lim = w.base + min(w.row0 + 32 * wave, w.rows - 1) / w.G;
+
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                         (((int64_t)w.r * p.max_chunk + j) * p.H + h) * kHeadDim;
+  QOp32 q;
+  load_qop32(q, qrow, row_ok, lg);
+  const uint16_t* kp = static_cast<const uint16_t*>(p.k_pool);
+  const uint16_t* vp = static_cast<const uint16_t*>(p.v_pool);
   const float sl2 = p.attn_scale * kLog2e;
   float m_run = kNegInf, l_run = 0.f;
-  f32x4_t o[8];
+  f32x16_t o[4];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
 
-  Tile<kBf16> st;
-  stage_load(st, kp, vp, km, x_begin);
-  for (int x0 = x_begin; x0 < x_end; x0 += KB) {
+  Tile<true> st;
+  stage_load(st, kp, vp, w.km, w.x_begin);
+  for (int x0 = w.x_begin; x0 < w.x_end; x0 += KB) {
     __syncthreads();                      // the previous block's reads of LDS are done
     stage_store(st, s_lds);
     __syncthreads();
-    if (x0 + KB < x_end) stage_load(st, kp, vp, km, x0 + KB);   // overlaps the products below
+    if (x0 + KB < w.x_end) stage_load(st, kp, vp, w.km, x0 + KB);   // overlaps the products
 
-    f32x4_t s[NT];
-    qk_block(s_lds, q, l16, a, s);
-    float pv[NT][4];
+    f32x16_t s[2];                        // scores, then probabilities, in place
+    qk_block32(s_lds, q, l32, lg, s);
     float mloc = kNegInf;
-    if (x0 + KB <= x_end && x0 + KB - 1 <= wave_lim) {   // wave-uniform: no key of a valid row masked
+    if (x0 + KB <= w.x_end && x0 + KB - 1 <= wave_lim) {     // wave-uniform: nothing masked
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[t][i] = s[t][i] * sl2;
-          mloc = fmaxf(mloc, pv[t][i]);
-        }
+        for (int i = 0; i < 16; ++i) { s[t][i] *= sl2; mloc = fmaxf(mloc, s[t][i]); }
     } else {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int x = x0 + 16 * t + 4 * a + i;
-          pv[t][i] = (x < x_end && x <= lim) ? s[t][i] * sl2 : kNegInf;
-          mloc = fmaxf(mloc, pv[t][i]);
+        for (int i = 0; i < 16; ++i) {
+          const int x = x0 + 32 * t + 8 * (i >> 2) + 4 * lg + (i & 3);
+          s[t][i] = (x < w.x_end && x <= lim) ? s[t][i] * sl2 : kNegInf;
+          mloc = fmaxf(mloc, s[t][i]);
         }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    // Rescale only when some row's block maximum exceeds its running maximum by more
-    // than kRescaleSlack (base 2): o and l stay relative to the same m_run, so the
-    // result is unchanged, and probabilities stay below 2^kRescaleSlack.
     if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
     float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[t][i] = (s[t][i] == kNegInf) ? 0.f : fast_exp2(s[t][i] - m_run);
+        psum += s[t][i];
+      }
+    l_run += psum;
+    pv_block32(s_lds, s, l32, lg, o);
+  }
+
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  if (row_ok) {
+    float* dst = p.partials +
+                 ((((int64_t)w.r * p.max_chunk + j) * p.H + h) * p.splits + w.split) * kPartStride;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * qd + 4 * lg) =
+            make_float4(o[dt][4 * qd], o[dt][4 * qd + 1], o[dt][4 * qd + 2], o[dt][4 * qd + 3]);
+    if (lg == 0) { dst[kHeadDim] = m_run; dst[kHeadDim + 1] = lt; }
+  }
+}
+
+// fp32: 4 waves x 16 rows, v_mfma_f32_16x16x4_f32, 32-key blocks. Lane l holds row
+// l % 16 (a = l / 16 picks which keys and dims of that row it carries).
+constexpr int kRows16 = 64;
+__global__ __launch_bounds__(256) void chunk_attn_f32_kernel(ChunkParams p) {
+  constexpr int KB = Tile<false>::kKeys;
+  constexpr int NT = KB / 16;
+  __shared__ __align__(16) char s_lds[Tile<false>::kLds];
+  __shared__ int64_t s_keys[kChunkSplitKeys];
+  __shared__ int s_geom[2];
+  UnitWork w;
+  if (!chunk_unit(p, kRows16, s_geom, s_keys, w)) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, a = lane >> 4;
+  const int rho = w.row0 + 16 * wave + l16;
+  const bool row_ok = rho < w.rows;
+  const int j = row_ok ? rho / w.G : 0;
+  const int h = w.g * w.G + (row_ok ? rho - (rho / w.G) * w.G : 0);
+  const int lim = row_ok ? w.base + j : -1;
+  const int wave_lim = w.base + min(w.row0 + 16 * wave, w.rows - 1) / w.G;
+
+  const float* qrow = static_cast<const float*>(p.q) + (((int64_t)w.r * p.max_chunk + j) * p.H + h) * kHeadDim;
+  QOpF32 q;
+  load_qop(q, qrow, row_ok, a);
+  const float* kp = static_cast<const float*>(p.k_pool);
+  const float* vp = static_cast<const float*>(p.v_pool);
+  const float sl2 = p.attn_scale * kLog2e;
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4_t o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  Tile<false> st;
+  stage_load(st, kp, vp, w.km, w.x_begin);
+  for (int x0 = w.x_begin; x0 < w.x_end; x0 += KB) {
+    __syncthreads();
+    stage_store(st, s_lds);
+    __syncthreads();
+    if (x0 + KB < w.x_end) stage_load(st, kp, vp, w.km, x0 + KB);
+
+    f32x4_t s[NT];
+    qk_block(s_lds, q, l16, a, s);
+    float pv[NT][4];
+    float mloc = kNegInf;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pv[t][i] = (pv[t][i] == kNegInf) ? 0.f : fast_exp2(pv[t][i] - m_run);
-        psum += pv[t][i];
+        const int x = x0 + 16 * t + 4 * a + i;
+        const bool vis = (x0 + KB <= w.x_end && x0 + KB - 1 <= wave_lim) || (x < w.x_end && x <= lim);
+        pv[t][i] = vis ? s[t][i] * sl2 : kNegInf;
+        mloc = fmaxf(mloc, pv[t][i]);
       }
-    l_run += psum;
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    softmax_step(reinterpret_cast<float(&)[NT * 4]>(pv), mloc, m_run, l_run, [&](float alpha) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    });
     pv_block(s_lds, pv, l16, a, o);
   }
 
@@ -444,7 +557,7 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(ChunkParams p) {
   lt += __shfl_xor(lt, 32);
   if (row_ok) {
     float* dst = p.partials +
-                 ((((int64_t)r * p.max_chunk + j) * H + h) * p.splits + split) * kPartStride;
+                 ((((int64_t)w.r * p.max_chunk + j) * p.H + h) * p.splits + w.split) * kPartStride;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
       *reinterpret_cast<float4*>(dst + 16 * dt + 4 * a) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
@@ -503,13 +616,14 @@ hipError_t launch_chunk_mean(const ChunkParams& p, hipStream_t s) {
 
 hipError_t launch_chunk_attn(const ChunkParams& p, hipStream_t s) {
   const int G = p.H / p.Hkv;
-  const int rt = (p.max_chunk * G + kChunkRows - 1) / kChunkRows;
+  const int rows_per_wg = p.bf16 ? kRows32 : kRows16;
+  const int rt = (p.max_chunk * G + rows_per_wg - 1) / rows_per_wg;
   const dim3 block(256);
   hipLaunchKernelGGL(chunk_keys_kernel, dim3(p.b * ((p.max_keys + 255) / 256)), block, 0, s, p);
   const int units = p.b * p.Hkv * p.splits;
   const dim3 grid(kXcds * rt * ((units + kXcds - 1) / kXcds));
-  if (p.bf16) hipLaunchKernelGGL(chunk_attn_kernel<true>, grid, block, 0, s, p);
-  else hipLaunchKernelGGL(chunk_attn_kernel<false>, grid, block, 0, s, p);
+  if (p.bf16) hipLaunchKernelGGL(chunk_attn_bf16_kernel, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(chunk_attn_f32_kernel, grid, block, 0, s, p);
   const dim3 cgrid((unsigned)(((int64_t)p.b * p.max_chunk * p.H + 7) / 8));
   if (p.bf16) hipLaunchKernelGGL(chunk_combine_kernel<true>, cgrid, block, 0, s, p);
   else hipLaunchKernelGGL(chunk_combine_kernel<false>, cgrid, block, 0, s, p);
