@@ -273,11 +273,12 @@ def make_batch(geo: Geometry, device="cpu", layer: int = 0, permute: bool = True
                seq_len: Optional[int] = None, pools: Optional[tuple] = None) -> PagedBatch:
     """Draw a whole workload (one layer) and page it.
 
-    Single-request workloads use ``seq_len`` (default the workload's N). The
-    ragged workload draws its lengths first, then each request in order.
+    Workloads with a length range (min_len) draw every request's length first,
+    then each request in order; the others use ``seq_len`` (default the
+    workload's N) for every request.
     """
     gen = _gen(geo.seed + layer, device)
-    if geo.batch > 1 and geo.min_len:
+    if geo.min_len and not seq_len:
         lens = request_lengths(gen, geo, device)
     else:
         lens = [seq_len or geo.seq_len] * geo.batch
@@ -337,7 +338,7 @@ def make_chunk_batch(geo: Geometry, device="cpu", layer: int = 0, permute: bool 
     gen = _gen(geo.seed + layer, device)
     c = geo.chunk
     assert c >= 1
-    if geo.batch > 1 and geo.min_len:
+    if geo.min_len and not seq_len:
         lens = request_lengths(gen, geo, device)
     else:
         lens = [seq_len or geo.seq_len] * geo.batch
