@@ -40,23 +40,33 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+SCORE_SOURCES = ("score.hip", "cache.h", "common.h", "kernels.h")
+
+
+def score_source_digest() -> str:
+    """sha256 over the score kernel's source files, in SCORE_SOURCES order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in SCORE_SOURCES:
+        with open(os.path.join(ROOT, "token_level_sparse_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per scoring launch from the committed counter summary, or None.
 
-    The summary records the sha256 of the score kernel source it was measured on;
-    if the source has changed since, the figure no longer describes the kernel.
+    The summary records the sha256 of the score kernel's sources it was measured on;
+    if they have changed since, the figure no longer describes the kernel.
     """
-    import hashlib
     path = os.path.join(ROOT, "profiles", "score_kernel_traffic_llama3-8b-1m.md")
-    src = os.path.join(ROOT, "token_level_sparse_amd", "csrc", "score.hip")
     try:
         fields = {}
         for line in open(path):
             if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "score_source_sha256"):
                 k, v = line.split(":", 1)
                 fields[k] = v.strip()
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if fields.get("score_source_sha256") != digest:
+        if fields.get("score_source_sha256") != score_source_digest():
             return None
         return float(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -428,7 +438,7 @@ def time_prefill(geo, n_layers, steps, warmup, dev):
            "prefill_tokens_per_s": c * 1e3 / ms, "select_ms": select_ms,
            "select_gbps": sel_bytes / (select_ms * 1e-3) / 1e9, "attn_ms": attn_ms,
            "attn_flops": flops, "attn_tflops": attn_tflops,
-           "attn_mfma_frac": attn_tflops * 1e3 / PEAK_BF16_TFLOPS}
+           "attn_mfma_frac": attn_tflops / PEAK_BF16_TFLOPS}
     del cbs, ws, KC, VC
     torch.cuda.empty_cache()
     return res

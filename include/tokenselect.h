@@ -153,7 +153,8 @@ ts_status tokenselect_vote_topk(const ts_shape* shape, const ts_select* sel,
 /* Step 5. Attention of every query head over S_r = TopK_r united with
    [max(0, N_r - n_local), N_r), without duplicates: out[r][h] = sum_{i in S_r}
    softmax_i(attn_scale * <q_h, K_{h/G}[i]>) V_{h/G}[i] (deepnotes selective
-   sparse attention formalisation). sel_idx rows must be ascending. */
+   sparse attention formalisation). sel_idx rows must be ascending. A request with
+   N_r = 0 has an empty S_r and gets out[r] = 0. */
 ts_status tokenselect_sparse_attn(const ts_shape* shape, const ts_select* sel,
                                   const void* q, const void* k_pool, const void* v_pool,
                                   const int32_t* block_table, const int32_t* seq_lens,

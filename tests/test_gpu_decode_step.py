@@ -168,3 +168,69 @@ def test_ragged_batch_mixed_hits():
                 assert np.array_equal(Ts[t][r], Ts[t - 1][r])
             gh.check_attention(outs[t][r], q_all[t], K[:, :N], V[:, :N], Ts[t][r], N, geo.n_local,
                                geo.attn_scale, False)
+
+
+def test_requests_sharing_score_blocks_and_an_empty_request():
+    """H_kv = 3 with one-chunk requests: the score kernel's 4-unit blocks straddle
+    requests, so a workgroup decides several requests' cache tests in one block.
+    Request 1 has N = 0 (no tokens): it still gets a decision, an empty TopK and a
+    zero output. Requests 0, 1 and 4 repeat their query (hits after step 0); the
+    others draw a new one every step."""
+    geo = wl.workload("llama3-8b-128k", num_q_heads=6, num_kv_heads=3, top_k=40, n_local=8,
+                      n_planted=2)
+    gh.log("[decode H_kv=3 shared score blocks, empty request]")
+    steps, lens0 = 4, [100, 50, 37, 2000, 16, 1, 700]
+    gen = torch.Generator(device=DEV).manual_seed(12)
+    reqs = [wl.make_request(gen, geo, n, DEV, extra_tokens=steps - 1) for n in lens0]
+    batch = wl.page_requests(reqs, geo, gen, DEV)
+    H, d, b = geo.num_q_heads, geo.head_dim, len(reqs)
+    qs = torch.randn(steps, b, H, d, generator=gen, device=DEV).to(torch.bfloat16)
+    for r in (0, 1, 4):
+        qs[:, r] = qs[0, r]
+    lens_all = np.array([[0 if r == 1 else lens0[r] + t for r in range(b)] for t in range(steps)])
+    shape = ts.make_shape(H, geo.num_kv_heads, b, batch.block_table.shape[1],
+                          sum(lens0) + b * (steps - 1), geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, 0.9)
+    ws = ts.alloc_workspace(shape, sel, DEV)
+    cache = ts.CacheState.allocate(b, H, d, geo.top_k, geo.torch_dtype, DEV)
+    hit = torch.full((b,), -7, dtype=torch.int32, device=DEV)
+    out = torch.full((b, H, d), float("nan"), dtype=geo.torch_dtype, device=DEV)
+    hits, Ts, outs = [], [], []
+    for t in range(steps):
+        lens = torch.from_numpy(lens_all[t].astype(np.int32)).to(DEV)
+        ts.decode_step(shape, sel, qs[t].contiguous(), batch.k_pool, batch.v_pool,
+                       batch.block_table, lens, cache, hit, out, ws)
+        torch.cuda.synchronize()
+        hits.append(hit.cpu().numpy().copy())
+        cnt = cache.cached_count.cpu().numpy()
+        idx = cache.cached_idx.cpu().numpy()
+        Ts.append([idx[r, :cnt[r]].astype(np.int64) for r in range(b)])
+        outs.append(gh.np32(out))
+    hits = np.array(hits)                              # [steps][b]
+    assert set(np.unique(hits)) <= {0, 1}
+    hits = hits.astype(bool)
+    for r in (0, 1, 4):
+        assert hits[:, r].tolist() == [False] + [True] * (steps - 1), (r, hits[:, r])
+    for r in (2, 3, 5, 6):
+        assert not hits[:, r].any(), (r, hits[:, r])
+    for t in range(steps):
+        assert Ts[t][1].size == 0
+        assert np.all(outs[t][1] == 0.0)
+    for r in (0, 2, 3, 4, 5, 6):
+        q_all = gh.np32(qs[:, r])
+        K, V = gh.np32(reqs[r].k), gh.np32(reqs[r].v)
+        ref = ora.decode_sequence(q_all, K, V, lens_all[:, r], geo.top_k, geo.n_local, 0.9,
+                                  want_outputs=False)
+        assert np.array_equal(hits[:, r], ref["hit"])
+        for t in range(steps):
+            N = int(lens_all[t, r])
+            if not hits[t, r]:
+                s = ora.select(q_all[t], K[:, :N], geo.top_k)
+                rel = gh.tol.vote_rel_budget(q_all[t], K[:, :N], s["z"], s["p"], s["M"], s["vote"])
+                amb = gh.tol.ambiguous_positions_log(s["vote"], rel, geo.top_k)
+                diff = np.setxor1d(Ts[t][r], s["T"])
+                assert np.all(amb[diff]), (r, t)
+            else:
+                assert np.array_equal(Ts[t][r], Ts[t - 1][r])
+            gh.check_attention(outs[t][r], q_all[t], K[:, :N], V[:, :N], Ts[t][r], N, geo.n_local,
+                               geo.attn_scale, False)

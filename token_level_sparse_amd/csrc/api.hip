@@ -566,16 +566,16 @@ ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel, c
   float* logits = at<float>(ws, L.logits);
   float* stats = at<float>(ws, L.stats);
 
-  ts::CacheParams cp{};
-  cp.q = q; cp.cached_q = cache->cached_q; cp.valid = cache->valid; cp.hit = hit;
-  cp.hist = at<uint32_t>(ws, L.hist);
-  cp.mass = sel->top_p > 0.0 ? at<unsigned long long>(ws, L.mass) : nullptr;
-  cp.H = shape->num_q_heads; cp.d = shape->head_dim; cp.b = shape->batch;
-  cp.theta = sel->cos_threshold; cp.bf16 = shape->dtype == TS_BF16;
-  if ((st = device_status(ts::launch_cache_check(cp, stream), "cache check launch")) != TS_OK) return st;
-
-  const ts::ScoreParams sp = score_params(*shape, *sel, q, k_pool, block_table, seq_lens, hit,
-                                          logits, stats, ws);
+  // Step 0 runs inside the score kernels: the score kernel decides hit[r] and skips
+  // the hits; the stats kernel applies each miss (C_Q <- Q, valid <- 1, cleared
+  // radix histograms) after every read of C_Q.
+  ts::ScoreParams sp = score_params(*shape, *sel, q, k_pool, block_table, seq_lens, nullptr,
+                                    logits, stats, ws);
+  sp.cache = 1;
+  sp.cached_q = cache->cached_q; sp.valid = cache->valid; sp.hit = hit;
+  sp.hist = at<uint32_t>(ws, L.hist);
+  sp.mass = sel->top_p > 0.0 ? at<unsigned long long>(ws, L.mass) : nullptr;
+  sp.theta = sel->cos_threshold;
   if ((st = device_status(ts::launch_score(sp, stream), "score launch")) != TS_OK) return st;
 
   const ts::VoteParams vp = vote_params(*shape, *sel, logits, stats, seq_lens, hit, nullptr,

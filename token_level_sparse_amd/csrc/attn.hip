@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(AttnParams p) {
   if ((tid & 63) == 0) s_red[tid >> 6] = L;
   __syncthreads();
   L = s_red[0] + s_red[1];
-  const float res = acc / L;
+  const float res = (L > 0.f) ? acc / L : 0.f;   // an empty set (N_r = 0) gives zeros
   if (kBf16)
     static_cast<uint16_t*>(p.out)[(int64_t)rh * kHeadDim + tid] = f32_to_bf16(res);
   else

@@ -24,6 +24,16 @@ struct ScoreParams {
   const int32_t* block_table; // [b][stride]
   const int32_t* seq_lens;    // [b]
   const int32_t* skip;        // [b] nonzero: request skipped (cache hit); may be null
+  // Selection Cache (decode step): the score kernel decides each request's hit itself
+  // and writes hit[r] (= skip); the stats kernel applies a miss (C_Q <- Q, valid <- 1,
+  // zeroed radix histograms). cache == 0: no cache.
+  int cache;
+  void* cached_q;             // [b][H * d]
+  int32_t* valid;             // [b]
+  int32_t* hit;               // [b]
+  uint32_t* hist;             // [b][3][kHistBins]
+  unsigned long long* mass;   // [b][3][kHistBins] or null
+  double theta;
   float* logits;              // ragged [H][N_r] per request
   float* partials;            // [chunks][H][2] per-chunk (max, sum exp)
   float* head_stats;          // [b][H][2]
@@ -79,17 +89,6 @@ struct AttnParams {
   int bf16;
 };
 
-struct CacheParams {
-  const void* q;
-  void* cached_q;
-  int32_t* valid;
-  int32_t* hit;
-  uint32_t* hist;             // zeroed for the requests that reselect
-  unsigned long long* mass;   // zeroed too when non-null (top-p)
-  int H, d, b;
-  double theta;
-  int bf16;
-};
 
 // Chunk-wise prefill. A request's chunk of c_r queries sits at positions
 // [P_r, P_r + c_r) of its cache, P_r = N_r - c_r. The attention of chunk query j
@@ -137,7 +136,6 @@ __host__ __device__ inline int attn_splits(int top_k, int n_local) {
 hipError_t launch_score(const ScoreParams& p, hipStream_t s);
 hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
-hipError_t launch_cache_check(const CacheParams& p, hipStream_t s);
 // Soft vote only (log2 votes into p.vote and the digit-0 histogram).
 hipError_t launch_vote_only(const VoteParams& p, hipStream_t s);
 // Radix TopK over any fp32 score array p.vote (segments p.seq_lens): histogram + phases.

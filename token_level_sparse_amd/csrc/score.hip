@@ -19,6 +19,7 @@
 // a page's 16 tokens x G heads land as one contiguous 64 G-byte block.
 #include <type_traits>
 
+#include "cache.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -248,6 +249,15 @@ __device__ __forceinline__ void row_reduce_scatter(const float (&acc)[4][S], int
   }
 }
 
+// Work chunks of request r. With the Selection Cache every request has at least one
+// (an empty request's units only take the cache decision), so the score kernel
+// writes hit[r] for all of them; a skipped request has none.
+__device__ __forceinline__ int32_t score_chunks(const ScoreParams& p, int r, int chunk_tokens) {
+  const int32_t c = (p.seq_lens[r] + chunk_tokens - 1) / chunk_tokens;
+  if (p.cache) return c > 1 ? c : 1;
+  return (p.skip && p.skip[r]) ? 0 : c;
+}
+
 template <bool kBf16, bool kQ32, int G>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
   using T = typename std::conditional<kBf16, uint16_t, float>::type;
@@ -261,12 +271,12 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
   const int b = p.b;
   const int chunk_tokens = p.chunk_pages * kPage;
   block_prefix(s_tok, b, [&](int r) -> int64_t { return p.seq_lens[r]; });
-  block_prefix(s_chunk, b, [&](int r) -> int32_t {
-    if (p.skip && p.skip[r]) return 0;
-    return (p.seq_lens[r] + chunk_tokens - 1) / chunk_tokens;
-  });
+  block_prefix(s_chunk, b, [&](int r) -> int32_t { return score_chunks(p, r, chunk_tokens); });
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ double s_red[3][4];
+  int dec_lo = -1, dec_hi = -1;                // requests of the last decided block (uniform)
+  int hit_v = 0;                               // the cache decision of this wave's request
   const int row = lane >> 4, col = lane & 15;
   const int H = p.H, Hkv = p.Hkv;
   const int total_units = s_chunk[b] * Hkv;
@@ -289,12 +299,31 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
   const int blk_hi = (int)((int64_t)blocks * (xcd + 1) / n_xcd);
   for (int blk = blk_lo + rank; blk < blk_hi; blk += per_xcd_wg) {
     const int u = blk * 4 + wave;
-    if (u >= total_units) break;
     // Wave-uniform unit coordinates (readfirstlane lets the block-table reads
     // below be scalar loads, which do not wait on the in-flight page loads).
-    const int cg = __builtin_amdgcn_readfirstlane(u / Hkv);
+    const int cg = __builtin_amdgcn_readfirstlane(min(u, total_units - 1) / Hkv);
     const int g = __builtin_amdgcn_readfirstlane(u - cg * Hkv);
     const int r = __builtin_amdgcn_readfirstlane(find_segment(s_chunk, b, cg));
+    if (p.cache) {
+      // Selection Cache (step 0): the workgroup decides each request its block
+      // touches, the same way in every workgroup; a hit skips the request's scoring.
+      // The block's first and last requests are uniform over the workgroup, so are
+      // the barriers inside the decision.
+      const int r_lo = find_segment(s_chunk, b, (blk * 4) / Hkv);
+      const int r_hi = find_segment(s_chunk, b, min(blk * 4 + 3, total_units - 1) / Hkv);
+      if (r_lo != dec_lo || r_hi != dec_hi) {
+        for (int rr = r_lo; rr <= r_hi; ++rr) {
+          const int h = cache_hit_wg<kBf16>(p.q, p.cached_q, rr, H * kHeadDim, p.valid[rr],
+                                            p.theta, s_red);
+          if (rr == r) hit_v = h;
+          if (threadIdx.x == 0) p.hit[rr] = h;
+        }
+        dec_lo = r_lo;
+        dec_hi = r_hi;
+      }
+    }
+    if (u >= total_units) break;                 // only in the workgroup's last block
+    if (p.cache && hit_v) continue;
     const int c0 = cg - __builtin_amdgcn_readfirstlane(s_chunk[r]);
     const int N = p.seq_lens[r];
     const int n_pages = (N + kPage - 1) / kPage;
@@ -387,11 +416,28 @@ __global__ __launch_bounds__(256) void stats_kernel(ScoreParams p) {
   const int b = p.b, H = p.H;
   const int r = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
   const int chunk_tokens = p.chunk_pages * kPage;
-  block_prefix(s_chunk, b, [&](int rr) -> int32_t {
-    if (p.skip && p.skip[rr]) return 0;
-    return (p.seq_lens[rr] + chunk_tokens - 1) / chunk_tokens;
-  });
-  if (p.skip && p.skip[r]) return;
+  block_prefix(s_chunk, b, [&](int rr) -> int32_t { return score_chunks(p, rr, chunk_tokens); });
+  if (p.cache) {
+    // every score wave has read C_Q: apply request r's decision (hit[r] was written by
+    // the score kernel). A miss stores the query and clears the radix histograms;
+    // the H workgroups of the request split the work.
+    if (p.hit[r]) return;
+    const int hd = kHeadDim * (p.bf16 ? 2 : 4) / 16;          // 16-byte chunks per head
+    const uint4* src = static_cast<const uint4*>(p.q) + ((int64_t)r * H + h) * hd;
+    uint4* dst = static_cast<uint4*>(p.cached_q) + ((int64_t)r * H + h) * hd;
+    for (int i = threadIdx.x; i < hd; i += blockDim.x) dst[i] = src[i];
+    const int per = (3 * kHistBins + H - 1) / H;
+    const int i0 = h * per, i1 = min(3 * kHistBins, i0 + per);
+    uint32_t* hg = p.hist + (int64_t)r * 3 * kHistBins;
+    for (int i = i0 + threadIdx.x; i < i1; i += blockDim.x) hg[i] = 0u;
+    if (p.mass) {
+      unsigned long long* mg = p.mass + (int64_t)r * 3 * kHistBins;
+      for (int i = i0 + threadIdx.x; i < i1; i += blockDim.x) mg[i] = 0ull;
+    }
+    if (h == 0 && threadIdx.x == 0) p.valid[r] = 1;
+  } else if (p.skip && p.skip[r]) {
+    return;
+  }
   const int c0 = s_chunk[r], c1 = s_chunk[r + 1];
   float M = kNegInf, S = 0.f;
   for (int c = c0 + threadIdx.x; c < c1; c += blockDim.x) {
