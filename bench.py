@@ -10,7 +10,9 @@ attention. Every timed step reselects (theta = 2 forces a cache miss), and the
 steps cycle through the 32 layers, so each step streams a different 2 GiB K pool.
 
 Prints one JSON line: decode steps/s (value), the scoring kernel's achieved HBM
-bandwidth against the 8 TB/s peak (roofline), the same metric at N = 131072
+bandwidth against the 8 TB/s peak (roofline; roofline.ceiling adds a plain streaming
+probe over the same K pools, read-only and with the scoring pass's 16:1 read/write
+mix, as the achievable reference), the same metric at N = 131072
 (secondary), the 16-request ragged batch (ragged_batch), the 256-step
 Selection Cache sequence on Qwen2-7B shapes (selection_cache: steps/s, hit rate,
 hit vector), chunk-wise prefill at 128K and 1M cached tokens with 512-token chunks
@@ -122,7 +124,54 @@ class Layer:
         self.out = torch.empty(1, H, d, dtype=geo.torch_dtype, device=dev)
 
 
-def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False):
+def stream_ceiling(pools, steps, dev):
+    """Time the streaming-bandwidth probe (libts_stream_probe.so) over the same K
+    pools the scoring launches read: a plain read of each pool, and the same read
+    with 1 byte written per 16 read (the scoring pass's K : logits mix at these
+    head counts). Returns GB/s of bytes moved, or None without the probe library."""
+    import ctypes
+    import torch
+    from token_level_sparse_amd import build as tb
+    if not os.path.exists(tb.PROBE_LIB):
+        log("[ceiling] libts_stream_probe.so not built; no ceiling figures")
+        return None
+    lib = ctypes.CDLL(tb.PROBE_LIB)
+    f = lib.ts_stream_probe
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    nbytes = pools[0].numel() * pools[0].element_size()
+    dst = torch.empty(nbytes // 16, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for write in (0, 1):
+        def launch(s):
+            P = pools[s % len(pools)]
+            rc = f(ctypes.c_void_p(P.data_ptr()), nbytes, ctypes.c_void_p(dst.data_ptr()), write, 2048,
+                   ctypes.c_void_p(sink.data_ptr()), st)
+            if rc != 0:
+                raise RuntimeError(f"ts_stream_probe failed ({rc})")
+        for s in range(4):
+            launch(s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(steps):
+            launch(s)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        moved = nbytes + (nbytes // 16 if write else 0)
+        res["read_plus_1_16_write" if write else "read_only"] = dict(ms=ms, gbps=moved / (ms * 1e-3) / 1e9)
+    del dst
+    log(f"[ceiling] probe over the same pools: read {res['read_only']['ms']:.4f} ms "
+        f"({res['read_only']['gbps']:.0f} GB/s), read + 1/16 write {res['read_plus_1_16_write']['ms']:.4f} ms "
+        f"({res['read_plus_1_16_write']['gbps']:.0f} GB/s)")
+    return res
+
+
+def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False, ceiling=False):
     import torch
     import token_level_sparse_amd as ts
     t0 = time.time()
@@ -182,6 +231,8 @@ def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False):
                score_bytes=algo, tokens=L0.total)
     log(f"[{geo.name}] score launch {score_ms:.4f} ms -> {res['score_gbps']:.0f} GB/s "
         f"(K stream {res['k_gbps']:.0f} GB/s)")
+    if ceiling:
+        res["ceiling"] = stream_ceiling([L.k_pool for L in layers], steps, dev)
     host = L0.host
     del layers, ws, logits, KC, VC
     torch.cuda.empty_cache()
@@ -496,6 +547,18 @@ def cpu_baseline(geo, host, min_seconds=10.0, max_steps=30):
                       f"{geo.name} (N={K.shape[1]}), {dt:.1f} s of host work"}
 
 
+def ceiling_line(res):
+    """The scoring launch against the probe's measured ceilings on the same pools."""
+    c = res.get("ceiling")
+    if not c:
+        return None
+    mixed = c["read_plus_1_16_write"]
+    return {"kernel": "ts_stream_probe (same K pools, 2048 workgroups)",
+            "read_only_gbps": c["read_only"]["gbps"], "read_only_ms": c["read_only"]["ms"],
+            "mixed_gbps": mixed["gbps"], "mixed_ms": mixed["ms"],
+            "score_frac_of_mixed": mixed["ms"] / res["score_ms"]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -524,7 +587,7 @@ def main():
         counter_run(geo, dev)
         return
     main_res, host = time_workload(geo, args.layers, args.steps, args.warmup, dev,
-                                   keep_host=not args.no_cpu_baseline)
+                                   keep_host=not args.no_cpu_baseline, ceiling=True)
     secondary = None
     if not args.no_secondary:
         g1 = wl.workload("llama3-8b-128k")
@@ -565,7 +628,8 @@ def main():
                      "unit": "GB/s", "frac": main_res["score_gbps"] / PEAK_HBM_GBPS,
                      "traffic": measured_traffic(),
                      "kernel": "score (tokenselect_score launch)",
-                     "bytes_per_launch": main_res["score_bytes"], "launch_ms": main_res["score_ms"]},
+                     "bytes_per_launch": main_res["score_bytes"], "launch_ms": main_res["score_ms"],
+                     "ceiling": ceiling_line(main_res)},
         "k_stream_gbps": main_res["k_gbps"],
         "scored_tokens_per_s": main_res["tokens"] * 1e3 / ms,
         "secondary": secondary,

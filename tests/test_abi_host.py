@@ -44,6 +44,28 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_stream_probe_library_exports_and_validates():
+    # measurement helper of bench.py: declared in its own header, built beside the
+    # main library; bad arguments are refused before any launch
+    from token_level_sparse_amd import build as tb
+    if not os.path.exists(tb.PROBE_LIB):
+        pytest.skip("probe library not built")
+    hdr = open(os.path.join(ROOT, "include", "ts_stream_probe.h")).read()
+    names = set(re.findall(r"\b(ts_stream_probe\w*)\s*\(", hdr))
+    assert names == {"ts_stream_probe"}
+    plib = ctypes.CDLL(tb.PROBE_LIB)
+    f = plib.ts_stream_probe
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(None, 4096, FAKE, 1, 8, FAKE, None) == -1          # no source
+    assert f(FAKE, 4096, FAKE, 1, 8, None, None) == -1          # no sink
+    assert f(FAKE, 4000 + 8, FAKE, 0, 8, FAKE, None) == -1      # not whole 16-byte words
+    assert f(ctypes.c_void_p(4104), 4096, FAKE, 0, 8, FAKE, None) == -1   # unaligned source
+    assert f(FAKE, 4096, None, 1, 8, FAKE, None) == -1          # writes without a destination
+    assert f(FAKE, 4096, FAKE, 0, 0, FAKE, None) == -1          # empty grid
+
+
 def test_workspace_size_valid_and_monotone(lib):
     a = ts.workspace_size(_shape(), _sel())
     b = ts.workspace_size(_shape(max_total_tokens=1 << 20), _sel())

@@ -1,7 +1,9 @@
 """Build libtokenselect.so (HIP, gfx950) in the package directory.
 
 Every kernel source under csrc/ is compiled by hipcc into one shared library
-exporting the C ABI declared in include/tokenselect.h.
+exporting the C ABI declared in include/tokenselect.h. The streaming-bandwidth
+probe under csrc/probe/ (measurement only, include/ts_stream_probe.h) is built
+into libts_stream_probe.so beside it.
 """
 from __future__ import annotations
 
@@ -14,6 +16,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libtokenselect.so")
+PROBE_LIB = os.path.join(PKG, "libts_stream_probe.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are turned off: the compiler would otherwise emit them
@@ -36,11 +39,10 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libtokenselect.so; returns the library path."""
-    tmp = LIB + ".tmp"
+def _compile(out: str, srcs, verbose: bool) -> str:
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           "-o", tmp, *sources()]
+           "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,7 +52,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libtokenselect.so (and the bandwidth probe into
+    libts_stream_probe.so); returns the main library path."""
+    _compile(LIB, sources(), verbose)
+    _compile(PROBE_LIB, sorted(glob.glob(os.path.join(PKG, "csrc", "probe", "*.hip"))), verbose)
     return LIB
 
 
