@@ -441,12 +441,18 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
 
     f32x16_t s[2];                        // scores, then probabilities, in place
     qk_block32(s_lds, q, l32, lg, s);
+    // Wave-uniform: every key of the block is visible to every row of the wave. Then
+    // the block maximum is taken on the raw scores (scaling by sl2 > 0 commutes with
+    // the rounded max) and each probability is one exp2 of an fma; the running maximum
+    // is finite after the rescale test, so no -inf guard is needed.
+    const bool full = x0 + KB <= w.x_end && x0 + KB - 1 <= wave_lim;
     float mloc = kNegInf;
-    if (x0 + KB <= w.x_end && x0 + KB - 1 <= wave_lim) {     // wave-uniform: nothing masked
+    if (full) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { s[t][i] *= sl2; mloc = fmaxf(mloc, s[t][i]); }
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[t][i]);
+      mloc *= sl2;
     } else {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -467,13 +473,24 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
     float psum = 0.f;
+    if (full) {
+      const float nm = -m_run;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[t][i] = (s[t][i] == kNegInf) ? 0.f : fast_exp2(s[t][i] - m_run);
-        psum += s[t][i];
-      }
+        for (int i = 0; i < 16; ++i) {
+          s[t][i] = fast_exp2(fmaf(s[t][i], sl2, nm));
+          psum += s[t][i];
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[t][i] = (s[t][i] == kNegInf) ? 0.f : fast_exp2(s[t][i] - m_run);
+          psum += s[t][i];
+        }
+    }
     l_run += psum;
     pv_block32(s_lds, s, l32, lg, o);
   }
