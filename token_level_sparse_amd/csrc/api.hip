@@ -305,10 +305,13 @@ ts_status prefill_select_launch(const ts_shape& s, const ts_select& sel, int max
   if (!stats) stats = at<float>(ws, L.dec.stats);
   ts::ScoreParams sp = score_params(s, sel, cp.qbar, k_pool, bt, past, nullptr, logits, stats, ws);
   sp.q_f32 = 1;
-  if ((st = device_status(ts::launch_score(sp, stream), "score launch")) != TS_OK) return st;
   const ts::VoteParams vp = vote_params(s, sel, logits, stats, past, nullptr, vote, sel_idx,
                                         sel_count, ws);
-  return device_status(ts::launch_vote_topk(vp, stream, true), "vote/top-k launch");
+  // the stats kernel clears the radix histograms (no separate clearing launch)
+  sp.hist = vp.hist;
+  sp.mass = vp.topp ? vp.mass : nullptr;
+  if ((st = device_status(ts::launch_score(sp, stream), "score launch")) != TS_OK) return st;
+  return device_status(ts::launch_vote_topk(vp, stream, false), "vote/top-k launch");
 }
 
 // ---------------------------------------------------------------- ablations

@@ -25,12 +25,14 @@ struct ScoreParams {
   const int32_t* seq_lens;    // [b]
   const int32_t* skip;        // [b] nonzero: request skipped (cache hit); may be null
   // Selection Cache (decode step): the score kernel decides each request's hit itself
-  // and writes hit[r] (= skip); the stats kernel applies a miss (C_Q <- Q, valid <- 1,
-  // zeroed radix histograms). cache == 0: no cache.
+  // and writes hit[r] (= skip); the stats kernel applies a miss (C_Q <- Q, valid <- 1).
+  // cache == 0: no cache.
   int cache;
   void* cached_q;             // [b][H * d]
   int32_t* valid;             // [b]
   int32_t* hit;               // [b]
+  // Radix histograms of the TopK launched next, or null: the stats kernel zeroes
+  // them for every request it folds (not for cache hits or skipped requests).
   uint32_t* hist;             // [b][3][kHistBins]
   unsigned long long* mass;   // [b][3][kHistBins] or null
   double theta;

@@ -426,6 +426,13 @@ __global__ __launch_bounds__(256) void stats_kernel(ScoreParams p) {
     const uint4* src = static_cast<const uint4*>(p.q) + ((int64_t)r * H + h) * hd;
     uint4* dst = static_cast<uint4*>(p.cached_q) + ((int64_t)r * H + h) * hd;
     for (int i = threadIdx.x; i < hd; i += blockDim.x) dst[i] = src[i];
+    if (h == 0 && threadIdx.x == 0) p.valid[r] = 1;
+  } else if (p.skip && p.skip[r]) {
+    return;
+  }
+  if (p.hist) {
+    // the radix histograms of the TopK that follows start from zero; the H
+    // workgroups of the request split them
     const int per = (3 * kHistBins + H - 1) / H;
     const int i0 = h * per, i1 = min(3 * kHistBins, i0 + per);
     uint32_t* hg = p.hist + (int64_t)r * 3 * kHistBins;
@@ -434,9 +441,6 @@ __global__ __launch_bounds__(256) void stats_kernel(ScoreParams p) {
       unsigned long long* mg = p.mass + (int64_t)r * 3 * kHistBins;
       for (int i = i0 + threadIdx.x; i < i1; i += blockDim.x) mg[i] = 0ull;
     }
-    if (h == 0 && threadIdx.x == 0) p.valid[r] = 1;
-  } else if (p.skip && p.skip[r]) {
-    return;
   }
   const int c0 = s_chunk[r], c1 = s_chunk[r + 1];
   float M = kNegInf, S = 0.f;
