@@ -199,18 +199,19 @@ __device__ __forceinline__ void stage_store(const Tile<true>& t, char* lds) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     *reinterpret_cast<uint4*>(Ks + (4 * kq + i) * Tile<true>::kKStride + 8 * dc) = t.k[i];
-  // V^T[d][key]: for each of the 8 dims, the 4 keys' values packed into 8 bytes
+  // V^T[d][key]: for each of the 8 dims, the 4 keys' values packed into 8 bytes. One
+  // byte permute joins the same 16-bit half of two keys' words (v_perm_b32: selector
+  // bytes 0-3 pick from the second operand, 4-7 from the first).
   const uint32_t w[4][4] = {{t.v[0].x, t.v[0].y, t.v[0].z, t.v[0].w},
                             {t.v[1].x, t.v[1].y, t.v[1].z, t.v[1].w},
                             {t.v[2].x, t.v[2].y, t.v[2].z, t.v[2].w},
                             {t.v[3].x, t.v[3].y, t.v[3].z, t.v[3].w}};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int sh = (e & 1) ? 16 : 0;
-    const uint32_t b0 = (w[0][e >> 1] >> sh) & 0xffffu, b1 = (w[1][e >> 1] >> sh) & 0xffffu;
-    const uint32_t b2 = (w[2][e >> 1] >> sh) & 0xffffu, b3 = (w[3][e >> 1] >> sh) & 0xffffu;
-    *reinterpret_cast<uint2*>(Vt + (8 * vc + e) * Tile<true>::kVStride + 4 * vq) =
-        make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+    const uint32_t k01 = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
+    const uint32_t k23 = __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel);
+    *reinterpret_cast<uint2*>(Vt + (8 * vc + e) * Tile<true>::kVStride + 4 * vq) = make_uint2(k01, k23);
   }
 }
 __device__ __forceinline__ void stage_load(Tile<false>& t, const float* kp, const float* vp,
@@ -405,7 +406,7 @@ constexpr int kRows32 = 128;
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void chunk_attn_bf16_kernel(ChunkParams p) {
   constexpr int KB = Tile<true>::kKeys;
-  __shared__ __align__(16) char s_lds[Tile<true>::kLds];
+  __shared__ __align__(16) char s_lds[2 * Tile<true>::kLds];
   __shared__ int64_t s_keys[kChunkSplitKeys];
   __shared__ int s_geom[2];
   UnitWork w;
@@ -431,68 +432,83 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
 
+  // The block products: scores, online softmax, O^T += V^T P^T over the block staged at lds.
+  auto block = [&](const char* lds, int x0) {
+      f32x16_t s[2];                        // scores, then probabilities, in place
+      qk_block32(lds, q, l32, lg, s);
+      // Wave-uniform: every key of the block is visible to every row of the wave. Then
+      // the block maximum is taken on the raw scores (scaling by sl2 > 0 commutes with
+      // the rounded max) and each probability is one exp2 of an fma; the running maximum
+      // is finite after the rescale test, so no -inf guard is needed.
+      const bool full = x0 + KB <= w.x_end && x0 + KB - 1 <= wave_lim;
+      float mloc = kNegInf;
+      if (full) {
+  #pragma unroll
+        for (int t = 0; t < 2; ++t)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[t][i]);
+        mloc *= sl2;
+      } else {
+  #pragma unroll
+        for (int t = 0; t < 2; ++t)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int x = x0 + 32 * t + 8 * (i >> 2) + 4 * lg + (i & 3);
+            s[t][i] = (x < w.x_end && x <= lim) ? s[t][i] * sl2 : kNegInf;
+            mloc = fmaxf(mloc, s[t][i]);
+          }
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+  #pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+      }
+      float psum = 0.f;
+      if (full) {
+        const float nm = -m_run;
+  #pragma unroll
+        for (int t = 0; t < 2; ++t)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            s[t][i] = fast_exp2(fmaf(s[t][i], sl2, nm));
+            psum += s[t][i];
+          }
+      } else {
+  #pragma unroll
+        for (int t = 0; t < 2; ++t)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            s[t][i] = (s[t][i] == kNegInf) ? 0.f : fast_exp2(s[t][i] - m_run);
+            psum += s[t][i];
+          }
+      }
+      l_run += psum;
+      pv_block32(lds, s, l32, lg, o);
+  };
+
+  // Two LDS buffers, one barrier per block: block n is read from one buffer while
+  // block n + 1, already in the staging registers, is written to the other after the
+  // products; the loads of block n + 2 then overlap the next block's products.
+  char* buf0 = s_lds;
+  char* buf1 = s_lds + Tile<true>::kLds;
   Tile<true> st;
   stage_load(st, kp, vp, w.km, w.x_begin);
+  stage_store(st, buf0);
+  if (w.x_begin + KB < w.x_end) stage_load(st, kp, vp, w.km, w.x_begin + KB);
+  __syncthreads();
+  int cur = 0;
   for (int x0 = w.x_begin; x0 < w.x_end; x0 += KB) {
-    __syncthreads();                      // the previous block's reads of LDS are done
-    stage_store(st, s_lds);
+    block(cur ? buf1 : buf0, x0);
+    if (x0 + KB < w.x_end) {
+      stage_store(st, cur ? buf0 : buf1);   // every wave finished reading it before the last barrier
+      if (x0 + 2 * KB < w.x_end) stage_load(st, kp, vp, w.km, x0 + 2 * KB);
+    }
     __syncthreads();
-    if (x0 + KB < w.x_end) stage_load(st, kp, vp, w.km, x0 + KB);   // overlaps the products
-
-    f32x16_t s[2];                        // scores, then probabilities, in place
-    qk_block32(s_lds, q, l32, lg, s);
-    // Wave-uniform: every key of the block is visible to every row of the wave. Then
-    // the block maximum is taken on the raw scores (scaling by sl2 > 0 commutes with
-    // the rounded max) and each probability is one exp2 of an fma; the running maximum
-    // is finite after the rescale test, so no -inf guard is needed.
-    const bool full = x0 + KB <= w.x_end && x0 + KB - 1 <= wave_lim;
-    float mloc = kNegInf;
-    if (full) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[t][i]);
-      mloc *= sl2;
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int x = x0 + 32 * t + 8 * (i >> 2) + 4 * lg + (i & 3);
-          s[t][i] = (x < w.x_end && x <= lim) ? s[t][i] * sl2 : kNegInf;
-          mloc = fmaxf(mloc, s[t][i]);
-        }
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-    }
-    float psum = 0.f;
-    if (full) {
-      const float nm = -m_run;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[t][i] = fast_exp2(fmaf(s[t][i], sl2, nm));
-          psum += s[t][i];
-        }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[t][i] = (s[t][i] == kNegInf) ? 0.f : fast_exp2(s[t][i] - m_run);
-          psum += s[t][i];
-        }
-    }
-    l_run += psum;
-    pv_block32(s_lds, s, l32, lg, o);
+    cur ^= 1;
   }
 
   const float lt = l_run + __shfl_xor(l_run, 32);
