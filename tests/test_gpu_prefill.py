@@ -116,3 +116,46 @@ def test_prefill_llama3_1m_sampled():
     gh.log(f"[prefill llama3 1m] N={geo.seq_len} c={geo.chunk} k={geo.top_k}")
     cb = wl.make_chunk_batch(geo, DEV)
     _run_all(cb, geo, rows=[0, 17, 200, 511])
+
+
+@pytest.mark.parametrize("p", [0.5, 0.9])
+def test_prefill_top_p_budget_and_workspace_reuse(p):
+    # The dynamic top-p budget through the prefill selection (mean query over the
+    # past): the set is exactly the top m of the GPU's own votes with m the budget
+    # those votes imply, and it holds >= p of the oracle's vote mass. The score launch
+    # clears the radix histograms and masses of the TopK that follows, so a second
+    # call on the same workspace must give the same selection bit for bit.
+    from tests.test_gpu_topp import _check_request
+    geo = wl.workload("prefill-llama3-128k", batch=3, min_len=2000, max_len=30000, seed=5600)
+    cb = wl.make_chunk_batch(geo, DEV, chunk_lens=[512, 100, 1])
+    b, H, k = 3, geo.num_q_heads, geo.top_k
+    mc = cb.q_chunk.shape[1]
+    lens = [int(x) for x in cb.seq_lens.cpu()]
+    clens = [int(x) for x in cb.chunk_lens.cpu()]
+    past = [n - c for n, c in zip(lens, clens)]
+    gh.log(f"[prefill top-p p={p}] past {past} chunk lengths {clens}")
+    max_total = sum(lens)
+    shape = ts.make_shape(H, geo.num_kv_heads, b, cb.paged.block_table.shape[1], max_total, geo.torch_dtype)
+    sel = ts.make_select(k, geo.n_local, 1.0, geo.attn_scale, geo.cos_threshold, p)
+    ws = ts.alloc_prefill_workspace(shape, sel, mc, DEV)
+    runs = []
+    for _ in range(2):
+        vote = torch.full((max_total,), float("nan"), dtype=torch.float32, device=DEV)
+        si = torch.full((b, k), -7, dtype=torch.int32, device=DEV)
+        sc = torch.full((b,), -7, dtype=torch.int32, device=DEV)
+        ts.prefill_select(shape, sel, mc, cb.q_chunk, cb.chunk_lens, cb.paged.k_pool, cb.paged.block_table,
+                          cb.seq_lens, None, None, vote, si, sc, ws)
+        torch.cuda.synchronize()
+        runs.append((vote.cpu().numpy(), si.cpu().numpy(), sc.cpu().numpy()))
+    assert np.array_equal(runs[0][2], runs[1][2])
+    assert np.array_equal(runs[0][1], runs[1][1])
+    lv, si, sc = runs[0]
+    off = 0
+    for r in range(b):
+        P, m = past[r], int(sc[r])
+        Qc = gh.np32(cb.q_chunk[r, :clens[r]])
+        K = gh.np32(cb.paged.requests[r].k[:, :P])
+        ref = pre.prefill_select(Qc, K, P, k)
+        _check_request(lv[off: off + P], si[r, :m].astype(np.int64), m, p, k, ref["vote"])
+        gh.log(f"  request {r}: P={P} budget {m}")
+        off += P
