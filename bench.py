@@ -203,7 +203,17 @@ def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False, ceiling=Fa
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / steps
-    log(f"[{geo.name}] decode step {ms_step:.4f} ms (wall {wall / steps * 1e3:.4f} ms)")
+    # the spread: each step of a second pass between its own events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s, (a, b) in enumerate(evs):
+        a.record()
+        step(s)
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    pct = {q: per[min(len(per) - 1, int(q / 100 * len(per)))] for q in (10, 50, 90)}
+    log(f"[{geo.name}] decode step {ms_step:.4f} ms (wall {wall / steps * 1e3:.4f} ms; per step "
+        f"p10 {pct[10]:.4f} p50 {pct[50]:.4f} p90 {pct[90]:.4f} ms)")
 
     # the scoring launch alone (tokenselect_score: the scoring kernel plus the small
     # kernel folding per-unit softmax pairs), timed per launch on the same stream
@@ -226,7 +236,8 @@ def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False, ceiling=Fa
     score_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
     algo = score_bytes_per_token(geo) * L0.total
     kbytes = geo.num_kv_heads * geo.head_dim * (2 if geo.dtype == "bf16" else 4) * L0.total
-    res = dict(ms_per_step=ms_step, wall_ms_per_step=wall / steps * 1e3, score_ms=score_ms,
+    res = dict(ms_per_step=ms_step, wall_ms_per_step=wall / steps * 1e3,
+               step_ms_p10=pct[10], step_ms_p50=pct[50], step_ms_p90=pct[90], score_ms=score_ms,
                score_gbps=algo / (score_ms * 1e-3) / 1e9, k_gbps=kbytes / (score_ms * 1e-3) / 1e9,
                score_bytes=algo, tokens=L0.total)
     log(f"[{geo.name}] score launch {score_ms:.4f} ms -> {res['score_gbps']:.0f} GB/s "
@@ -400,10 +411,72 @@ def time_cache_sequence(geo, dev):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     hv = hits.cpu().tolist()
-    log(f"[{geo.name}] {steps} steps: {ms:.4f} ms/step, hit rate {sum(hv) / steps:.3f}")
+    # untimed third pass: how much of each reselected TopK the previous one already held
+    cache.valid.zero_()
+    snaps = []
+    for t in range(steps):
+        ts.decode_step(shape, sel, qs[t], batch.k_pool, batch.v_pool, batch.block_table, lens[t],
+                       cache, hits[t:t + 1], out, ws)
+        snaps.append((cache.cached_idx.clone(), cache.cached_count.clone()))
+    torch.cuda.synchronize()
+    hv3 = hits.cpu().tolist()
+    miss_sets = [set(snaps[t][0][0, :int(snaps[t][1][0])].tolist()) for t in range(steps) if hv3[t] == 0]
+    overlaps = [len(a & b) / max(1, len(b)) for a, b in zip(miss_sets, miss_sets[1:])]
+    overlap = sum(overlaps) / len(overlaps) if overlaps else None
+    log(f"[{geo.name}] {steps} steps: {ms:.4f} ms/step, hit rate {sum(hv) / steps:.3f}, "
+        f"mean overlap of consecutive reselections {overlap if overlap is None else round(overlap, 4)}")
     res = {"workload": geo.name, "steps": steps, "decode_steps_per_s": 1e3 / ms, "ms_per_step": ms,
-           "hit_rate": sum(hv) / steps, "hits": "".join(str(h) for h in hv)}
+           "hit_rate": sum(hv) / steps, "hits": "".join(str(h) for h in hv),
+           "miss_topk_overlap": overlap, "same_hits_on_rerun": hv3 == hv}
     del batch, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_dense(geo, decode_ms, read_gbps, dev, reps=10):
+    """Dense attention at the workload's N for reference. Timed: the sparse attention
+    kernel with every position selected (k = N), which reads all of K and V of one
+    layer; it is built for gathers, not for a dense stream, so the fair reference is
+    the bound: K + V bytes at the measured plain-read bandwidth (read_gbps)."""
+    import torch
+    import token_level_sparse_amd as ts
+    KC, VC = kv_cache(geo, 1, dev)
+    L = Layer(geo, 0, dev, False, (KC[0], VC[0]))
+    N, H = L.total, geo.num_q_heads
+    shape = ts.make_shape(H, geo.num_kv_heads, 1, L.block_table.shape[1], N, geo.torch_dtype)
+    sel = ts.make_select(N, geo.n_local, 1.0, geo.attn_scale, 2.0)
+    ws = ts.alloc_workspace(shape, sel, dev)
+    idx = torch.arange(N, dtype=torch.int32, device=dev).reshape(1, N)
+    cnt = torch.full((1,), N, dtype=torch.int32, device=dev)
+    out = torch.empty(1, H, geo.head_dim, dtype=geo.torch_dtype, device=dev)
+
+    def run():
+        ts.sparse_attn(shape, sel, L.q, L.k_pool, L.v_pool, L.block_table, L.seq_lens, idx, cnt, out, ws)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    kv_bytes = 2 * geo.num_kv_heads * geo.head_dim * (2 if geo.dtype == "bf16" else 4) * N
+    bound_ms = kv_bytes / (read_gbps * 1e9) * 1e3 if read_gbps else None
+    log(f"[{geo.name}] dense attention over all {N} positions: sparse kernel with k = N {ms:.4f} ms "
+        f"({kv_bytes / (ms * 1e-3) / 1e9:.0f} GB/s of K+V); K+V at the plain-read bandwidth "
+        f"{bound_ms if bound_ms is None else round(bound_ms, 4)} ms; decode step {decode_ms:.4f} ms")
+    res = {"workload": geo.name, "N": N, "kv_bytes": kv_bytes,
+           "sparse_kernel_k_eq_n_ms": ms, "sparse_kernel_k_eq_n_gbps": kv_bytes / (ms * 1e-3) / 1e9,
+           "dense_bound_ms": bound_ms,
+           "decode_step_vs_dense_bound": (bound_ms / decode_ms) if bound_ms else None,
+           "what": "dense attention reference for one decode step at this N: the bound is all of "
+                   "K and V read at the plain streaming bandwidth measured on the same box "
+                   "(roofline.ceiling.read_only_gbps); the ratio compares it with one whole "
+                   "TokenSelect decode step, selection included"}
+    del L, ws, KC, VC
     torch.cuda.empty_cache()
     return res
 
@@ -594,10 +667,15 @@ def main():
         # 8 rotating layers: 8 x 256 MiB of K, so no step finds its pool in the 256 MB MALL
         r1, _ = time_workload(g1, 8, max(args.steps, 32), args.warmup, dev)
         secondary = {"workload": g1.name, "N": g1.seq_len, "decode_steps_per_s": 1e3 / r1["ms_per_step"],
-                     "ms_per_step": r1["ms_per_step"], "score_ms": r1["score_ms"],
+                     "ms_per_step": r1["ms_per_step"],
+                     "step_ms_percentiles": {q: r1[f"step_ms_p{q}"] for q in (10, 50, 90)},
+                     "score_ms": r1["score_ms"],
                      "score_gbps": r1["score_gbps"], "k_gbps": r1["k_gbps"], "rotating_layers": 8}
-    ragged = cache_seq = prefill = topp = ablations = None
+    ragged = cache_seq = prefill = topp = ablations = dense = None
     if not args.no_secondary:
+        ceil = main_res.get("ceiling") or {}
+        dense = time_dense(geo, main_res["ms_per_step"],
+                           (ceil.get("read_only") or {}).get("gbps"), dev)
         ragged = time_ragged(wl.workload("llama3-8b-ragged16"), max(8, args.steps // 4), 2, dev)
         cache_seq = time_cache_sequence(wl.workload("qwen2-7b-cache256"), dev)
         topp = time_topp(geo, 8, max(16, args.steps // 2), 4, dev)
@@ -615,6 +693,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "step_ms_percentiles": {q: main_res[f"step_ms_p{q}"] for q in (10, 50, 90)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -638,6 +717,7 @@ def main():
         "prefill": prefill,
         "top_p": topp,
         "ablations": ablations,
+        "dense_reference": dense,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

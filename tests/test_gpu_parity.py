@@ -175,6 +175,23 @@ def test_attention_given_oracle_selection():
     assert np.max(np.abs(po.out[0] - ref)) <= 2e-2
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_over_every_position(dtype):
+    # k = N selects everything: step 5 is then dense attention over the whole cache
+    # (the dense reference the benchmark times at 1M), here at 40000 positions
+    # (313 selection slices of 128 and the window overlapping the selection)
+    n = 40000
+    geo = wl.workload("llama3-8b-128k", seq_len=n, top_k=n, n_local=512, n_planted=4, dtype=dtype)
+    gh.log(f"[attn over all {n} positions, {dtype}]")
+    batch = wl.make_batch(geo, device=DEV)
+    r = batch.requests[0]
+    q, K, V = gh.np32(r.q), gh.np32(r.k), gh.np32(r.v)
+    sel_idx = torch.arange(n, dtype=torch.int32, device=DEV)[None]
+    sel_count = torch.tensor([n], dtype=torch.int32, device=DEV)
+    po = gh.run_path(batch, geo, sel_override=(sel_idx, sel_count))
+    gh.check_attention(po.out[0], q, K, V, np.arange(n), n, geo.n_local, geo.attn_scale, dtype == "f32")
+
+
 # ------------------------------------------------------------------ head groupings and batch limits
 @pytest.mark.parametrize("H,Hkv,dtype", [(8, 8, "bf16"), (16, 8, "f32"), (12, 4, "bf16"), (40, 8, "bf16"),
                                          (48, 8, "f32"), (64, 8, "bf16")])
