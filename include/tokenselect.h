@@ -35,8 +35,9 @@
  *     gives a message (thread-local). A failed launch returns TS_ERR_DEVICE.
  *   - Device-side contract (not checked): every block-table entry a request
  *     reaches (pages [0, ceil(N_r / page_size))) is a valid pool page;
- *     1 <= N_r <= block_table_stride * page_size; sum of N_r <=
- *     shape.max_total_tokens; every selected index lies in [0, N_r).
+ *     0 <= N_r <= block_table_stride * page_size; sum of N_r <=
+ *     shape.max_total_tokens; every selected index lies in [0, N_r). A request
+ *     with N_r = 0 selects nothing (sel_count 0) and its attention output is 0.
  *
  * Layouts
  *   q          [batch][H][d]                      element type `dtype`
