@@ -215,7 +215,7 @@ ts::AttnParams attn_params(const ts_shape& s, const ts_select& sel, const void* 
 // ---------------------------------------------------------------- prefill
 struct PrefillLayout {
   Layout dec;                  // the decode regions, used by the selection over the past
-  size_t qbar, past, cpart, keytab, total;
+  size_t qbar, past, cpart, total;
 };
 
 int chunk_splits_for(const ts_shape& s, const ts_select& sel, int max_chunk) {
@@ -235,7 +235,6 @@ PrefillLayout prefill_layout(const ts_shape& s, const ts_select& sel, int max_ch
   L.past = off;  off += align_up(sizeof(int32_t) * (size_t)s.batch);
   L.cpart = off; off += align_up(sizeof(float) * bH * (size_t)max_chunk *
                                  chunk_splits_for(s, sel, max_chunk) * ts::kChunkPartStride);
-  L.keytab = off; off += align_up(sizeof(int32_t) * (size_t)s.batch * chunk_max_keys_for(s, sel, max_chunk));
   L.total = off;
   return L;
 }
@@ -279,8 +278,6 @@ ts::ChunkParams chunk_params(const ts_shape& s, const ts_select& sel, int max_ch
   p.block_table = bt; p.sel_idx = sel_idx; p.sel_count = sel_count;
   p.qbar = at<float>(ws, L.qbar); p.past_lens = at<int32_t>(ws, L.past);
   p.partials = at<float>(ws, L.cpart); p.out = out;
-  p.keytab = at<int32_t>(ws, L.keytab);
-  p.max_keys = (int)chunk_max_keys_for(s, sel, max_chunk);
   p.H = s.num_q_heads; p.Hkv = s.num_kv_heads; p.b = s.batch; p.stride = s.block_table_stride;
   p.max_chunk = max_chunk; p.sel_stride = sel.top_k; p.n_local = sel.n_local;
   p.splits = chunk_splits_for(s, sel, max_chunk);

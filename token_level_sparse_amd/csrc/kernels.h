@@ -116,9 +116,8 @@ struct ChunkParams {
   float* qbar;                // [b][H][d] fp32 mean query (output of the mean kernel)
   int32_t* past_lens;         // [b] P_r (output of the mean kernel)
   float* partials;            // [b][max_chunk][H][splits][kChunkPartStride]
-  int32_t* keytab;            // [b][max_keys] page * 16 + slot of each key-list entry
   void* out;                  // [b][max_chunk][H][d]
-  int H, Hkv, b, stride, max_chunk, sel_stride, n_local, splits, max_keys;
+  int H, Hkv, b, stride, max_chunk, sel_stride, n_local, splits;
   float attn_scale;
   int bf16;
 };

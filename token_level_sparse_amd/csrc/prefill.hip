@@ -135,27 +135,6 @@ __global__ __launch_bounds__(kMeanThreads) void chunk_mean_kernel(ChunkParams p)
   if (h == 0 && threadIdx.x == 0) p.past_lens[r] = gm.P;
 }
 
-// ---------------------------------------------------------------- key list
-// keytab[r][x] = page * 16 + slot of key-list entry x of request r (x < base + c),
-// built once per request so the attention's K/V loads wait on one LDS read.
-__global__ __launch_bounds__(256) void chunk_keys_kernel(ChunkParams p) {
-  __shared__ int s_geom[5];
-  const int per = (p.max_keys + 255) / 256;
-  const int r = blockIdx.x / per, blk = blockIdx.x - (blockIdx.x / per) * per;
-  if (threadIdx.x == 0) {
-    const ChunkGeom gm = chunk_geom(p, r, true);
-    s_geom[0] = gm.c; s_geom[1] = gm.w0; s_geom[2] = gm.n_sel; s_geom[3] = gm.base; s_geom[4] = gm.N;
-  }
-  __syncthreads();
-  const int c = s_geom[0], w0 = s_geom[1], n_sel = s_geom[2], base = s_geom[3], N = s_geom[4];
-  const int x = blk * 256 + threadIdx.x;
-  if (x >= base + c || x >= p.max_keys) return;
-  int pos = x < n_sel ? p.sel_idx[(int64_t)r * p.sel_stride + x] : w0 + (x - n_sel);
-  pos = min(max(pos, 0), N - 1);
-  const int page = p.block_table[(int64_t)r * p.stride + (pos >> 4)];
-  p.keytab[(int64_t)r * p.max_keys + x] = page * kPage + (pos & (kPage - 1));
-}
-
 // ---------------------------------------------------------------- attention
 template <bool kBf16> struct Tile;
 template <> struct Tile<true> {
@@ -354,7 +333,7 @@ __device__ bool chunk_unit(const ChunkParams& p, int rows_per_wg, int* s_geom, i
   w.r = u / (p.splits * Hkv);
   if (threadIdx.x == 0) {
     const ChunkGeom gm = chunk_geom(p, w.r, true);
-    s_geom[0] = gm.c; s_geom[1] = gm.base;
+    s_geom[0] = gm.c; s_geom[1] = gm.base; s_geom[2] = gm.w0; s_geom[3] = gm.n_sel; s_geom[4] = gm.N;
   }
   __syncthreads();
   const int c = s_geom[0];
@@ -367,10 +346,16 @@ __device__ bool chunk_unit(const ChunkParams& p, int rows_per_wg, int* s_geom, i
   w.x_begin = w.split * kChunkSplitKeys;
   if (w.x_begin >= n_vis) return false;
   w.x_end = min(w.x_begin + kChunkSplitKeys, n_vis);
-  const int32_t* kt = p.keytab + (int64_t)w.r * p.max_keys;
-  for (int x = w.x_begin + (int)threadIdx.x; x < w.x_end; x += 256) {
-    const int v = kt[x];                                       // page * 16 + slot
-    s_keys[x - w.x_begin] = (((int64_t)(v >> 4) * Hkv + w.g) * kPage + (v & (kPage - 1))) * kHeadDim;
+  // key-list entry x: the x-th selected position below the window (the TopK is
+  // ascending), then the window and the chunk [w0, P + c); its row of this KV head
+  const int w0 = s_geom[2], n_sel = s_geom[3], N = s_geom[4];
+  const int32_t* sel = p.sel_idx + (int64_t)w.r * p.sel_stride;
+  const int32_t* bt = p.block_table + (int64_t)w.r * p.stride;
+  for (int x = w.x_begin + (int)threadIdx.x; x < w.x_end; x += blockDim.x) {
+    int pos = x < n_sel ? sel[x] : w0 + (x - n_sel);
+    pos = min(max(pos, 0), max(N - 1, 0));
+    const int64_t page = bt[pos >> 4];
+    s_keys[x - w.x_begin] = ((page * Hkv + w.g) * kPage + (pos & (kPage - 1))) * kHeadDim;
   }
   __syncthreads();
   w.km.off = s_keys; w.km.x_begin = w.x_begin; w.km.x_end = w.x_end;
@@ -408,7 +393,7 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
   constexpr int KB = Tile<true>::kKeys;
   __shared__ __align__(16) char s_lds[2 * Tile<true>::kLds];
   __shared__ int64_t s_keys[kChunkSplitKeys];
-  __shared__ int s_geom[2];
+  __shared__ int s_geom[5];
   UnitWork w;
   if (!chunk_unit(p, kRows32, s_geom, s_keys, w)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -533,7 +518,7 @@ __global__ __launch_bounds__(256) void chunk_attn_f32_kernel(ChunkParams p) {
   constexpr int NT = KB / 16;
   __shared__ __align__(16) char s_lds[Tile<false>::kLds];
   __shared__ int64_t s_keys[kChunkSplitKeys];
-  __shared__ int s_geom[2];
+  __shared__ int s_geom[5];
   UnitWork w;
   if (!chunk_unit(p, kRows16, s_geom, s_keys, w)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -652,7 +637,6 @@ hipError_t launch_chunk_attn(const ChunkParams& p, hipStream_t s) {
   const int rows_per_wg = p.bf16 ? kRows32 : kRows16;
   const int rt = (p.max_chunk * G + rows_per_wg - 1) / rows_per_wg;
   const dim3 block(256);
-  hipLaunchKernelGGL(chunk_keys_kernel, dim3(p.b * ((p.max_keys + 255) / 256)), block, 0, s, p);
   const int units = p.b * p.Hkv * p.splits;
   const dim3 grid(kXcds * rt * ((units + kXcds - 1) / kXcds));
   if (p.bf16) hipLaunchKernelGGL(chunk_attn_bf16_kernel, grid, block, 0, s, p);
