@@ -37,7 +37,7 @@ struct ScoreParams {
   unsigned long long* mass;   // [b][3][kHistBins] or null
   double theta;
   float* logits;              // ragged [H][N_r] per request
-  float* partials;            // [chunks][H][2] per-chunk (max, sum exp)
+  float* partials;            // [H][chunks][2] per-chunk (max, sum exp), chunks of all requests
   float* head_stats;          // [b][H][2]
   int H, Hkv, b, stride;
   int chunk_pages;            // pages per work unit

@@ -401,7 +401,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
 #pragma unroll
       for (int x = 16; x <= 32; x <<= 1) merge_ms(mm, ss, __shfl_xor(mm, x), __shfl_xor(ss, x));
       if (row == 0 && (col & 3) == 0 && hd[c] < G) {
-        float* dst = p.partials + ((int64_t)cg * H + g * G + hd[c]) * 2;
+        float* dst = p.partials + ((int64_t)(g * G + hd[c]) * s_chunk[b] + cg) * 2;
         dst[0] = mm;
         dst[1] = ss;
       }
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(256) void stats_kernel(ScoreParams p) {
   const int c0 = s_chunk[r], c1 = s_chunk[r + 1];
   float M = kNegInf, S = 0.f;
   for (int c = c0 + threadIdx.x; c < c1; c += blockDim.x) {
-    const float* src = p.partials + ((int64_t)c * H + h) * 2;
+    const float* src = p.partials + ((int64_t)h * s_chunk[b] + c) * 2;   // [H][chunks]: coalesced
     merge_ms(M, S, src[0], src[1]);
   }
   for (int o = 32; o > 0; o >>= 1) {
