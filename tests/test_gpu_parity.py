@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import token_level_sparse_amd as ts
 from tests import gpu_helpers as gh
 from synth import workloads as wl
 from oracle import tokenselect_oracle as ora
@@ -112,6 +113,26 @@ def test_llama3_1m_one_layer_full():
     # planted recall (the vote bound): any position with vote > H/k is selected
     big = np.nonzero(np.exp2(po.vote[0].astype(np.float64)) > geo.num_q_heads / geo.top_k)[0]
     assert np.all(np.isin(big, po.T[0]))
+    # the benchmark's configuration: one tokenselect_decode_step with theta = 2 (every
+    # step reselects) gives the checked TopK and output bit for bit, then a hit
+    # (theta = -1) reuses that TopK
+    H, d = geo.num_q_heads, geo.head_dim
+    shape = ts.make_shape(H, geo.num_kv_heads, 1, batch.block_table.shape[1], batch.total_tokens,
+                          geo.torch_dtype)
+    cache = ts.CacheState.allocate(1, H, d, geo.top_k, geo.torch_dtype, DEV)
+    hit = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    out = torch.empty(1, H, d, dtype=geo.torch_dtype, device=DEV)
+    for theta, want_hit in ((2.0, 0), (-1.0, 1)):
+        sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, theta)
+        ws = ts.alloc_workspace(shape, sel, DEV)
+        ts.decode_step(shape, sel, batch.q, batch.k_pool, batch.v_pool, batch.block_table, batch.seq_lens,
+                       cache, hit, out, ws)
+        torch.cuda.synchronize()
+        assert int(hit[0]) == want_hit
+        m = int(cache.cached_count[0])
+        assert np.array_equal(cache.cached_idx[0, :m].cpu().numpy().astype(np.int64), po.T[0])
+        assert np.array_equal(gh.np32(out[0]), po.out[0])
+        del ws
 
 
 def test_planted_recall_without_scale_spread():
