@@ -95,6 +95,32 @@ def test_ragged_batch_reduced():
     gh.log(f"  {st}")
 
 
+def _decode_step_matches(batch, geo, po):
+    """The benchmark's configuration: one tokenselect_decode_step with theta = 2 (every
+    request reselects) gives the oracle-checked TopK and outputs of the separate entry
+    points bit for bit; then theta = -1 makes every request a hit that reuses them."""
+    b = batch.q.shape[0]
+    H, d = geo.num_q_heads, geo.head_dim
+    shape = ts.make_shape(H, geo.num_kv_heads, b, batch.block_table.shape[1], batch.total_tokens,
+                          geo.torch_dtype)
+    cache = ts.CacheState.allocate(b, H, d, geo.top_k, geo.torch_dtype, DEV)
+    hit = torch.full((b,), -1, dtype=torch.int32, device=DEV)
+    out = torch.empty(b, H, d, dtype=geo.torch_dtype, device=DEV)
+    for theta, want_hit in ((2.0, 0), (-1.0, 1)):
+        sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, theta)
+        ws = ts.alloc_workspace(shape, sel, DEV)
+        ts.decode_step(shape, sel, batch.q, batch.k_pool, batch.v_pool, batch.block_table, batch.seq_lens,
+                       cache, hit, out, ws)
+        torch.cuda.synchronize()
+        assert hit.cpu().tolist() == [want_hit] * b
+        counts = cache.cached_count.cpu().tolist()
+        idx = cache.cached_idx.cpu().numpy()
+        for r in range(b):
+            assert np.array_equal(idx[r, :counts[r]].astype(np.int64), po.T[r]), (theta, r)
+        assert np.array_equal(gh.np32(out), po.out)
+        del ws
+
+
 def test_ragged_batch_full():
     geo = wl.workload("llama3-8b-ragged16")
     gh.log("[llama3-8b-ragged16] full lengths")
@@ -102,6 +128,7 @@ def test_ragged_batch_full():
     gh.log(f"  lens={batch.seq_lens.tolist()} total={batch.total_tokens}")
     po, st = _check_all(batch, geo)
     gh.log(f"  {st}")
+    _decode_step_matches(batch, geo, po)
 
 
 def test_llama3_1m_one_layer_full():
@@ -113,26 +140,7 @@ def test_llama3_1m_one_layer_full():
     # planted recall (the vote bound): any position with vote > H/k is selected
     big = np.nonzero(np.exp2(po.vote[0].astype(np.float64)) > geo.num_q_heads / geo.top_k)[0]
     assert np.all(np.isin(big, po.T[0]))
-    # the benchmark's configuration: one tokenselect_decode_step with theta = 2 (every
-    # step reselects) gives the checked TopK and output bit for bit, then a hit
-    # (theta = -1) reuses that TopK
-    H, d = geo.num_q_heads, geo.head_dim
-    shape = ts.make_shape(H, geo.num_kv_heads, 1, batch.block_table.shape[1], batch.total_tokens,
-                          geo.torch_dtype)
-    cache = ts.CacheState.allocate(1, H, d, geo.top_k, geo.torch_dtype, DEV)
-    hit = torch.full((1,), -1, dtype=torch.int32, device=DEV)
-    out = torch.empty(1, H, d, dtype=geo.torch_dtype, device=DEV)
-    for theta, want_hit in ((2.0, 0), (-1.0, 1)):
-        sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, theta)
-        ws = ts.alloc_workspace(shape, sel, DEV)
-        ts.decode_step(shape, sel, batch.q, batch.k_pool, batch.v_pool, batch.block_table, batch.seq_lens,
-                       cache, hit, out, ws)
-        torch.cuda.synchronize()
-        assert int(hit[0]) == want_hit
-        m = int(cache.cached_count[0])
-        assert np.array_equal(cache.cached_idx[0, :m].cpu().numpy().astype(np.int64), po.T[0])
-        assert np.array_equal(gh.np32(out[0]), po.out[0])
-        del ws
+    _decode_step_matches(batch, geo, po)
 
 
 def test_planted_recall_without_scale_spread():
