@@ -278,18 +278,25 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
       float x[kPerThread][G];
 #pragma unroll
       for (int e = 0; e < kPerThread; ++e) load_group<G>(zg, idx[e], x[e]);
+      float mh[G], lh[G];
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const float mh = s_m[g * G + j], lh = s_l[g * G + j];
+      for (int j = 0; j < G; ++j) { mh[j] = s_m[g * G + j]; lh[j] = s_l[g * G + j]; }
 #pragma unroll
-        for (int e = 0; e < kPerThread; ++e) {
-          const float xv = fmaf(x[e][j] - mh, kLog2eF, -lh);
-          // online log-sum-exp in base 2, one exp per term
-          const float d = xv - m[e];
-          const float w = fast_exp2(-fabsf(d));
-          s[e] = (d > 0.f) ? fmaf(s[e], w, 1.f) : s[e] + w;
-          m[e] = fmaxf(m[e], xv);
+      for (int e = 0; e < kPerThread; ++e) {
+        // online log-sum-exp in base 2 over the group's G terms at once: one rescale
+        // of the running sum per group, then one exp per term
+        float xv[G];
+        float gm = m[e];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          xv[j] = fmaf(x[e][j] - mh[j], kLog2eF, -lh[j]);
+          gm = fmaxf(gm, xv[j]);
         }
+        float acc = s[e] * fast_exp2(m[e] - gm);   // 0 while m is -inf (gm is finite)
+#pragma unroll
+        for (int j = 0; j < G; ++j) acc += fast_exp2(xv[j] - gm);
+        s[e] = acc;
+        m[e] = gm;
       }
     }
     float* vout = p.vote + tb.tok[r];
