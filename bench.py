@@ -171,7 +171,10 @@ def stream_ceiling(pools, steps, dev):
     return res
 
 
-def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False, ceiling=False):
+def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False, ceiling=False, then=None):
+    """Decode steps over n_layers rotating layers, then the score launches alone
+    (and the streaming probe with ceiling=True); `then(layers)`, if given, runs on
+    the same layers before they are freed and its result is returned as res["then"]."""
     import torch
     import token_level_sparse_amd as ts
     t0 = time.time()
@@ -244,19 +247,27 @@ def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False, ceiling=Fa
         f"(K stream {res['k_gbps']:.0f} GB/s)")
     if ceiling:
         res["ceiling"] = stream_ceiling([L.k_pool for L in layers], steps, dev)
+    if then is not None:
+        res["then"] = then(layers)
     host = L0.host
     del layers, ws, logits, KC, VC
     torch.cuda.empty_cache()
     return res, host
 
 
-def time_topp(geo, n_layers, steps, warmup, dev, top_p=0.9):
+def time_topp(geo, n_layers, steps, warmup, dev, top_p=0.9, layers=None):
     """Decode steps with the dynamic top-p budget (ts_select.top_p) instead of the
-    fixed TopK, every step reselecting; reports steps/s and the mean budget."""
+    fixed TopK, every step reselecting; reports steps/s and the mean budget. Given
+    `layers` (the headline's, same workload), it runs on their first n_layers pools,
+    so both figures come from the same memory."""
     import torch
     import token_level_sparse_amd as ts
-    KC, VC = kv_cache(geo, n_layers, dev)
-    layers = [Layer(geo, l, dev, False, (KC[l], VC[l])) for l in range(n_layers)]
+    KC = VC = None
+    if layers is None:
+        KC, VC = kv_cache(geo, n_layers, dev)
+        layers = [Layer(geo, l, dev, False, (KC[l], VC[l])) for l in range(n_layers)]
+    else:
+        layers = layers[:n_layers]
     L0 = layers[0]
     shape = ts.make_shape(geo.num_q_heads, geo.num_kv_heads, 1, L0.block_table.shape[1], L0.total,
                           geo.torch_dtype)
@@ -659,8 +670,10 @@ def main():
     if args.counters:
         counter_run(geo, dev)
         return
+    topp_run = None if args.no_secondary else (
+        lambda layers: time_topp(geo, 8, max(16, args.steps // 2), 4, dev, layers=layers))
     main_res, host = time_workload(geo, args.layers, args.steps, args.warmup, dev,
-                                   keep_host=not args.no_cpu_baseline, ceiling=True)
+                                   keep_host=not args.no_cpu_baseline, ceiling=True, then=topp_run)
     secondary = None
     if not args.no_secondary:
         g1 = wl.workload("llama3-8b-128k")
@@ -678,7 +691,7 @@ def main():
                            (ceil.get("read_only") or {}).get("gbps"), dev)
         ragged = time_ragged(wl.workload("llama3-8b-ragged16"), max(8, args.steps // 4), 2, dev)
         cache_seq = time_cache_sequence(wl.workload("qwen2-7b-cache256"), dev)
-        topp = time_topp(geo, 8, max(16, args.steps // 2), 4, dev)
+        topp = main_res.get("then")
         ablations = time_ablations(wl.workload("llama3-8b-128k"), dev)
         prefill = [time_prefill(wl.workload("prefill-llama3-128k"), 8, max(16, args.steps // 2), 4, dev),
                    time_prefill(wl.workload("prefill-llama3-1m"), 4, max(8, args.steps // 8), 2, dev)]
