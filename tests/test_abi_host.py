@@ -66,6 +66,18 @@ def test_stream_probe_library_exports_and_validates():
     assert f(FAKE, 4096, FAKE, 0, 0, FAKE, None) == -1          # empty grid
 
 
+def test_attention_grid_beyond_int32_rejected(lib):
+    # one attention workgroup per (request, KV head, 128 selected positions): a shape
+    # whose grid would not fit a 32-bit count is refused before any launch
+    shape = _shape(num_q_heads=256, num_kv_heads=256, batch=1024, max_total_tokens=1 << 31)
+    sel = _sel(top_k=(1 << 31) - 1, n_local=0)
+    assert lib.tokenselect_workspace_size(ctypes.byref(shape), ctypes.byref(sel)) == 0
+    st = lib.tokenselect_sparse_attn(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == ts.TS_ERR_UNSUPPORTED
+    assert "attention grid" in lib.tokenselect_last_error().decode()
+
+
 def test_workspace_size_valid_and_monotone(lib):
     a = ts.workspace_size(_shape(), _sel())
     b = ts.workspace_size(_shape(max_total_tokens=1 << 20), _sel())

@@ -121,6 +121,12 @@ ts_status check_shape(const ts_shape* s, const ts_select* sel) {
   if (sel->n_local < 0) return fail(TS_ERR_INVALID_ARG, "n_local %d < 0", sel->n_local);
   if (!(sel->top_p >= 0.0 && sel->top_p <= 1.0))
     return fail(TS_ERR_INVALID_ARG, "top_p %g outside [0, 1] (0 turns the top-p budget off)", sel->top_p);
+  // the attention grid has one workgroup per (request, KV head, slice of 128 selected
+  // or window positions)
+  const int64_t slices = (int64_t)ts::attn_splits(eff_top_k(*s, *sel), eff_local(*s, *sel));
+  if ((int64_t)s->batch * s->num_kv_heads * slices > INT32_MAX)
+    return fail(TS_ERR_UNSUPPORTED, "batch x num_kv_heads x (top_k + n_local) / 128 too large for "
+                "the attention grid");
   return TS_OK;
 }
 

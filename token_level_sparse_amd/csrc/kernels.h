@@ -131,7 +131,7 @@ __host__ __device__ inline int chunk_splits(int top_k, int n_local, int max_chun
 }
 
 __host__ __device__ inline int attn_splits(int top_k, int n_local) {
-  return (top_k + kAttnTile - 1) / kAttnTile + (n_local + kAttnTile - 1) / kAttnTile;
+  return (int)(((long long)top_k + kAttnTile - 1) / kAttnTile + ((long long)n_local + kAttnTile - 1) / kAttnTile);
 }
 
 hipError_t launch_score(const ScoreParams& p, hipStream_t s);
