@@ -33,7 +33,8 @@
  *   - Host-side validation runs before any launch. On failure nothing is
  *     launched and a non-zero ts_status is returned; tokenselect_last_error()
  *     gives a message (thread-local). A failed launch returns TS_ERR_DEVICE.
- *   - Device-side contract (not checked): every block-table entry a request
+ *   - Device-side contract (not checked by the steps; tokenselect_validate checks
+ *     it on request): every block-table entry a request
  *     reaches (pages [0, ceil(N_r / page_size))) is a valid pool page;
  *     0 <= N_r <= block_table_stride * page_size; sum of N_r <=
  *     shape.max_total_tokens; every selected index lies in [0, N_r). A request
@@ -267,6 +268,21 @@ ts_status tokenselect_select_ablation(const ts_shape* shape, const ts_select* se
                                       const int32_t* seq_lens, float* score, int32_t* sel_idx,
                                       int32_t* sel_count, void* ws, size_t ws_bytes,
                                       hipStream_t stream);
+
+/* Check of the device-side contract above, for callers that want it before a step
+   (the other entry points trust these inputs): for every request r, 0 <= N_r <=
+   block_table_stride * page_size, and every block-table entry it reaches (pages
+   [0, min(ceil(N_r / page_size), block_table_stride))) lies in [0, num_pool_pages).
+   Entries are only read, never followed. `report` (device uint64[4], caller-owned,
+   8-byte aligned) receives: [0] the number of violations, [1] the smallest key
+   (r << 32) | p over them, p the page index or 0xffffffff for a length violation
+   (all ones if there is none), [2] the number of length violations, [3] the sum of
+   the non-negative N_r (compare it with max_total_tokens). Only batch,
+   block_table_stride and page_size of `shape` are used. Asynchronous on `stream`:
+   read the report after synchronising. */
+ts_status tokenselect_validate(const ts_shape* shape, const int32_t* block_table,
+                               const int32_t* seq_lens, int64_t num_pool_pages, uint64_t* report,
+                               hipStream_t stream);
 
 /* Static text for a status code. */
 const char* tokenselect_status_string(ts_status status);

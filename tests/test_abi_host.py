@@ -78,6 +78,18 @@ def test_attention_grid_beyond_int32_rejected(lib):
     assert "attention grid" in lib.tokenselect_last_error().decode()
 
 
+def test_validate_arguments_checked_before_launch(lib):
+    shape = _shape(batch=4, block_table_stride=64)
+    f = lib.tokenselect_validate
+    assert f(None, FAKE, FAKE, 100, FAKE, None) == ts.TS_ERR_INVALID_ARG
+    assert f(ctypes.byref(shape), None, FAKE, 100, FAKE, None) == ts.TS_ERR_INVALID_ARG
+    assert "block_table" in lib.tokenselect_last_error().decode()
+    assert f(ctypes.byref(shape), FAKE, FAKE, 0, FAKE, None) == ts.TS_ERR_INVALID_ARG
+    assert f(ctypes.byref(shape), FAKE, FAKE, 100, ctypes.c_void_p(4100), None) == ts.TS_ERR_INVALID_ARG
+    bad = _shape(batch=0)
+    assert f(ctypes.byref(bad), FAKE, FAKE, 100, FAKE, None) == ts.TS_ERR_INVALID_ARG
+
+
 def test_workspace_size_valid_and_monotone(lib):
     a = ts.workspace_size(_shape(), _sel())
     b = ts.workspace_size(_shape(max_total_tokens=1 << 20), _sel())

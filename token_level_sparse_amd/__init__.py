@@ -34,6 +34,7 @@ ENTRY_POINTS = (
     "tokenselect_prefill_chunk",
     "tokenselect_ablation_workspace_size",
     "tokenselect_select_ablation",
+    "tokenselect_validate",
     "tokenselect_status_string",
     "tokenselect_last_error",
 )
@@ -118,6 +119,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tokenselect_ablation_workspace_size.restype = sz
     lib.tokenselect_select_ablation.argtypes = [sp, selp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tokenselect_select_ablation.restype = ctypes.c_int
+    lib.tokenselect_validate.argtypes = [sp, vp, vp, ctypes.c_int64, vp, vp]
+    lib.tokenselect_validate.restype = ctypes.c_int
     lib.tokenselect_status_string.argtypes = [ctypes.c_int]
     lib.tokenselect_status_string.restype = ctypes.c_char_p
     lib.tokenselect_last_error.argtypes = []
@@ -294,3 +297,16 @@ def select_ablation(shape, sel, fn, block, logits, head_stats, seq_lens, score, 
                                            _ptr(logits), _ptr(head_stats), _ptr(seq_lens), _ptr(score),
                                            _ptr(sel_idx), _ptr(sel_count), _ptr(ws), ws.numel(),
                                            _stream(stream)))
+
+
+# ---------------------------------------------------------------- input checks
+def validate(shape, block_table, seq_lens, num_pool_pages: int, report=None, stream=None) -> torch.Tensor:
+    """tokenselect_validate: returns the device report (int64 [4]: violations, first
+    (request << 32 | page) key, length violations, sum of lengths); read it after
+    synchronising. `report` may be given to reuse a buffer."""
+    lib = load_library()
+    if report is None:
+        report = torch.empty(4, dtype=torch.int64, device=seq_lens.device)
+    _check(lib.tokenselect_validate(ctypes.byref(shape), _ptr(block_table), _ptr(seq_lens),
+                                    int(num_pool_pages), _ptr(report), _stream(stream)))
+    return report

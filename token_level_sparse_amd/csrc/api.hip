@@ -594,6 +594,26 @@ ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel, c
   return device_status(ts::launch_attn(ap, stream), "sparse attention launch");
 }
 
+ts_status tokenselect_validate(const ts_shape* shape, const int32_t* block_table,
+                               const int32_t* seq_lens, int64_t num_pool_pages, uint64_t* report,
+                               hipStream_t stream) {
+  if (!shape) return fail(TS_ERR_INVALID_ARG, "shape must not be NULL");
+  TS_REQUIRE(block_table); TS_REQUIRE(seq_lens); TS_REQUIRE(report);
+  if (shape->batch < 1 || shape->batch > ts::kMaxBatch)
+    return fail(TS_ERR_INVALID_ARG, "batch %d outside [1, %d]", shape->batch, ts::kMaxBatch);
+  if (shape->block_table_stride < 1)
+    return fail(TS_ERR_INVALID_ARG, "block_table_stride %d < 1", shape->block_table_stride);
+  if (shape->page_size != ts::kPage)
+    return fail(TS_ERR_UNSUPPORTED, "page_size %d != 16", shape->page_size);
+  if (num_pool_pages < 1) return fail(TS_ERR_INVALID_ARG, "num_pool_pages %lld < 1", (long long)num_pool_pages);
+  if (reinterpret_cast<uintptr_t>(report) % 8) return fail(TS_ERR_INVALID_ARG, "report must be 8-byte aligned");
+  ts::ValidateParams p{};
+  p.block_table = block_table; p.seq_lens = seq_lens; p.b = shape->batch;
+  p.stride = shape->block_table_stride; p.pool_pages = num_pool_pages;
+  p.report = reinterpret_cast<unsigned long long*>(report);
+  return device_status(ts::launch_validate(p, stream), "validate launch");
+}
+
 const char* tokenselect_status_string(ts_status s) {
   switch (s) {
     case TS_OK: return "ok";

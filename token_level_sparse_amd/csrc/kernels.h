@@ -164,6 +164,16 @@ hipError_t launch_count_votes(const AblationParams& p, hipStream_t s);
 hipError_t launch_block_scores(const AblationParams& p, hipStream_t s);
 hipError_t launch_expand_blocks(const AblationParams& p, hipStream_t s);
 
+// Input checks (tokenselect_validate).
+struct ValidateParams {
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int b, stride;
+  int64_t pool_pages;
+  unsigned long long* report;   // [4]
+};
+hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
+
 hipError_t launch_chunk_mean(const ChunkParams& p, hipStream_t s);
 hipError_t launch_chunk_attn(const ChunkParams& p, hipStream_t s);
 
