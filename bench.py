@@ -631,6 +631,25 @@ def cpu_baseline(geo, host, min_seconds=10.0, max_steps=30):
                       f"{geo.name} (N={K.shape[1]}), {dt:.1f} s of host work"}
 
 
+def guarded(name, fn):
+    """Run a secondary section. A Python-level failure is logged with its traceback
+    and reported as {"error": ...} in that section's field instead of ending the run,
+    so the headline line is always printed."""
+    try:
+        return fn()
+    except Exception as e:  # noqa: BLE001 - any failure of a secondary section
+        import traceback
+        log(f"[{name}] failed: {e!r}")
+        traceback.print_exc(file=sys.stderr)
+        try:
+            import torch
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        except Exception:  # noqa: BLE001
+            pass
+        return {"error": repr(e)}
+
+
 def ceiling_line(res):
     """The scoring launch against the probe's measured ceilings on the same pools."""
     c = res.get("ceiling")
@@ -671,31 +690,37 @@ def main():
         counter_run(geo, dev)
         return
     topp_run = None if args.no_secondary else (
-        lambda layers: time_topp(geo, 8, max(16, args.steps // 2), 4, dev, layers=layers))
+        lambda layers: guarded("top_p", lambda: time_topp(geo, 8, max(16, args.steps // 2), 4, dev,
+                                                            layers=layers)))
     main_res, host = time_workload(geo, args.layers, args.steps, args.warmup, dev,
                                    keep_host=not args.no_cpu_baseline, ceiling=True, then=topp_run)
     secondary = None
     if not args.no_secondary:
-        g1 = wl.workload("llama3-8b-128k")
-        # 8 rotating layers: 8 x 256 MiB of K, so no step finds its pool in the 256 MB MALL
-        r1, _ = time_workload(g1, 8, max(args.steps, 32), args.warmup, dev)
-        secondary = {"workload": g1.name, "N": g1.seq_len, "decode_steps_per_s": 1e3 / r1["ms_per_step"],
-                     "ms_per_step": r1["ms_per_step"],
-                     "step_ms_percentiles": {q: r1[f"step_ms_p{q}"] for q in (10, 50, 90)},
-                     "score_ms": r1["score_ms"],
-                     "score_gbps": r1["score_gbps"], "k_gbps": r1["k_gbps"], "rotating_layers": 8}
+        def run_128k():
+            g1 = wl.workload("llama3-8b-128k")
+            # 8 rotating layers: 8 x 256 MiB of K, so no step finds its pool in the 256 MB MALL
+            r1, _ = time_workload(g1, 8, max(args.steps, 32), args.warmup, dev)
+            return {"workload": g1.name, "N": g1.seq_len, "decode_steps_per_s": 1e3 / r1["ms_per_step"],
+                    "ms_per_step": r1["ms_per_step"],
+                    "step_ms_percentiles": {q: r1[f"step_ms_p{q}"] for q in (10, 50, 90)},
+                    "score_ms": r1["score_ms"],
+                    "score_gbps": r1["score_gbps"], "k_gbps": r1["k_gbps"], "rotating_layers": 8}
+        secondary = guarded("llama3-8b-128k", run_128k)
     ragged = cache_seq = prefill = topp = ablations = dense = None
     if not args.no_secondary:
         ceil = main_res.get("ceiling") or {}
-        dense = time_dense(geo, main_res["ms_per_step"],
-                           (ceil.get("read_only") or {}).get("gbps"), dev)
-        ragged = time_ragged(wl.workload("llama3-8b-ragged16"), max(8, args.steps // 4), 2, dev)
-        cache_seq = time_cache_sequence(wl.workload("qwen2-7b-cache256"), dev)
+        dense = guarded("dense", lambda: time_dense(geo, main_res["ms_per_step"],
+                                                    (ceil.get("read_only") or {}).get("gbps"), dev))
+        ragged = guarded("ragged", lambda: time_ragged(wl.workload("llama3-8b-ragged16"),
+                                                       max(8, args.steps // 4), 2, dev))
+        cache_seq = guarded("selection_cache", lambda: time_cache_sequence(wl.workload("qwen2-7b-cache256"), dev))
         topp = main_res.get("then")
-        ablations = time_ablations(wl.workload("llama3-8b-128k"), dev)
-        prefill = [time_prefill(wl.workload("prefill-llama3-128k"), 8, max(16, args.steps // 2), 4, dev),
-                   time_prefill(wl.workload("prefill-llama3-1m"), 4, max(8, args.steps // 8), 2, dev)]
-    cpu = cpu_baseline(geo, host) if host is not None else None
+        ablations = guarded("ablations", lambda: time_ablations(wl.workload("llama3-8b-128k"), dev))
+        prefill = [guarded("prefill-128k", lambda: time_prefill(wl.workload("prefill-llama3-128k"), 8,
+                                                                 max(16, args.steps // 2), 4, dev)),
+                   guarded("prefill-1m", lambda: time_prefill(wl.workload("prefill-llama3-1m"), 4,
+                                                               max(8, args.steps // 8), 2, dev))]
+    cpu = guarded("cpu_baseline", lambda: cpu_baseline(geo, host)) if host is not None else None
 
     ms = main_res["ms_per_step"]
     line = {
