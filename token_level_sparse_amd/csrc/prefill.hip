@@ -27,10 +27,14 @@
 //     products, so the gather latency overlaps the matrix work);
 //   * S^T = K Q^T on MFMA (A = 32 keys x 16 dims from LDS, B = the wave's queries
 //     held in registers), so a lane ends with 16 keys of one row: row = lane % 32;
-//   * online softmax in base 2 per row (row max across the 2 lane halves);
+//   * online softmax in base 2 per row (row max across the 2 lane halves); in bf16
+//     the exp2 of block n runs between the MFMAs of block n + 1's scores, so the
+//     VALU and the matrix cores work at the same time inside one wave;
 //   * O^T += V^T P^T on MFMA: the lane's probabilities are already the B operand
 //     (row = lane % 32, 8 keys per step), with the key order of the A operand (V^T
 //     rows from LDS) permuted to match, so P never leaves registers.
+// The staging registers are clang vector types: with HIP's struct vector types the
+// compiler kept them in scratch memory, and each block then waited for its prefetch.
 // bf16 uses v_mfma_f32_32x32x16_bf16 on 64-key blocks (accumulators in VGPRs, two
 // waves per SIMD); fp32 uses v_mfma_f32_16x16x4_f32 on 32-key blocks with 16-row
 // waves and the same index and mask logic.
@@ -142,13 +146,13 @@ template <> struct Tile<true> {
   static constexpr int kKStride = kHeadDim + 8;    // bf16 elements per K row in LDS
   static constexpr int kVStride = 64 + 4;          // bf16 elements per V^T row in LDS
   static constexpr int kLds = kKeys * kKStride * 2 + kHeadDim * kVStride * 2;
-  uint4 k[4], v[4];                                // staging registers: 4 keys x 8 dims
+  u32x4_t k[4], v[4];                              // staging registers: 4 keys x 8 dims
 };
 template <> struct Tile<false> {
   static constexpr int kKeys = 32;
   static constexpr int kStride = kHeadDim + 4;     // floats per K / V row in LDS
   static constexpr int kLds = 2 * kKeys * kStride * 4;
-  float4 k[4], v[4];                               // staging registers: 1 key x 16 dims
+  f32x4_t k[4], v[4];                              // staging registers: 1 key x 16 dims
 };
 
 struct KeyMap {
@@ -160,36 +164,37 @@ struct KeyMap {
 // K: thread t stages dims 8 (t % 16) + [0, 8) of keys 4 (t / 16) + [0, 4).
 // V: thread t stages dims 8 (t / 16) + [0, 8) of keys 4 (t % 16) + [0, 4), so that
 // the transposed writes of a 32-lane group fill two whole V^T rows (no bank conflict).
-__device__ __forceinline__ void stage_load(Tile<true>& t, const uint16_t* kp, const uint16_t* vp,
-                                           const KeyMap& km, int x0) {
+// K and V of a block are staged separately: the loop keeps K one block ahead of V.
+__device__ __forceinline__ void stage_load_k(Tile<true>& t, const uint16_t* kp, const KeyMap& km, int x0) {
   const int kq = threadIdx.x >> 4, dc = threadIdx.x & 15;
-  const int vq = threadIdx.x & 15, vc = threadIdx.x >> 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    t.k[i] = *reinterpret_cast<const uint4*>(kp + km.row(x0 + 4 * kq + i) + 8 * dc);
-    t.v[i] = *reinterpret_cast<const uint4*>(vp + km.row(x0 + 4 * vq + i) + 8 * vc);
-  }
+  for (int i = 0; i < 4; ++i)
+    t.k[i] = *reinterpret_cast<const u32x4_t*>(kp + km.row(x0 + 4 * kq + i) + 8 * dc);
 }
-__device__ __forceinline__ void stage_store(const Tile<true>& t, char* lds) {
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(lds);
-  uint16_t* Vt = Ks + Tile<true>::kKeys * Tile<true>::kKStride;
-  const int kq = threadIdx.x >> 4, dc = threadIdx.x & 15;
+__device__ __forceinline__ void stage_load_v(Tile<true>& t, const uint16_t* vp, const KeyMap& km, int x0) {
   const int vq = threadIdx.x & 15, vc = threadIdx.x >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint4*>(Ks + (4 * kq + i) * Tile<true>::kKStride + 8 * dc) = t.k[i];
+    t.v[i] = *reinterpret_cast<const u32x4_t*>(vp + km.row(x0 + 4 * vq + i) + 8 * vc);
+}
+__device__ __forceinline__ void stage_store_k(const Tile<true>& t, char* lds) {
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(lds);
+  const int kq = threadIdx.x >> 4, dc = threadIdx.x & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<u32x4_t*>(Ks + (4 * kq + i) * Tile<true>::kKStride + 8 * dc) = t.k[i];
+}
+__device__ __forceinline__ void stage_store_v(const Tile<true>& t, char* lds) {
+  uint16_t* Vt = reinterpret_cast<uint16_t*>(lds) + Tile<true>::kKeys * Tile<true>::kKStride;
+  const int vq = threadIdx.x & 15, vc = threadIdx.x >> 4;
   // V^T[d][key]: for each of the 8 dims, the 4 keys' values packed into 8 bytes. One
   // byte permute joins the same 16-bit half of two keys' words (v_perm_b32: selector
   // bytes 0-3 pick from the second operand, 4-7 from the first).
-  const uint32_t w[4][4] = {{t.v[0].x, t.v[0].y, t.v[0].z, t.v[0].w},
-                            {t.v[1].x, t.v[1].y, t.v[1].z, t.v[1].w},
-                            {t.v[2].x, t.v[2].y, t.v[2].z, t.v[2].w},
-                            {t.v[3].x, t.v[3].y, t.v[3].z, t.v[3].w}};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-    const uint32_t k01 = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
-    const uint32_t k23 = __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel);
+    const uint32_t k01 = __builtin_amdgcn_perm(t.v[1][e >> 1], t.v[0][e >> 1], sel);
+    const uint32_t k23 = __builtin_amdgcn_perm(t.v[3][e >> 1], t.v[2][e >> 1], sel);
     *reinterpret_cast<uint2*>(Vt + (8 * vc + e) * Tile<true>::kVStride + 4 * vq) = make_uint2(k01, k23);
   }
 }
@@ -199,8 +204,8 @@ __device__ __forceinline__ void stage_load(Tile<false>& t, const float* kp, cons
   const int64_t off = km.row(x0 + key) + 16 * dq;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    t.k[m] = *reinterpret_cast<const float4*>(kp + off + 4 * m);
-    t.v[m] = *reinterpret_cast<const float4*>(vp + off + 4 * m);
+    t.k[m] = *reinterpret_cast<const f32x4_t*>(kp + off + 4 * m);
+    t.v[m] = *reinterpret_cast<const f32x4_t*>(vp + off + 4 * m);
   }
 }
 __device__ __forceinline__ void stage_store(const Tile<false>& t, char* lds) {
@@ -209,8 +214,8 @@ __device__ __forceinline__ void stage_store(const Tile<false>& t, char* lds) {
   const int key = threadIdx.x >> 3, dq = threadIdx.x & 7;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    *reinterpret_cast<float4*>(Ks + key * Tile<false>::kStride + 16 * dq + 4 * m) = t.k[m];
-    *reinterpret_cast<float4*>(Vs + key * Tile<false>::kStride + 16 * dq + 4 * m) = t.v[m];
+    *reinterpret_cast<f32x4_t*>(Ks + key * Tile<false>::kStride + 16 * dq + 4 * m) = t.k[m];
+    *reinterpret_cast<f32x4_t*>(Vs + key * Tile<false>::kStride + 16 * dq + 4 * m) = t.v[m];
   }
 }
 
@@ -417,83 +422,122 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
 
-  // The block products: scores, online softmax, O^T += V^T P^T over the block staged at lds.
-  auto block = [&](const char* lds, int x0) {
-      f32x16_t s[2];                        // scores, then probabilities, in place
-      qk_block32(lds, q, l32, lg, s);
-      // Wave-uniform: every key of the block is visible to every row of the wave. Then
-      // the block maximum is taken on the raw scores (scaling by sl2 > 0 commutes with
-      // the rounded max) and each probability is one exp2 of an fma; the running maximum
-      // is finite after the rescale test, so no -inf guard is needed.
-      const bool full = x0 + KB <= w.x_end && x0 + KB - 1 <= wave_lim;
-      float mloc = kNegInf;
-      if (full) {
-  #pragma unroll
-        for (int t = 0; t < 2; ++t)
-  #pragma unroll
-          for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[t][i]);
-        mloc *= sl2;
-      } else {
-  #pragma unroll
-        for (int t = 0; t < 2; ++t)
-  #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int x = x0 + 32 * t + 8 * (i >> 2) + 4 * lg + (i & 3);
-            s[t][i] = (x < w.x_end && x <= lim) ? s[t][i] * sl2 : kNegInf;
-            mloc = fmaxf(mloc, s[t][i]);
-          }
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-        m_run = m_new;
-  #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-      }
-      float psum = 0.f;
-      if (full) {
-        const float nm = -m_run;
-  #pragma unroll
-        for (int t = 0; t < 2; ++t)
-  #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            s[t][i] = fast_exp2(fmaf(s[t][i], sl2, nm));
-            psum += s[t][i];
-          }
-      } else {
-  #pragma unroll
-        for (int t = 0; t < 2; ++t)
-  #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            s[t][i] = (s[t][i] == kNegInf) ? 0.f : fast_exp2(s[t][i] - m_run);
-            psum += s[t][i];
-          }
-      }
-      l_run += psum;
-      pv_block32(lds, s, l32, lg, o);
+  // Online softmax of one block, first half: the block maximum and the rescale of the
+  // running state. Returns whether every key of the block is visible to every row of
+  // the wave (wave-uniform); then the scores stay raw (the maximum is taken on them:
+  // scaling by sl2 > 0 commutes with the rounded max), otherwise they are scaled, with
+  // -inf where masked.
+  auto soft_max = [&](f32x16_t (&s)[2], int x0) -> bool {
+    const bool full = x0 + KB <= w.x_end && x0 + KB - 1 <= wave_lim;
+    float mloc = kNegInf;
+    if (full) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[t][i]);
+      mloc *= sl2;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int x = x0 + 32 * t + 8 * (i >> 2) + 4 * lg + (i & 3);
+          s[t][i] = (x < w.x_end && x <= lim) ? s[t][i] * sl2 : kNegInf;
+          mloc = fmaxf(mloc, s[t][i]);
+        }
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    }
+    return full;
   };
 
-  // Two LDS buffers, one barrier per block: block n is read from one buffer while
-  // block n + 1, already in the staging registers, is written to the other after the
-  // products; the loads of block n + 2 then overlap the next block's products.
+  // Second half, fused with the scores of the next block: the probabilities of block n
+  // (in place in cur) are computed between the MFMAs of S_{n+1} = K_{n+1} Q^T (into nxt,
+  // from the K buffer kb), so the matrix cores and the VALU work at the same time. In a
+  // fully visible block every probability is one exp2 of an fma and the running
+  // maximum is finite, so no -inf guard is needed.
+  auto exp_qk = [&](auto full_c, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], const char* kb) {
+    constexpr bool kFull = decltype(full_c)::value;
+    const uint16_t* Ks = reinterpret_cast<const uint16_t*>(kb);
+    const float nm = -m_run;
+    f32x16_t a0 = {}, a1 = {};
+    float psum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(Ks + l32 * Tile<true>::kKStride + 16 * ks + 8 * lg);
+      const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(Ks + (32 + l32) * Tile<true>::kKStride + 16 * ks + 8 * lg);
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q.v[ks], a0, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float x = cur[ks >> 2][4 * (ks & 3) + e];
+        const float pr = kFull ? fast_exp2(fmaf(x, sl2, nm)) : ((x == kNegInf) ? 0.f : fast_exp2(x - m_run));
+        cur[ks >> 2][4 * (ks & 3) + e] = pr;
+        psum += pr;
+      }
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q.v[ks], a1, 0, 0, 0);
+#pragma unroll
+      for (int e = 2; e < 4; ++e) {
+        const float x = cur[ks >> 2][4 * (ks & 3) + e];
+        const float pr = kFull ? fast_exp2(fmaf(x, sl2, nm)) : ((x == kNegInf) ? 0.f : fast_exp2(x - m_run));
+        cur[ks >> 2][4 * (ks & 3) + e] = pr;
+        psum += pr;
+      }
+    }
+    nxt[0] = a0;
+    nxt[1] = a1;
+    l_run += psum;
+  };
+
+  // Software pipeline, one barrier per block: the scores of block n + 1 go to the
+  // matrix cores before block n's softmax, so the two overlap within the wave. Block m
+  // keeps K in buffer m % 2 and V^T in buffer m % 2, with K staged one block ahead:
+  // entering iteration n, S_n is in registers, K_{n+1} and V_n are in LDS, and the
+  // staging registers hold K_{n+2} and V_{n+1}. Iteration n writes K_{n+2} over K_n
+  // (read in iteration n - 1) and V_{n+1} over V_{n-1} (read in iteration n - 1).
   char* buf0 = s_lds;
   char* buf1 = s_lds + Tile<true>::kLds;
+  const int nb = (w.x_end - w.x_begin + KB - 1) / KB;
   Tile<true> st;
-  stage_load(st, kp, vp, w.km, w.x_begin);
-  stage_store(st, buf0);
-  if (w.x_begin + KB < w.x_end) stage_load(st, kp, vp, w.km, w.x_begin + KB);
+  stage_load_k(st, kp, w.km, w.x_begin);
+  stage_load_v(st, vp, w.km, w.x_begin);
+  stage_store_k(st, buf0);
+  stage_store_v(st, buf0);
+  if (nb > 1) {
+    stage_load_k(st, kp, w.km, w.x_begin + KB);
+    stage_load_v(st, vp, w.km, w.x_begin + KB);
+  }
   __syncthreads();
-  int cur = 0;
-  for (int x0 = w.x_begin; x0 < w.x_end; x0 += KB) {
-    block(cur ? buf1 : buf0, x0);
-    if (x0 + KB < w.x_end) {
-      stage_store(st, cur ? buf0 : buf1);   // every wave finished reading it before the last barrier
-      if (x0 + 2 * KB < w.x_end) stage_load(st, kp, vp, w.km, x0 + 2 * KB);
-    }
+  f32x16_t sa[2], sb[2];
+  qk_block32(buf0, q, l32, lg, sa);
+  if (nb > 1) {
+    stage_store_k(st, buf1);
+    if (nb > 2) stage_load_k(st, kp, w.km, w.x_begin + 2 * KB);
+  }
+  __syncthreads();
+  auto step = [&](int n, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+    const int x0 = w.x_begin + n * KB;
+    char* bn = (n & 1) ? buf1 : buf0;
+    char* bn1 = (n & 1) ? buf0 : buf1;
+    // S_{n+1} is computed even past the last block (from stale, in-bounds LDS) and unused
+    if (soft_max(cur, x0)) exp_qk(std::true_type{}, cur, nxt, bn1);
+    else exp_qk(std::false_type{}, cur, nxt, bn1);
+    pv_block32(bn, cur, l32, lg, o);
+    if (n + 2 < nb) stage_store_k(st, bn);
+    if (n + 1 < nb) stage_store_v(st, bn1);
+    if (n + 3 < nb) stage_load_k(st, kp, w.km, x0 + 3 * KB);
+    if (n + 2 < nb) stage_load_v(st, vp, w.km, x0 + 2 * KB);
     __syncthreads();
-    cur ^= 1;
+  };
+  for (int n = 0; n < nb; n += 2) {
+    step(n, sa, sb);
+    if (n + 1 < nb) step(n + 1, sb, sa);
   }
 
   const float lt = l_run + __shfl_xor(l_run, 32);
