@@ -221,7 +221,7 @@ ts::AttnParams attn_params(const ts_shape& s, const ts_select& sel, const void* 
 // ---------------------------------------------------------------- prefill
 struct PrefillLayout {
   Layout dec;                  // the decode regions, used by the selection over the past
-  size_t qbar, past, cpart, total;
+  size_t qbar, past, kbase, cpart, total;
 };
 
 int chunk_splits_for(const ts_shape& s, const ts_select& sel, int max_chunk) {
@@ -239,6 +239,7 @@ PrefillLayout prefill_layout(const ts_shape& s, const ts_select& sel, int max_ch
   const size_t bH = (size_t)s.batch * s.num_q_heads;
   L.qbar = off;  off += align_up(sizeof(float) * bH * ts::kHeadDim);
   L.past = off;  off += align_up(sizeof(int32_t) * (size_t)s.batch);
+  L.kbase = off; off += align_up(sizeof(int32_t) * (size_t)s.batch);
   L.cpart = off; off += align_up(sizeof(float) * bH * (size_t)max_chunk *
                                  chunk_splits_for(s, sel, max_chunk) * ts::kChunkPartStride);
   L.total = off;
@@ -283,6 +284,7 @@ ts::ChunkParams chunk_params(const ts_shape& s, const ts_select& sel, int max_ch
   p.q = q; p.chunk_lens = chunk_lens; p.seq_lens = seq; p.k_pool = k_pool; p.v_pool = v_pool;
   p.block_table = bt; p.sel_idx = sel_idx; p.sel_count = sel_count;
   p.qbar = at<float>(ws, L.qbar); p.past_lens = at<int32_t>(ws, L.past);
+  p.key_base = at<int32_t>(ws, L.kbase);
   p.partials = at<float>(ws, L.cpart); p.out = out;
   p.H = s.num_q_heads; p.Hkv = s.num_kv_heads; p.b = s.batch; p.stride = s.block_table_stride;
   p.max_chunk = max_chunk; p.sel_stride = sel.top_k; p.n_local = sel.n_local;

@@ -115,6 +115,7 @@ struct ChunkParams {
   const int32_t* sel_count;   // [b]
   float* qbar;                // [b][H][d] fp32 mean query (output of the mean kernel)
   int32_t* past_lens;         // [b] P_r (output of the mean kernel)
+  int32_t* key_base;          // [b] entries before the chunk's own keys (written by the attention kernel)
   float* partials;            // [b][max_chunk][H][splits][kChunkPartStride]
   void* out;                  // [b][max_chunk][H][d]
   int H, Hkv, b, stride, max_chunk, sel_stride, n_local, splits;

@@ -339,6 +339,8 @@ __device__ bool chunk_unit(const ChunkParams& p, int rows_per_wg, int* s_geom, i
   if (threadIdx.x == 0) {
     const ChunkGeom gm = chunk_geom(p, w.r, true);
     s_geom[0] = gm.c; s_geom[1] = gm.base; s_geom[2] = gm.w0; s_geom[3] = gm.n_sel; s_geom[4] = gm.N;
+    // for the combine kernel (every workgroup of the request writes the same value)
+    if (w.split == 0 && tile == 0) p.key_base[w.r] = gm.base;
   }
   __syncthreads();
   const int c = s_geom[0];
@@ -637,22 +639,28 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkParams p) {
   const int h = (int)(row % p.H);
   const int j = (int)((row / p.H) % p.max_chunk);
   const int r = (int)(row / ((int64_t)p.H * p.max_chunk));
-  const ChunkGeom gm = chunk_geom(p, r, true);
+  const ChunkGeom gm = chunk_geom(p, r, false);
   if (j >= gm.c) return;
-  const int S = min(p.splits, (gm.base + j + kChunkSplitKeys) / kChunkSplitKeys);
+  // splits that hold entries visible to chunk query j (the attention kernel stored the
+  // request's key-list base, so no search of the TopK list here)
+  const int S = min(p.splits, (p.key_base[r] + j + kChunkSplitKeys) / kChunkSplitKeys);
   const int d4 = 4 * (threadIdx.x & 31);
   const float* src = p.partials + row * p.splits * kPartStride;
-  float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, src[s * kPartStride + kHeadDim]);
-  float L = 0.f;
+  // one pass: the splits' loads are independent, the merge keeps a running maximum
+  float M = kNegInf, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
   for (int s = 0; s < S; ++s) {
     const float ms = src[s * kPartStride + kHeadDim];
-    const float w = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
-    L = fmaf(w, src[s * kPartStride + kHeadDim + 1], L);
+    const float ls = src[s * kPartStride + kHeadDim + 1];
     const float4 o = *reinterpret_cast<const float4*>(src + s * kPartStride + d4);
-    acc.x = fmaf(w, o.x, acc.x); acc.y = fmaf(w, o.y, acc.y);
-    acc.z = fmaf(w, o.z, acc.z); acc.w = fmaf(w, o.w, acc.w);
+    const float Mn = fmaxf(M, ms);
+    const float a = (M == kNegInf) ? 0.f : fast_exp2(M - Mn);     // rescale of the running sums
+    const float w = (ms == kNegInf) ? 0.f : fast_exp2(ms - Mn);
+    L = fmaf(w, ls, L * a);
+    acc.x = fmaf(w, o.x, acc.x * a); acc.y = fmaf(w, o.y, acc.y * a);
+    acc.z = fmaf(w, o.z, acc.z * a); acc.w = fmaf(w, o.w, acc.w * a);
+    M = Mn;
   }
   const float inv = 1.f / L;
   const int64_t oi = row * kHeadDim + d4;
