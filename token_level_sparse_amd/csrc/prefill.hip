@@ -91,12 +91,16 @@ __device__ ChunkGeom chunk_geom(const ChunkParams& p, int r, bool with_sel) {
 // One workgroup of 1024 threads per (request, head): qbar = (sum_j q_j) / c with the
 // sum in fp64 (exact for bf16 queries of ordinary range), rounded once to fp32.
 // Thread t owns dims 8 (t % 16) + [0, 8) of rows j = t / 16 (mod 64): 16-byte loads,
-// 64 rows in flight per pass, then an LDS sum over the 64 row groups.
+// 64 rows in flight per pass; then the 64 row groups are added in LDS in two levels
+// (8 slices of 8 groups, then the 8 slices), so no thread adds 64 values in a chain.
 constexpr int kMeanThreads = 1024;
 constexpr int kMeanGroups = kMeanThreads / 16;
+constexpr int kMeanSlices = kMeanThreads / kHeadDim;
+static_assert(kMeanGroups % kMeanSlices == 0, "row groups split evenly over the slices");
 template <bool kBf16>
 __global__ __launch_bounds__(kMeanThreads) void chunk_mean_kernel(ChunkParams p) {
-  __shared__ double s_acc[kMeanGroups][kHeadDim / 2];     // two passes of 64 dims
+  __shared__ double s_acc[kMeanGroups][kHeadDim];
+  __shared__ double s_part[kMeanSlices][kHeadDim];
   const int r = blockIdx.x / p.H, h = blockIdx.x - (blockIdx.x / p.H) * p.H;
   const ChunkGeom gm = chunk_geom(p, r, false);
   const int dc = threadIdx.x & 15, rg = threadIdx.x >> 4;
@@ -121,20 +125,23 @@ __global__ __launch_bounds__(kMeanThreads) void chunk_mean_kernel(ChunkParams p)
       acc[4] += (double)x1.x; acc[5] += (double)x1.y; acc[6] += (double)x1.z; acc[7] += (double)x1.w;
     }
   }
-  // dims [0, 64) then [64, 128): threads with dc < 8, then dc >= 8, publish
-  for (int half = 0; half < 2; ++half) {
-    if ((dc >> 3) == half) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[rg][8 * (dc & 7) + e] = acc[e];
-    }
-    __syncthreads();
-    if (threadIdx.x < kHeadDim / 2) {
-      double t = 0.0;
-      for (int g = 0; g < kMeanGroups; ++g) t += s_acc[g][threadIdx.x];
-      p.qbar[((int64_t)r * p.H + h) * kHeadDim + 64 * half + threadIdx.x] =
-          (float)(t / (double)max(gm.c, 1));
-    }
-    __syncthreads();
+  for (int e = 0; e < 8; ++e) s_acc[rg][8 * dc + e] = acc[e];
+  __syncthreads();
+  {
+    const int d = threadIdx.x % kHeadDim, sl = threadIdx.x / kHeadDim;
+    constexpr int kPer = kMeanGroups / kMeanSlices;
+    double t = 0.0;
+#pragma unroll
+    for (int g = 0; g < kPer; ++g) t += s_acc[kPer * sl + g][d];
+    s_part[sl][d] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < kHeadDim) {
+    double t = 0.0;
+#pragma unroll
+    for (int sl = 0; sl < kMeanSlices; ++sl) t += s_part[sl][threadIdx.x];
+    p.qbar[((int64_t)r * p.H + h) * kHeadDim + threadIdx.x] = (float)(t / (double)max(gm.c, 1));
   }
   if (h == 0 && threadIdx.x == 0) p.past_lens[r] = gm.P;
 }
