@@ -68,7 +68,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   const int g = rg % p.Hkv;
   const int r = rg / p.Hkv;
   const int H = p.H;
+  // The request's length, its TopK count and this lane's TopK entry are independent
+  // loads, all issued before any of them is used (the entry is read within the row).
+  const int e_sel = min(s * kAttnTile + wave * kAttnSplit + (lane & (kAttnSplit - 1)), p.sel_stride - 1);
+  const int cand = (s < nT) ? p.sel_idx[(int64_t)r * p.sel_stride + e_sel] : 0;
   const int N = p.seq_lens[r];
+  const int cnt = (s < nT) ? min(p.sel_count[r], p.sel_stride) : 0;
   const int lstart = max(0, N - p.n_local);
 
   // Token of this wave's slot e = lane (lanes 0..31), then broadcast by shuffle.
@@ -77,8 +82,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   if (lane < kAttnSplit) {
     if (s < nT) {
       const int e = s * kAttnTile + wave * kAttnSplit + lane;
-      if (e < min(p.sel_count[r], p.sel_stride)) {
-        tok = p.sel_idx[(int64_t)r * p.sel_stride + e];
+      if (e < cnt) {
+        tok = cand;
         ok = tok >= 0 && tok < lstart;
       }
     } else {
