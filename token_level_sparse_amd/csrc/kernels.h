@@ -97,7 +97,7 @@ struct AttnParams {
 // runs over a gathered key list: the TopK positions below the window start
 // w0 = max(0, P_r - L) (n_sel of them), then the contiguous range
 // [w0, P_r + c_r); query j sees the first base + j + 1 entries, base = n_sel + P_r - w0.
-constexpr int kChunkRows = 64;        // fewest (query, head) rows per attention workgroup (fp32; bf16 128)
+constexpr int kChunkRows = 64;        // fewest (query, head) rows per attention workgroup (fp32; bf16 256)
 #ifndef TS_CHUNK_SPLIT_KEYS
 #define TS_CHUNK_SPLIT_KEYS 1024
 #endif

@@ -18,10 +18,11 @@
 // That is a causal attention with a key offset over an index-mapped paged pool, a
 // dense contraction of c*G rows by ~k+L+c keys, so it runs on the matrix cores.
 //
-// gfx950 design. A workgroup owns 128 (query, head) rows of one (request, KV head)
+// gfx950 design. A workgroup owns 256 (query, head) rows of one (request, KV head)
 // (64 for fp32): row = j * G + head-in-group, so one staged key block serves all G
-// heads of the group. Each of the 4 waves owns 32 rows (16 for fp32), so every K and
-// V fragment a wave reads from LDS feeds 32 rows. Per block of keys:
+// heads of the group. Each of the 8 waves (4 for fp32) owns 32 rows (16 for fp32), so
+// every K and V fragment a wave reads from LDS feeds 32 rows, and each block staged
+// in LDS serves 256 rows. Per block of keys:
 //   * the workgroup stages K as [key][d] and V transposed as [d][key] in LDS (the
 //     next block's loads are issued into registers before the current block's
 //     products, so the gather latency overlaps the matrix work);
@@ -153,7 +154,7 @@ template <> struct Tile<true> {
   static constexpr int kKStride = kHeadDim + 8;    // bf16 elements per K row in LDS
   static constexpr int kVStride = 64 + 4;          // bf16 elements per V^T row in LDS
   static constexpr int kLds = kKeys * kKStride * 2 + kHeadDim * kVStride * 2;
-  u32x4_t k[4], v[4];                              // staging registers: 4 keys x 8 dims
+  u32x4_t k[2], v[2];                              // staging registers: 2 keys x 8 dims
 };
 template <> struct Tile<false> {
   static constexpr int kKeys = 32;
@@ -168,41 +169,41 @@ struct KeyMap {
   __device__ int64_t row(int x) const { return off[min(x, x_end - 1) - x_begin]; }
 };
 
-// K: thread t stages dims 8 (t % 16) + [0, 8) of keys 4 (t / 16) + [0, 4).
-// V: thread t stages dims 8 (t / 16) + [0, 8) of keys 4 (t % 16) + [0, 4), so that
-// the transposed writes of a 32-lane group fill two whole V^T rows (no bank conflict).
+// 512 threads stage a 64-key block. K: thread t stages dims 8 (t % 16) + [0, 8) of keys
+// 2 (t / 16) + [0, 2). V: thread t stages dims 8 (t / 32) + [0, 8) of keys 2 (t % 32) +
+// [0, 2), so that the transposed writes of a 32-lane group fill one whole V^T row (no
+// bank conflict).
 // K and V of a block are staged separately: the loop keeps K one block ahead of V.
 __device__ __forceinline__ void stage_load_k(Tile<true>& t, const uint16_t* kp, const KeyMap& km, int x0) {
   const int kq = threadIdx.x >> 4, dc = threadIdx.x & 15;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    t.k[i] = *reinterpret_cast<const u32x4_t*>(kp + km.row(x0 + 4 * kq + i) + 8 * dc);
+  for (int i = 0; i < 2; ++i)
+    t.k[i] = *reinterpret_cast<const u32x4_t*>(kp + km.row(x0 + 2 * kq + i) + 8 * dc);
 }
 __device__ __forceinline__ void stage_load_v(Tile<true>& t, const uint16_t* vp, const KeyMap& km, int x0) {
-  const int vq = threadIdx.x & 15, vc = threadIdx.x >> 4;
+  const int vq = threadIdx.x & 31, vc = threadIdx.x >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    t.v[i] = *reinterpret_cast<const u32x4_t*>(vp + km.row(x0 + 4 * vq + i) + 8 * vc);
+  for (int i = 0; i < 2; ++i)
+    t.v[i] = *reinterpret_cast<const u32x4_t*>(vp + km.row(x0 + 2 * vq + i) + 8 * vc);
 }
 __device__ __forceinline__ void stage_store_k(const Tile<true>& t, char* lds) {
   uint16_t* Ks = reinterpret_cast<uint16_t*>(lds);
   const int kq = threadIdx.x >> 4, dc = threadIdx.x & 15;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<u32x4_t*>(Ks + (4 * kq + i) * Tile<true>::kKStride + 8 * dc) = t.k[i];
+  for (int i = 0; i < 2; ++i)
+    *reinterpret_cast<u32x4_t*>(Ks + (2 * kq + i) * Tile<true>::kKStride + 8 * dc) = t.k[i];
 }
 __device__ __forceinline__ void stage_store_v(const Tile<true>& t, char* lds) {
   uint16_t* Vt = reinterpret_cast<uint16_t*>(lds) + Tile<true>::kKeys * Tile<true>::kKStride;
-  const int vq = threadIdx.x & 15, vc = threadIdx.x >> 4;
-  // V^T[d][key]: for each of the 8 dims, the 4 keys' values packed into 8 bytes. One
-  // byte permute joins the same 16-bit half of two keys' words (v_perm_b32: selector
+  const int vq = threadIdx.x & 31, vc = threadIdx.x >> 5;
+  // V^T[d][key]: for each of the 8 dims, the 2 keys' values packed into 4 bytes by one
+  // byte permute of the same 16-bit half of the two keys' words (v_perm_b32: selector
   // bytes 0-3 pick from the second operand, 4-7 from the first).
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-    const uint32_t k01 = __builtin_amdgcn_perm(t.v[1][e >> 1], t.v[0][e >> 1], sel);
-    const uint32_t k23 = __builtin_amdgcn_perm(t.v[3][e >> 1], t.v[2][e >> 1], sel);
-    *reinterpret_cast<uint2*>(Vt + (8 * vc + e) * Tile<true>::kVStride + 4 * vq) = make_uint2(k01, k23);
+    *reinterpret_cast<uint32_t*>(Vt + (8 * vc + e) * Tile<true>::kVStride + 2 * vq) =
+        __builtin_amdgcn_perm(t.v[1][e >> 1], t.v[0][e >> 1], sel);
   }
 }
 __device__ __forceinline__ void stage_load(Tile<false>& t, const float* kp, const float* vp,
@@ -399,10 +400,14 @@ __device__ __forceinline__ void softmax_step(float (&pv)[kN], float mloc, float&
   l_run += psum;
 }
 
-// bf16: 4 waves x 32 rows, v_mfma_f32_32x32x16_bf16. Lane l holds row l % 32 (lg = l / 32
+// bf16: 8 waves x 32 rows, v_mfma_f32_32x32x16_bf16. Lane l holds row l % 32 (lg = l / 32
 // picks which keys and dims of that row it carries).
-constexpr int kRows32 = 128;
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+constexpr int kRows32 = 256;
+constexpr int kThreads32 = 512;
+static_assert(kThreads32 / 64 * 32 == kRows32, "32 rows per wave");
+static_assert(Tile<true>::kKeys / 2 * 16 == kThreads32 && Tile<true>::kKeys / 2 * (kHeadDim / 8) == kThreads32,
+              "the K and V staging maps cover a block with 2 keys x 8 dims per thread");
+__global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void chunk_attn_bf16_kernel(ChunkParams p) {
   constexpr int KB = Tile<true>::kKeys;
   __shared__ __align__(16) char s_lds[2 * Tile<true>::kLds];
@@ -698,7 +703,7 @@ hipError_t launch_chunk_attn(const ChunkParams& p, hipStream_t s) {
   const dim3 block(256);
   const int units = p.b * p.Hkv * p.splits;
   const dim3 grid(kXcds * rt * ((units + kXcds - 1) / kXcds));
-  if (p.bf16) hipLaunchKernelGGL(chunk_attn_bf16_kernel, grid, block, 0, s, p);
+  if (p.bf16) hipLaunchKernelGGL(chunk_attn_bf16_kernel, grid, dim3(kThreads32), 0, s, p);
   else hipLaunchKernelGGL(chunk_attn_f32_kernel, grid, block, 0, s, p);
   const dim3 cgrid((unsigned)(((int64_t)p.b * p.max_chunk * p.H + 7) / 8));
   if (p.bf16) hipLaunchKernelGGL(chunk_combine_kernel<true>, cgrid, block, 0, s, p);
