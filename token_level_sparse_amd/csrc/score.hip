@@ -444,9 +444,22 @@ __global__ __launch_bounds__(256) void stats_kernel(ScoreParams p) {
   }
   const int c0 = s_chunk[r], c1 = s_chunk[r + 1];
   float M = kNegInf, S = 0.f;
-  for (int c = c0 + threadIdx.x; c < c1; c += blockDim.x) {
-    const float* src = p.partials + ((int64_t)h * s_chunk[b] + c) * 2;   // [H][chunks]: coalesced
-    merge_ms(M, S, src[0], src[1]);
+  // [H][chunks] pairs: coalesced 8-byte loads, 8 per thread in flight before they are
+  // merged in chunk order
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t* src = reinterpret_cast<const f32x2_t*>(p.partials) + (int64_t)h * s_chunk[b];
+  const int step = blockDim.x;
+  int c = c0 + threadIdx.x;
+  for (; c + 7 * step < c1; c += 8 * step) {
+    f32x2_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[c + k * step];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) merge_ms(M, S, v[k].x, v[k].y);
+  }
+  for (; c < c1; c += step) {
+    const f32x2_t v = src[c];
+    merge_ms(M, S, v.x, v.y);
   }
   for (int o = 32; o > 0; o >>= 1) {
     const float m2 = __shfl_xor(M, o), s2 = __shfl_xor(S, o);
