@@ -380,7 +380,8 @@ __device__ void refine_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
         if (kTopP) {
           // target mass: ceil(p * total mass of the request)
           u64 part = 0;
-          for (int i = threadIdx.x; i < kHistBins; i += kThreads) part += gm[i];
+#pragma unroll
+          for (int e = 0; e < kHistBins / kThreads; ++e) part += gm[threadIdx.x + e * kThreads];
           const u64 Q = block_excl_scan64(part, sh.w64) + part;    // inclusive: thread 255 holds the total
           if (threadIdx.x == kThreads - 1) sh.mres = Q;
           __syncthreads();
@@ -520,11 +521,22 @@ __device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) x[e] = lv[min(i0 + e, N - 1)];
     // counts of the request's earlier tiles
+    // (8-byte loads, four in flight per thread before they are added)
     int gtb = 0, eqb = 0;
-    const int first = sh.tb.tile[r];
-    for (int tt = threadIdx.x; tt < t; tt += kThreads) {
-      gtb += p.tile_counts[(int64_t)(first + tt) * 2 + 0];
-      eqb += p.tile_counts[(int64_t)(first + tt) * 2 + 1];
+    typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+    const i32x2_t* tc = reinterpret_cast<const i32x2_t*>(p.tile_counts) + sh.tb.tile[r];
+    int tt = threadIdx.x;
+    for (; tt + 3 * kThreads < t; tt += 4 * kThreads) {
+      i32x2_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = tc[tt + u * kThreads];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { gtb += v[u].x; eqb += v[u].y; }
+    }
+    for (; tt < t; tt += kThreads) {
+      const i32x2_t v = tc[tt];
+      gtb += v.x;
+      eqb += v.y;
     }
     __syncthreads();
     uint32_t key_t;
