@@ -18,7 +18,7 @@ Sources (pages of the reference set):
        Cache) and Algorithm 2 (Paged Dot Product Kernel).
   [BL] "TokenSelect: ... 128K->1M 23.84x" (ai-paper-analysis blog page).
        Section 3.1 (head soft vote), section 3.2 (Algorithm 1, Selection
-       Cache), section 4.2 / Table 2 (the "2K + 512 local" budget).
+       Cache), section 4.2 / Table 2 (a budget of 2K selected plus 512 local tokens).
 
 Readings taken where the pages are silent (each is listed in the design notes):
   * selection softmax has no 1/sqrt(d): the printed vote equation applies the
