@@ -23,19 +23,21 @@
 // heads of the group. Each of the 8 waves (4 for fp32) owns 32 rows (16 for fp32), so
 // every K and V fragment a wave reads from LDS feeds 32 rows, and each block staged
 // in LDS serves 256 rows. Per block of keys:
-//   * the workgroup stages K as [key][d] and V transposed as [d][key] in LDS (the
-//     next block's loads are issued into registers before the current block's
-//     products, so the gather latency overlaps the matrix work);
+//   * bf16: K and V rows go from global memory straight into LDS as [key][d]
+//     (global_load_lds_dwordx4, one 1 KiB window per wave and load), issued at the top
+//     of the previous block's iteration so they land while it computes; fp32: staged
+//     through registers, K and V as [key][d];
 //   * S^T = K Q^T on MFMA (A = 32 keys x 16 dims from LDS, B = the wave's queries
 //     held in registers), so a lane ends with 16 keys of one row: row = lane % 32;
 //   * online softmax in base 2 per row (row max across the 2 lane halves); in bf16
 //     the exp2 of block n runs between the MFMAs of block n + 1's scores, so the
 //     VALU and the matrix cores work at the same time inside one wave;
 //   * O^T += V^T P^T on MFMA: the lane's probabilities are already the B operand
-//     (row = lane % 32, 8 keys per step), with the key order of the A operand (V^T
-//     rows from LDS) permuted to match, so P never leaves registers.
-// The staging registers are clang vector types: with HIP's struct vector types the
-// compiler kept them in scratch memory, and each block then waited for its prefetch.
+//     (row = lane % 32, 8 keys per step); in bf16 the A operand (V^T) is read from the
+//     [key][d] rows with LDS transpose reads (ds_read_b64_tr_b16) in the key order of
+//     the probabilities, so P never leaves registers.
+// The fp32 staging registers are clang vector types: with HIP's struct vector types
+// the compiler kept them in scratch memory, and each block waited for its prefetch.
 // bf16 uses v_mfma_f32_32x32x16_bf16 on 64-key blocks (accumulators in VGPRs, two
 // waves per SIMD); fp32 uses v_mfma_f32_16x16x4_f32 on 32-key blocks with 16-row
 // waves and the same index and mask logic.
@@ -151,10 +153,8 @@ __global__ __launch_bounds__(kMeanThreads) void chunk_mean_kernel(ChunkParams p)
 template <bool kBf16> struct Tile;
 template <> struct Tile<true> {
   static constexpr int kKeys = 64;                 // keys per staged block
-  static constexpr int kKStride = kHeadDim + 8;    // bf16 elements per K row in LDS
-  static constexpr int kVStride = 64 + 4;          // bf16 elements per V^T row in LDS
-  static constexpr int kLds = kKeys * kKStride * 2 + kHeadDim * kVStride * 2;
-  u32x4_t k[2], v[2];                              // staging registers: 2 keys x 8 dims
+  static constexpr int kRow = kHeadDim * 2;        // bytes per K or V row in LDS (no padding)
+  static constexpr int kLds = 2 * kKeys * kRow;    // K rows, then V rows, [key][d]
 };
 template <> struct Tile<false> {
   static constexpr int kKeys = 32;
@@ -169,43 +169,38 @@ struct KeyMap {
   __device__ int64_t row(int x) const { return off[min(x, x_end - 1) - x_begin]; }
 };
 
-// 512 threads stage a 64-key block. K: thread t stages dims 8 (t % 16) + [0, 8) of keys
-// 2 (t / 16) + [0, 2). V: thread t stages dims 8 (t / 32) + [0, 8) of keys 2 (t % 32) +
-// [0, 2), so that the transposed writes of a 32-lane group fill one whole V^T row (no
-// bank conflict).
-// K and V of a block are staged separately: the loop keeps K one block ahead of V.
-__device__ __forceinline__ void stage_load_k(Tile<true>& t, const uint16_t* kp, const KeyMap& km, int x0) {
-  const int kq = threadIdx.x >> 4, dc = threadIdx.x & 15;
+// bf16 blocks are staged straight from global memory into LDS (global_load_lds_dwordx4:
+// lane i of a wave's load writes bytes 16 i .. 16 i + 15 of a 1 KiB LDS window, i.e.
+// 4 rows of 256 bytes). Rows keep no padding; instead the 16-byte chunks are permuted
+// per row so the operand reads are conflict-free: chunk c of K row x sits at position
+// c ^ (x mod 16), chunk c of V row x at position c ^ 2 (x mod 4). A lane therefore
+// fetches the global chunk that belongs at its LDS position.
+__device__ __forceinline__ int k_pos(int x, int c) { return c ^ (x & 15); }
+__device__ __forceinline__ int v_pos(int x, int c) { return c ^ ((x & 3) << 1); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
+
+// Wave w stages rows 8 w .. 8 w + 7 of the block (K into kl and/or V into vl) starting
+// at list entry x0.
+__device__ __forceinline__ void stage_direct(char* kl, char* vl, const uint16_t* kp, const uint16_t* vp,
+                                             const KeyMap& km, int x0, bool do_k, bool do_v) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    t.k[i] = *reinterpret_cast<const u32x4_t*>(kp + km.row(x0 + 2 * kq + i) + 8 * dc);
-}
-__device__ __forceinline__ void stage_load_v(Tile<true>& t, const uint16_t* vp, const KeyMap& km, int x0) {
-  const int vq = threadIdx.x & 31, vc = threadIdx.x >> 5;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    t.v[i] = *reinterpret_cast<const u32x4_t*>(vp + km.row(x0 + 2 * vq + i) + 8 * vc);
-}
-__device__ __forceinline__ void stage_store_k(const Tile<true>& t, char* lds) {
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(lds);
-  const int kq = threadIdx.x >> 4, dc = threadIdx.x & 15;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    *reinterpret_cast<u32x4_t*>(Ks + (2 * kq + i) * Tile<true>::kKStride + 8 * dc) = t.k[i];
-}
-__device__ __forceinline__ void stage_store_v(const Tile<true>& t, char* lds) {
-  uint16_t* Vt = reinterpret_cast<uint16_t*>(lds) + Tile<true>::kKeys * Tile<true>::kKStride;
-  const int vq = threadIdx.x & 31, vc = threadIdx.x >> 5;
-  // V^T[d][key]: for each of the 8 dims, the 2 keys' values packed into 4 bytes by one
-  // byte permute of the same 16-bit half of the two keys' words (v_perm_b32: selector
-  // bytes 0-3 pick from the second operand, 4-7 from the first).
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-    *reinterpret_cast<uint32_t*>(Vt + (8 * vc + e) * Tile<true>::kVStride + 2 * vq) =
-        __builtin_amdgcn_perm(t.v[1][e >> 1], t.v[0][e >> 1], sel);
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * wave + 4 * j + (lane >> 4), pos = lane & 15;
+    const int64_t off = km.row(x0 + row);
+    const int at = (8 * wave + 4 * j) * Tile<true>::kRow;
+    if (do_k)
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(kp + off + 8 * k_pos(row, pos)), (lds_void*)(kl + at), 16, 0, 0);
+    if (do_v)
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(vp + off + 8 * v_pos(row, pos)), (lds_void*)(vl + at), 16, 0, 0);
   }
 }
+// Every staged write of this thread has landed in LDS (the barrier that follows makes
+// them visible to the other waves).
+__device__ __forceinline__ void stage_wait() { __builtin_amdgcn_s_waitcnt(0); }
+
 __device__ __forceinline__ void stage_load(Tile<false>& t, const float* kp, const float* vp,
                                            const KeyMap& km, int x0) {
   const int key = threadIdx.x >> 3, dq = threadIdx.x & 7;
@@ -245,14 +240,13 @@ __device__ __forceinline__ void load_qop32(QOp32& q, const uint16_t* qrow, bool 
 // <q_row, k_{32 t + 8 (j / 4) + 4 lg + j % 4}> for the lane's row l32.
 __device__ __forceinline__ void qk_block32(const char* lds, const QOp32& q, int l32, int lg,
                                            f32x16_t (&s)[2]) {
-  const uint16_t* Ks = reinterpret_cast<const uint16_t*>(lds);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     f32x16_t acc = {};
+    const int x = 32 * t + l32;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(
-          Ks + (32 * t + l32) * Tile<true>::kKStride + 16 * ks + 8 * lg);
+      const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(lds + x * Tile<true>::kRow + 16 * k_pos(x, 2 * ks + lg));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, q.v[ks], acc, 0, 0, 0);
     }
     s[t] = acc;
@@ -261,10 +255,16 @@ __device__ __forceinline__ void qk_block32(const char* lds, const QOp32& q, int 
 
 // bf16 O^T += V^T P^T: o[dt][j] = O[row][32 dt + 8 (j / 4) + 4 lg + j % 4]. The B operand
 // of the 16-key step (t, hh) is the lane's pv[t][8 hh .. 8 hh + 8) (keys 32 t + 16 hh +
-// 4 lg + [0, 4) and + 8), so the A operand's keys are read in that order from V^T.
+// 4 lg + [0, 4) and + 8), so the A operand (dim 32 dt + l32 of those 8 keys) is read in
+// that order from the [key][d] V rows with ds_read_b64_tr_b16: in each 16-lane group,
+// element k of lane i is element i % 4 of the 8 bytes that lane 4 k + i / 4 addresses, so
+// lane s of the group addresses key (first key + s / 4), dims (group's first dim + 4 (s % 4)).
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 __device__ __forceinline__ void pv_block32(const char* lds, const f32x16_t (&pv)[2], int l32, int lg,
                                            f32x16_t (&o)[4]) {
-  const uint16_t* Vt = reinterpret_cast<const uint16_t*>(lds) + Tile<true>::kKeys * Tile<true>::kKStride;
+  const char* Vs = lds;
+  const int s = threadIdx.x & 15, half = l32 >> 4;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -276,10 +276,13 @@ __device__ __forceinline__ void pv_block32(const char* lds, const f32x16_t (&pv)
                            (__bf16)pv[t][b8 + 6], (__bf16)pv[t][b8 + 7]};
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* vr = Vt + (32 * dt + l32) * Tile<true>::kVStride + 32 * t + 16 * hh + 4 * lg;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        const int x = 32 * t + 16 * hh + 4 * lg + (s >> 2);               // keys x, then x + 8
+        const int c = 4 * dt + 2 * half + ((s & 3) >> 1), b = 8 * (s & 1);
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(Vs + x * Tile<true>::kRow + 16 * v_pos(x, c) + b));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(Vs + (x + 8) * Tile<true>::kRow + 16 * v_pos(x + 8, c) + b));
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[dt], 0, 0, 0);
       }
     }
@@ -405,12 +408,14 @@ __device__ __forceinline__ void softmax_step(float (&pv)[kN], float mloc, float&
 constexpr int kRows32 = 256;
 constexpr int kThreads32 = 512;
 static_assert(kThreads32 / 64 * 32 == kRows32, "32 rows per wave");
-static_assert(Tile<true>::kKeys / 2 * 16 == kThreads32 && Tile<true>::kKeys / 2 * (kHeadDim / 8) == kThreads32,
-              "the K and V staging maps cover a block with 2 keys x 8 dims per thread");
+static_assert(kThreads32 / 64 * 8 == Tile<true>::kKeys, "each wave stages 8 rows of a block");
 __global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void chunk_attn_bf16_kernel(ChunkParams p) {
   constexpr int KB = Tile<true>::kKeys;
-  __shared__ __align__(16) char s_lds[2 * Tile<true>::kLds];
+  __shared__ __align__(16) char s_k0[Tile<true>::kKeys * Tile<true>::kRow];
+  __shared__ __align__(16) char s_k1[Tile<true>::kKeys * Tile<true>::kRow];
+  __shared__ __align__(16) char s_v0[Tile<true>::kKeys * Tile<true>::kRow];
+  __shared__ __align__(16) char s_v1[Tile<true>::kKeys * Tile<true>::kRow];
   __shared__ int64_t s_keys[kChunkSplitKeys];
   __shared__ int s_geom[5];
   UnitWork w;
@@ -479,14 +484,14 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
   // maximum is finite, so no -inf guard is needed.
   auto exp_qk = [&](auto full_c, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], const char* kb) {
     constexpr bool kFull = decltype(full_c)::value;
-    const uint16_t* Ks = reinterpret_cast<const uint16_t*>(kb);
     const float nm = -m_run;
     f32x16_t a0 = {}, a1 = {};
     float psum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(Ks + l32 * Tile<true>::kKStride + 16 * ks + 8 * lg);
-      const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(Ks + (32 + l32) * Tile<true>::kKStride + 16 * ks + 8 * lg);
+      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(kb + l32 * Tile<true>::kRow + 16 * k_pos(l32, 2 * ks + lg));
+      const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(kb + (32 + l32) * Tile<true>::kRow +
+                                                             16 * k_pos(32 + l32, 2 * ks + lg));
       a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q.v[ks], a0, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -511,47 +516,35 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
 
   // Software pipeline, one barrier per block: the scores of block n + 1 go to the
   // matrix cores before block n's softmax, so the two overlap within the wave. Block m
-  // keeps K in buffer m % 2 and V^T in buffer m % 2, with K staged one block ahead:
-  // entering iteration n, S_n is in registers, K_{n+1} and V_n are in LDS, and the
-  // staging registers hold K_{n+2} and V_{n+1}. Iteration n writes K_{n+2} over K_n
-  // (read in iteration n - 1) and V_{n+1} over V_{n-1} (read in iteration n - 1).
-  char* buf0 = s_lds;
-  char* buf1 = s_lds + Tile<true>::kLds;
+  // keeps K in buffer m % 2 and V in buffer m % 2, with K staged one block ahead:
+  // entering iteration n, S_n is in registers and K_{n+1}, V_n are in LDS. Iteration n
+  // first starts the staging of K_{n+2} over K_n (read in iteration n - 1) and of V_{n+1}
+  // over V_{n-1} (read in iteration n - 1); they land while the block is computed.
   const int nb = (w.x_end - w.x_begin + KB - 1) / KB;
-  Tile<true> st;
-  stage_load_k(st, kp, w.km, w.x_begin);
-  stage_load_v(st, vp, w.km, w.x_begin);
-  stage_store_k(st, buf0);
-  stage_store_v(st, buf0);
-  if (nb > 1) {
-    stage_load_k(st, kp, w.km, w.x_begin + KB);
-    stage_load_v(st, vp, w.km, w.x_begin + KB);
-  }
+  stage_direct(s_k0, s_v0, kp, vp, w.km, w.x_begin, true, true);
+  if (nb > 1) stage_direct(s_k1, s_v1, kp, vp, w.km, w.x_begin + KB, true, false);
+  stage_wait();
   __syncthreads();
   f32x16_t sa[2], sb[2];
-  qk_block32(buf0, q, l32, lg, sa);
-  if (nb > 1) {
-    stage_store_k(st, buf1);
-    if (nb > 2) stage_load_k(st, kp, w.km, w.x_begin + 2 * KB);
-  }
+  qk_block32(s_k0, q, l32, lg, sa);
   __syncthreads();
-  auto step = [&](int n, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+  // Even blocks use the buffers named 0, odd blocks those named 1, fixed per unrolled
+  // step: with the staging writes and the reads of an iteration in distinct LDS
+  // objects, the compiler does not wait for the staging before the reads.
+  auto step = [&](int n, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], char* kn, char* vn, char* kn1, char* vn1) {
     const int x0 = w.x_begin + n * KB;
-    char* bn = (n & 1) ? buf1 : buf0;
-    char* bn1 = (n & 1) ? buf0 : buf1;
+    if (n + 2 < nb) stage_direct(kn, vn1, kp, vp, w.km, x0 + 2 * KB, true, false);   // K_{n+2}
+    if (n + 1 < nb) stage_direct(kn, vn1, kp, vp, w.km, x0 + KB, false, true);       // V_{n+1}
     // S_{n+1} is computed even past the last block (from stale, in-bounds LDS) and unused
-    if (soft_max(cur, x0)) exp_qk(std::true_type{}, cur, nxt, bn1);
-    else exp_qk(std::false_type{}, cur, nxt, bn1);
-    pv_block32(bn, cur, l32, lg, o);
-    if (n + 2 < nb) stage_store_k(st, bn);
-    if (n + 1 < nb) stage_store_v(st, bn1);
-    if (n + 3 < nb) stage_load_k(st, kp, w.km, x0 + 3 * KB);
-    if (n + 2 < nb) stage_load_v(st, vp, w.km, x0 + 2 * KB);
+    if (soft_max(cur, x0)) exp_qk(std::true_type{}, cur, nxt, kn1);
+    else exp_qk(std::false_type{}, cur, nxt, kn1);
+    pv_block32(vn, cur, l32, lg, o);
+    stage_wait();
     __syncthreads();
   };
   for (int n = 0; n < nb; n += 2) {
-    step(n, sa, sb);
-    if (n + 1 < nb) step(n + 1, sb, sa);
+    step(n, sa, sb, s_k0, s_v0, s_k1, s_v1);
+    if (n + 1 < nb) step(n + 1, sb, sa, s_k1, s_v1, s_k0, s_v0);
   }
 
   const float lt = l_run + __shfl_xor(l_run, 32);
