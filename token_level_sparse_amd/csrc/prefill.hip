@@ -154,7 +154,6 @@ template <bool kBf16> struct Tile;
 template <> struct Tile<true> {
   static constexpr int kKeys = 64;                 // keys per staged block
   static constexpr int kRow = kHeadDim * 2;        // bytes per K or V row in LDS (no padding)
-  static constexpr int kLds = 2 * kKeys * kRow;    // K rows, then V rows, [key][d]
 };
 template <> struct Tile<false> {
   static constexpr int kKeys = 32;
@@ -641,7 +640,6 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkParams p) {
   const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   const int64_t rows = (int64_t)p.b * p.max_chunk * p.H;
   if (row >= rows) return;
-  const int h = (int)(row % p.H);
   const int j = (int)((row / p.H) % p.max_chunk);
   const int r = (int)(row / ((int64_t)p.H * p.max_chunk));
   const ChunkGeom gm = chunk_geom(p, r, false);

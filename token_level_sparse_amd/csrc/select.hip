@@ -153,7 +153,7 @@ __device__ void find_digit_pk(const uint32_t* hist, const u64* mhist, int kk, u6
   }
   __syncthreads();
   const int bin = max(max(s_bin[0], s_bin[1]), 0);
-  if (threadIdx.x == (kBins - 1 - bin) / kPer) {
+  if ((int)threadIdx.x == (kBins - 1 - bin) / kPer) {
     uint32_t acc = ac;
     u64 accm = am;
 #pragma unroll
