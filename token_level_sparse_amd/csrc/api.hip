@@ -224,8 +224,18 @@ struct PrefillLayout {
   size_t qbar, past, kbase, cpart, total;
 };
 
+// Compute units a chunk-attention launch should fill at least once.
+constexpr int kComputeUnits = 256;
+
+int chunk_split_keys_for(const ts_shape& s, const ts_select& sel, int max_chunk) {
+  const int G = s.num_q_heads / s.num_kv_heads;
+  const int rows = s.dtype == TS_BF16 ? ts::kChunkRowsBf16 : ts::kChunkRows;
+  const int64_t wgs = cdiv((int64_t)max_chunk * G, rows) * s.num_kv_heads * s.batch;
+  return ts::chunk_split_keys(eff_top_k(s, sel), eff_local(s, sel), max_chunk, wgs, kComputeUnits);
+}
+
 int chunk_splits_for(const ts_shape& s, const ts_select& sel, int max_chunk) {
-  return ts::chunk_splits(eff_top_k(s, sel), eff_local(s, sel), max_chunk);
+  return ts::chunk_splits(eff_top_k(s, sel), eff_local(s, sel), max_chunk, chunk_split_keys_for(s, sel, max_chunk));
 }
 
 int64_t chunk_max_keys_for(const ts_shape& s, const ts_select& sel, int max_chunk) {
@@ -289,6 +299,7 @@ ts::ChunkParams chunk_params(const ts_shape& s, const ts_select& sel, int max_ch
   p.H = s.num_q_heads; p.Hkv = s.num_kv_heads; p.b = s.batch; p.stride = s.block_table_stride;
   p.max_chunk = max_chunk; p.sel_stride = sel.top_k; p.n_local = sel.n_local;
   p.splits = chunk_splits_for(s, sel, max_chunk);
+  p.split_keys = chunk_split_keys_for(s, sel, max_chunk);
   p.attn_scale = sel.attn_scale;
   p.bf16 = s.dtype == TS_BF16;
   return p;

@@ -97,11 +97,12 @@ struct AttnParams {
 // runs over a gathered key list: the TopK positions below the window start
 // w0 = max(0, P_r - L) (n_sel of them), then the contiguous range
 // [w0, P_r + c_r); query j sees the first base + j + 1 entries, base = n_sel + P_r - w0.
-constexpr int kChunkRows = 64;        // fewest (query, head) rows per attention workgroup (fp32; bf16 256)
+constexpr int kChunkRows = 64;        // (query, head) rows per fp32 attention workgroup (the fewest)
+constexpr int kChunkRowsBf16 = 256;   // (query, head) rows per bf16 attention workgroup
 #ifndef TS_CHUNK_SPLIT_KEYS
 #define TS_CHUNK_SPLIT_KEYS 1024
 #endif
-constexpr int kChunkSplitKeys = TS_CHUNK_SPLIT_KEYS;  // key-list entries per attention split
+constexpr int kChunkSplitKeys = TS_CHUNK_SPLIT_KEYS;  // most key-list entries per attention split
 constexpr int kChunkPartStride = 128 + 4;  // floats per split partial: o[128], m, l, pad
 
 struct ChunkParams {
@@ -119,6 +120,7 @@ struct ChunkParams {
   float* partials;            // [b][max_chunk][H][splits][kChunkPartStride]
   void* out;                  // [b][max_chunk][H][d]
   int H, Hkv, b, stride, max_chunk, sel_stride, n_local, splits;
+  int split_keys;             // key-list entries per split (<= kChunkSplitKeys)
   float attn_scale;
   int bf16;
 };
@@ -127,8 +129,25 @@ struct ChunkParams {
 __host__ __device__ inline long long chunk_max_keys(int top_k, int n_local, int max_chunk) {
   return (long long)top_k + n_local + max_chunk;
 }
-__host__ __device__ inline int chunk_splits(int top_k, int n_local, int max_chunk) {
-  return (int)((chunk_max_keys(top_k, n_local, max_chunk) + kChunkSplitKeys - 1) / kChunkSplitKeys);
+// Key-list entries per attention split: kChunkSplitKeys, or fewer (a multiple of 64;
+// at most ceil(keys / 256) splits) when the workgroups of one split (`wgs_per_split`,
+// from the largest chunk) would not fill the machine's compute units once.
+__host__ __device__ inline int chunk_split_keys(int top_k, int n_local, int max_chunk, long long wgs_per_split,
+                                                int num_cus) {
+  const long long keys = chunk_max_keys(top_k, n_local, max_chunk);
+  long long splits = (keys + kChunkSplitKeys - 1) / kChunkSplitKeys;
+  if (wgs_per_split * splits < num_cus) {
+    const long long want = (num_cus + wgs_per_split - 1) / wgs_per_split;
+    const long long most = (keys + 255) / 256;
+    splits = want < most ? want : most;
+    if (splits < 1) splits = 1;
+  }
+  const long long per = (keys + splits - 1) / splits;
+  const long long rounded = (per + 63) / 64 * 64;
+  return (int)(rounded < kChunkSplitKeys ? rounded : kChunkSplitKeys);
+}
+__host__ __device__ inline int chunk_splits(int top_k, int n_local, int max_chunk, int split_keys) {
+  return (int)((chunk_max_keys(top_k, n_local, max_chunk) + split_keys - 1) / split_keys);
 }
 
 __host__ __device__ inline int attn_splits(int top_k, int n_local) {

@@ -360,9 +360,9 @@ __device__ bool chunk_unit(const ChunkParams& p, int rows_per_wg, int* s_geom, i
   if (w.row0 >= w.rows) return false;
   const int jmax = (min(w.row0 + rows_per_wg, w.rows) - 1) / w.G;
   const int n_vis = w.base + jmax + 1;                        // entries the last query sees
-  w.x_begin = w.split * kChunkSplitKeys;
+  w.x_begin = w.split * p.split_keys;
   if (w.x_begin >= n_vis) return false;
-  w.x_end = min(w.x_begin + kChunkSplitKeys, n_vis);
+  w.x_end = min(w.x_begin + p.split_keys, n_vis);
   // key-list entry x: the x-th selected position below the window (the TopK is
   // ascending), then the window and the chunk [w0, P + c); its row of this KV head
   const int w0 = s_geom[2], n_sel = s_geom[3], N = s_geom[4];
@@ -404,7 +404,7 @@ __device__ __forceinline__ void softmax_step(float (&pv)[kN], float mloc, float&
 
 // bf16: 8 waves x 32 rows, v_mfma_f32_32x32x16_bf16. Lane l holds row l % 32 (lg = l / 32
 // picks which keys and dims of that row it carries).
-constexpr int kRows32 = 256;
+constexpr int kRows32 = kChunkRowsBf16;
 constexpr int kThreads32 = 512;
 static_assert(kThreads32 / 64 * 32 == kRows32, "32 rows per wave");
 static_assert(kThreads32 / 64 * 8 == Tile<true>::kKeys, "each wave stages 8 rows of a block");
@@ -562,7 +562,7 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
 
 // fp32: 4 waves x 16 rows, v_mfma_f32_16x16x4_f32, 32-key blocks. Lane l holds row
 // l % 16 (a = l / 16 picks which keys and dims of that row it carries).
-constexpr int kRows16 = 64;
+constexpr int kRows16 = kChunkRows;
 __global__ __launch_bounds__(256) void chunk_attn_f32_kernel(ChunkParams p) {
   constexpr int KB = Tile<false>::kKeys;
   constexpr int NT = KB / 16;
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkParams p) {
   if (j >= gm.c) return;
   // splits that hold entries visible to chunk query j (the attention kernel stored the
   // request's key-list base, so no search of the TopK list here)
-  const int S = min(p.splits, (p.key_base[r] + j + kChunkSplitKeys) / kChunkSplitKeys);
+  const int S = min(p.splits, (p.key_base[r] + j + p.split_keys) / p.split_keys);
   const int d4 = 4 * (threadIdx.x & 31);
   const float* src = p.partials + row * p.splits * kPartStride;
   // one pass: the splits' loads are independent, the merge keeps a running maximum
