@@ -674,7 +674,7 @@ def main():
                     help="short program for rocprofv3 --pmc passes (scoring launches + a 1 GiB copy)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 

@@ -86,8 +86,8 @@ typedef enum { TS_F32 = 0, TS_BF16 = 1 } ts_dtype;
 typedef struct {
   int32_t num_q_heads;        /* H, >= 1                                         */
   int32_t num_kv_heads;       /* H_kv, >= 1, H % H_kv == 0, H / H_kv <= 8         */
-  int32_t head_dim;           /* d; this build supports 128                     */
-  int32_t page_size;          /* tokens per page; this build supports 16        */
+  int32_t head_dim;           /* d; the library supports 128                    */
+  int32_t page_size;          /* tokens per page; the library supports 16       */
   int32_t batch;              /* requests, 1 ... 1024                           */
   int32_t block_table_stride; /* int32 entries per block-table row, >= 1        */
   int64_t max_total_tokens;   /* upper bound of sum_r N_r (sizes grids/workspace) */

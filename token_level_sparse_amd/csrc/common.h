@@ -6,8 +6,8 @@
 
 namespace ts {
 
-constexpr int kHeadDim = 128;     // d handled by this build
-constexpr int kPage = 16;         // tokens per page handled by this build
+constexpr int kHeadDim = 128;     // the head dimension the kernels support
+constexpr int kPage = 16;         // the page size (tokens) the kernels support
 constexpr int kWave = 64;         // CDNA wavefront
 constexpr int kXcds = 8;          // accelerator complex dies; workgroup i runs on XCD i % 8
 constexpr int kMaxBatch = 1024;   // requests per call (LDS prefix tables)
