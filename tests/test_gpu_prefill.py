@@ -102,6 +102,22 @@ def test_prefill_llama3_128k_full_selection():
     assert np.all(np.isin(big, po.T[0]))
 
 
+def test_prefill_chunk1024_group8_ragged_bf16():
+    # a chunk of 1024 queries with G = 8 (32 row tiles of 256 per KV head, 4 splits)
+    # next to a chunk of 300: rows across row tiles, splits and the causal edge
+    geo = wl.workload("prefill-llama3-128k", num_q_heads=32, num_kv_heads=4, batch=2, min_len=20000,
+                      max_len=40000, chunk=1024, top_k=2048, n_local=512, seed=5700)
+    cb = wl.make_chunk_batch(geo, DEV, chunk_lens=[1024, 300])
+    gh.log(f"[prefill chunk 1024, G=8, bf16] N={[int(x) for x in cb.seq_lens.cpu()]} chunk lengths 1024 / 300")
+    po = gh.run_prefill(cb, geo)
+    rows = [0, 1, 31, 32, 255, 256, 299, 511, 512, 767, 1000, 1023]
+    for r in range(2):
+        c = int(cb.chunk_lens[r])
+        s = gh.check_prefill_selection(po, r, cb, geo)
+        w = gh.check_chunk_attention(po, r, cb, geo, po.T[r], rows=[j for j in rows if j < c])
+        gh.log(f"  request {r}: c={c} topk diff {s['n_diff']} attn max-abs {w:.2e}")
+
+
 def test_prefill_planted_recall_without_scale_spread():
     geo = wl.workload("prefill-llama3-128k", seq_len=32768)
     gh.log("[prefill llama3 N=32768, s=1] planted recall of the mean query")
