@@ -97,7 +97,9 @@ typedef struct {
 /* Selection parameters (host struct). */
 typedef struct {
   int32_t top_k;              /* k >= 1: TopK budget of the head soft vote       */
-  int32_t n_local;            /* L >= 0: most recent positions always attended   */
+  int32_t n_local;            /* L >= 0: most recent positions always attended;
+                                 the decode window is [N_r - max(L, 1), N_r), so
+                                 the current token is attended even with L = 0  */
   float score_scale;          /* multiplies <q, k> before the selection softmax;
                                  1.0 is the printed vote equation (raw logits)  */
   float attn_scale;           /* SDPA scale, normally 1/sqrt(d)                  */
@@ -153,10 +155,12 @@ ts_status tokenselect_vote_topk(const ts_shape* shape, const ts_select* sel,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Step 5. Attention of every query head over S_r = TopK_r united with
-   [max(0, N_r - n_local), N_r), without duplicates: out[r][h] = sum_{i in S_r}
+   [max(0, N_r - max(n_local, 1)), N_r), without duplicates: out[r][h] = sum_{i in S_r}
    softmax_i(attn_scale * <q_h, K_{h/G}[i]>) V_{h/G}[i] (deepnotes selective
-   sparse attention formalisation). sel_idx rows must be ascending. A request with
-   N_r = 0 has an empty S_r and gets out[r] = 0. */
+   sparse attention formalisation: the selected keys plus the current one, so the
+   current token N_r - 1 is in S_r even with n_local = 0). sel_idx entries outside
+   [0, N_r) are ignored. A request with N_r = 0 has an empty S_r and gets
+   out[r] = 0; its block-table row is not read. */
 ts_status tokenselect_sparse_attn(const ts_shape* shape, const ts_select* sel,
                                   const void* q, const void* k_pool, const void* v_pool,
                                   const int32_t* block_table, const int32_t* seq_lens,

@@ -27,7 +27,8 @@ Readings taken where the pages are silent (each is listed in the design notes):
     heads, so the votes sum to H;
   * TopK runs over all N positions; ties go to the lower position; the result
     is returned in ascending order; k >= N selects everything;
-  * the selected set is TopK united with the window [N - L, N), deduplicated;
+  * the selected set is TopK united with the window [N - max(L, 1), N),
+    deduplicated: the current token is attended even with L = 0;
   * attention covers the N cached tokens including the current one, with
     scale 1/sqrt(d), no causal mask (a single decode query);
   * the Selection Cache compares with the query stored at the last miss
@@ -107,12 +108,16 @@ def topk_indices(v, k: int) -> np.ndarray:
 
 
 def union_local(T, N: int, n_local: int) -> np.ndarray:
-    """Selected set S = TopK result united with the last n_local positions.
+    """Selected set S = TopK result united with the last max(n_local, 1) positions.
 
     [BL] section 4.2 and [DN] results paragraph: the budget is k selected
-    tokens plus a window of recent local tokens. Ascending, no duplicates.
+    tokens plus a window of recent local tokens. [DN] selective sparse
+    attention formalisation: the attended keys are [K_select, K_current], so
+    the current token (position N - 1) belongs to S whatever the window size;
+    with n_local = 0 the window is that one position. Ascending, no duplicates.
     """
-    win = np.arange(max(0, N - n_local), N, dtype=np.int64)
+    width = max(n_local, 1)
+    win = np.arange(max(0, N - width), N, dtype=np.int64)
     return np.union1d(np.asarray(T, dtype=np.int64), win)
 
 

@@ -234,3 +234,64 @@ def test_requests_sharing_score_blocks_and_an_empty_request():
                 assert np.array_equal(Ts[t][r], Ts[t - 1][r])
             gh.check_attention(outs[t][r], q_all[t], K[:, :N], V[:, :N], Ts[t][r], N, geo.n_local,
                                geo.attn_scale, False)
+
+
+def test_empty_request_with_invalid_block_table_row():
+    """A request with N_r = 0 reaches no page, so its block-table row may hold
+    anything: here every entry is -1 and its TopK row holds stale, negative and
+    out-of-range positions. Its output is zero, and the other requests' outputs are
+    bit-identical to a run where the empty request's row holds valid pages."""
+    geo = wl.workload("llama3-8b-128k", top_k=64, n_local=16, n_planted=2)
+    gh.log("[empty request, block-table row of -1]")
+    gen = torch.Generator(device=DEV).manual_seed(31)
+    lens0 = [300, 40, 1000]
+    reqs = [wl.make_request(gen, geo, n, DEV) for n in lens0]
+    batch = wl.page_requests(reqs, geo, gen, DEV)
+    H, d, b = geo.num_q_heads, geo.head_dim, len(reqs)
+    lens = torch.tensor([300, 0, 1000], dtype=torch.int32, device=DEV)
+    shape = ts.make_shape(H, geo.num_kv_heads, b, batch.block_table.shape[1], sum(lens0),
+                          geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, 0.9)
+    ws = ts.alloc_workspace(shape, sel, DEV)
+    outs = {}
+    for name in ("valid_row", "row_of_minus_one"):
+        bt = batch.block_table.clone()
+        if name == "row_of_minus_one":
+            bt[1] = -1
+        report = ts.validate(shape, bt, lens, batch.k_pool.shape[0])
+        torch.cuda.synchronize()
+        assert report.cpu().tolist()[0] == 0, (name, report.cpu().tolist())
+        cache = ts.CacheState.allocate(b, H, d, geo.top_k, geo.torch_dtype, DEV)
+        cache.cached_idx[1] = torch.tensor([5, -3, 10 ** 6] * 21 + [7], dtype=torch.int32, device=DEV)
+        hit = torch.zeros(b, dtype=torch.int32, device=DEV)
+        res = []
+        for step in range(2):                   # a miss, then a hit with the same query
+            out = torch.full((b, H, d), float("nan"), dtype=geo.torch_dtype, device=DEV)
+            ts.decode_step(shape, sel, batch.q, batch.k_pool, batch.v_pool, bt, lens, cache, hit,
+                           out, ws)
+            torch.cuda.synchronize()
+            assert hit.cpu().tolist() == [step, step, step], (name, step, hit.cpu().tolist())
+            assert int(cache.cached_count[1]) == 0
+            res.append(gh.np32(out))
+        # step 5 alone with a stale TopK row and count for the empty request
+        sel_idx = cache.cached_idx.clone()
+        sel_idx[1] = torch.tensor([5, -3, 10 ** 6] * 21 + [7], dtype=torch.int32, device=DEV)
+        sel_count = cache.cached_count.clone()
+        sel_count[1] = geo.top_k
+        out = torch.full((b, H, d), float("nan"), dtype=geo.torch_dtype, device=DEV)
+        ts.sparse_attn(shape, sel, batch.q, batch.k_pool, batch.v_pool, bt, lens, sel_idx, sel_count,
+                       out, ws)
+        torch.cuda.synchronize()
+        res.append(gh.np32(out))
+        for o in res:
+            assert np.all(o[1] == 0.0), name
+        outs[name] = res
+    for a, c in zip(outs["valid_row"], outs["row_of_minus_one"]):
+        assert np.array_equal(a[[0, 2]], c[[0, 2]])
+    # the non-empty requests against the oracle (window and TopK of the miss step)
+    for r in (0, 2):
+        N = int(lens[r])
+        q, K, V = gh.np32(reqs[r].q), gh.np32(reqs[r].k)[:, :N], gh.np32(reqs[r].v)[:, :N]
+        T = ora.select(q, K, geo.top_k)["T"]
+        ref = ora.sparse_attention(q, K, V, ora.union_local(T, N, geo.n_local), geo.attn_scale)
+        assert np.max(np.abs(outs["valid_row"][0][r] - ref)) <= 2e-2

@@ -189,6 +189,25 @@ def test_window_union():
     assert ora.union_local([0, 8], 10, 3).tolist() == [0, 7, 8, 9]
     assert ora.union_local([1], 2, 5).tolist() == [0, 1]
     assert ora.union_local([3, 4], 5, 0).tolist() == [3, 4]
+    # the current token (position N - 1) is attended whatever the window size:
+    # the deepnotes formalisation attends [K_select, K_current]
+    assert ora.union_local([0, 2], 10, 0).tolist() == [0, 2, 9]
+    assert ora.union_local([], 1, 0).tolist() == [0]
+    assert ora.union_local([], 0, 0).tolist() == []
+
+
+def test_decode_step_without_window_attends_current_token():
+    # H = 1, d = 1, q = 1, keys 3, 1, 0: the TopK (k = 1) is position 0, the
+    # current token is position 2. S = {0, 2}; with attn_scale 1 the weights are
+    # e^3 / (e^3 + 1) and 1 / (e^3 + 1), so o = (10 e^3 + 30) / (e^3 + 1).
+    q = np.array([[1.0]])
+    K = np.array([[[3.0], [1.0], [0.0]]])
+    V = np.array([[[10.0], [20.0], [30.0]]])
+    res = ora.decode_step(q, K, V, k=1, n_local=0, attn_scale=1.0)
+    assert res["T"].tolist() == [0]
+    assert res["S"].tolist() == [0, 2]
+    e3 = math.exp(3.0)
+    assert abs(res["out"][0, 0] - (10.0 * e3 + 30.0) / (e3 + 1.0)) < 1e-12
 
 
 def test_lemma1_topk_invariant_within_angle():

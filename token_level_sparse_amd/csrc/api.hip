@@ -74,6 +74,11 @@ int eff_top_k(const ts_shape& s, const ts_select& sel) {
 int eff_local(const ts_shape& s, const ts_select& sel) {
   return (int)std::min<int64_t>(sel.n_local, s.max_total_tokens);
 }
+// Window of the decode attention: the n_local newest positions, and never fewer
+// than one, so the current token is always attended.
+int decode_window(const ts_shape& s, const ts_select& sel) {
+  return std::max(1, eff_local(s, sel));
+}
 
 Layout layout(const ts_shape& s, const ts_select& sel) {
   Layout L;
@@ -89,7 +94,7 @@ Layout layout(const ts_shape& s, const ts_select& sel) {
   L.mstate = off;   off += align_up(sizeof(uint64_t) * 4 * (size_t)s.batch);
   L.state = off;    off += align_up(sizeof(int32_t) * 8 * (size_t)s.batch);
   L.tiles = off;    off += align_up(sizeof(int32_t) * 2 * (size_t)max_tiles(s));
-  const int S = ts::attn_splits(eff_top_k(s, sel), eff_local(s, sel));
+  const int S = ts::attn_splits(eff_top_k(s, sel), decode_window(s, sel));
   L.attn = off;     off += align_up(sizeof(float) * (ts::kHeadDim + 2) * (size_t)s.batch * H * S);
   L.total = off;
   return L;
@@ -123,7 +128,7 @@ ts_status check_shape(const ts_shape* s, const ts_select* sel) {
     return fail(TS_ERR_INVALID_ARG, "top_p %g outside [0, 1] (0 turns the top-p budget off)", sel->top_p);
   // the attention grid has one workgroup per (request, KV head, slice of 128 selected
   // or window positions)
-  const int64_t slices = (int64_t)ts::attn_splits(eff_top_k(*s, *sel), eff_local(*s, *sel));
+  const int64_t slices = (int64_t)ts::attn_splits(eff_top_k(*s, *sel), decode_window(*s, *sel));
   if ((int64_t)s->batch * s->num_kv_heads * slices > INT32_MAX)
     return fail(TS_ERR_UNSUPPORTED, "batch x num_kv_heads x (top_k + n_local) / 128 too large for "
                 "the attention grid");
@@ -212,7 +217,7 @@ ts::AttnParams attn_params(const ts_shape& s, const ts_select& sel, const void* 
   p.H = s.num_q_heads; p.Hkv = s.num_kv_heads; p.b = s.batch; p.stride = s.block_table_stride;
   p.sel_stride = sel.top_k;
   p.top_k = eff_top_k(s, sel);
-  p.n_local = eff_local(s, sel);
+  p.n_local = decode_window(s, sel);
   p.attn_scale = sel.attn_scale;
   p.bf16 = s.dtype == TS_BF16;
   return p;

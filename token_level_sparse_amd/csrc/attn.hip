@@ -8,7 +8,8 @@
 // tokens to the selected budget.
 //
 // gfx950 design. The selected set of request r is the TopK list (ascending)
-// united with the window [N - L, N); TopK entries inside the window are skipped
+// united with the window [N - L, N), L >= 1 (with a window size of 0 the window is
+// the current token alone); TopK entries inside the window are skipped
 // because the window covers them, so no sort or merge is needed. A workgroup
 // covers 128 selected slots (32 per wavefront) of the TopK list or of the window,
 // for one KV head and all G query heads of its group: each key and value row
@@ -74,23 +75,36 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   const int cand = (s < nT) ? p.sel_idx[(int64_t)r * p.sel_stride + e_sel] : 0;
   const int N = p.seq_lens[r];
   const int cnt = (s < nT) ? min(p.sel_count[r], p.sel_stride) : 0;
+  // p.n_local >= 1: the window always holds the current token N - 1
   const int lstart = max(0, N - p.n_local);
+  float* part = p.partials + ((int64_t)r * H + g * G) * S * (kHeadDim + 2);
+  if (N <= 0) {
+    // An empty request reaches no page: its block-table row is not read at all
+    // and the partial is the empty one (o = 0, m = -inf, l = 0).
+    for (int e = threadIdx.x; e < G * (kHeadDim + 2); e += blockDim.x) {
+      const int h = e / (kHeadDim + 2), c = e % (kHeadDim + 2);
+      part[((int64_t)h * S + s) * (kHeadDim + 2) + c] = (c == kHeadDim) ? kNegInf : 0.f;
+    }
+    return;
+  }
 
   // Token of this wave's slot e = lane (lanes 0..31), then broadcast by shuffle.
-  int tok = 0;
+  // A slot that holds no selected token gathers the current token N - 1 (always a
+  // reached page) and gets weight 0.
+  int tok = N - 1;
   bool ok = false;
   if (lane < kAttnSplit) {
     if (s < nT) {
       const int e = s * kAttnTile + wave * kAttnSplit + lane;
       if (e < cnt) {
-        tok = cand;
-        ok = tok >= 0 && tok < lstart;
+        ok = cand >= 0 && cand < lstart;
+        if (ok) tok = cand;
       }
     } else {
-      tok = lstart + (s - nT) * kAttnTile + wave * kAttnSplit + lane;
-      ok = tok < N;
+      const int t = lstart + (s - nT) * kAttnTile + wave * kAttnSplit + lane;
+      ok = t < N;
+      if (ok) tok = t;
     }
-    if (!ok) tok = 0;                               // a real token; its weight is forced to 0
   }
   const int32_t* bt = p.block_table + (int64_t)r * p.stride;
   int64_t rowoff = 0;
@@ -202,7 +216,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
         L = fmaf(c, s_part[w][h][kHeadDim + 1], L);
       }
     }
-    float* dst = p.partials + (((int64_t)r * H + g * G + h) * S + s) * (kHeadDim + 2);
+    float* dst = part + ((int64_t)h * S + s) * (kHeadDim + 2);
     dst[dim] = acc;
     if (dim == 0) {
       dst[kHeadDim] = M;

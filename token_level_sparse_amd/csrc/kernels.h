@@ -86,7 +86,7 @@ struct AttnParams {
   void* out;                  // [b][H][d]
   int H, Hkv, b, stride;
   int sel_stride;             // int32 entries per sel_idx row (the caller's top_k)
-  int top_k, n_local;         // min(top_k, max tokens), min(n_local, max tokens): work items
+  int top_k, n_local;         // min(top_k, max tokens), max(1, min(n_local, max tokens)): work items
   float attn_scale;
   int bf16;
 };
