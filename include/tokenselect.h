@@ -179,6 +179,29 @@ ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel,
                                   const ts_cache* cache, int32_t* hit, void* out,
                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the static device scratch behind tokenselect_decode_step_noalloc (64 MiB):
+   enough for tokenselect_workspace_size() of e.g. 32 query heads over ~480K cached
+   tokens in total. */
+#define TS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* tokenselect_decode_step without a workspace argument, for callers that cannot
+   allocate device memory (code under HIP graph capture, tight serving loops,
+   harnesses that forbid hipMalloc). Same arguments, results and errors as
+   tokenselect_decode_step; the workspace is a static device array of
+   TS_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+   process ends (its address is looked up on the first call on a device). The call
+   allocates nothing. A shape whose tokenselect_workspace_size() exceeds
+   TS_NOALLOC_SCRATCH_BYTES is rejected with TS_ERR_WORKSPACE before any launch.
+   Every call on one GPU uses that GPU's one scratch array: calls that may overlap
+   on one device (several streams, several host threads) race and must be ordered
+   by the caller; the scratch keeps no state from one call to the next that a later
+   call relies on. */
+ts_status tokenselect_decode_step_noalloc(const ts_shape* shape, const ts_select* sel,
+                                          const void* q, const void* k_pool, const void* v_pool,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          const ts_cache* cache, int32_t* hit, void* out,
+                                          hipStream_t stream);
+
 /* ---------------------------------------------------------------- chunk-wise prefill
    A prefill chunk of request r is its c_r newest tokens: their K/V are already in
    the pool at positions [P_r, P_r + c_r) with P_r = N_r - c_r (seq_lens[r] = N_r

@@ -50,7 +50,7 @@ def test_stream_probe_library_exports_and_validates():
     from token_level_sparse_amd import build as tb
     if not os.path.exists(tb.PROBE_LIB):
         pytest.skip("probe library not built")
-    hdr = open(os.path.join(ROOT, "include", "ts_stream_probe.h")).read()
+    hdr = open(os.path.join(ROOT, "token_level_sparse_amd", "csrc", "probe", "ts_stream_probe.h")).read()
     names = set(re.findall(r"\b(ts_stream_probe\w*)\s*\(", hdr))
     assert names == {"ts_stream_probe"}
     plib = ctypes.CDLL(tb.PROBE_LIB)
@@ -242,3 +242,31 @@ def test_top_p_field_layout(lib):
     # the binding's struct matches the header's field order and size
     assert ctypes.sizeof(ts.Select) == 4 * 4 + 8 + 8
     assert ts.Select.top_p.offset == 24
+
+
+def test_noalloc_step_rejects_before_any_device_call(lib):
+    # argument checks and the static-scratch limit are host-side: no HIP call runs
+    cache = ts.Cache(FAKE, FAKE, FAKE, FAKE)
+    f = lib.tokenselect_decode_step_noalloc
+    shape, sel = _shape(max_total_tokens=1 << 20, block_table_stride=65536), _sel()
+    assert ts.workspace_size(shape, sel) > ts.NOALLOC_SCRATCH_BYTES
+    st = f(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(cache),
+           FAKE, FAKE, None)
+    assert st == ts.TS_ERR_WORKSPACE
+    msg = lib.tokenselect_last_error().decode()
+    assert "static scratch" in msg and str(ts.NOALLOC_SCRATCH_BYTES) in msg
+    shape = _shape()
+    assert ts.workspace_size(shape, sel) <= ts.NOALLOC_SCRATCH_BYTES
+    st = f(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(cache),
+           None, FAKE, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+    assert "hit" in lib.tokenselect_last_error().decode()
+    st = f(ctypes.byref(shape), ctypes.byref(_sel(top_k=0)), FAKE, FAKE, FAKE, FAKE, FAKE,
+           ctypes.byref(cache), FAKE, FAKE, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define TS_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ts.NOALLOC_SCRATCH_BYTES

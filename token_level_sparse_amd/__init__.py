@@ -28,6 +28,7 @@ ENTRY_POINTS = (
     "tokenselect_vote_topk",
     "tokenselect_sparse_attn",
     "tokenselect_decode_step",
+    "tokenselect_decode_step_noalloc",
     "tokenselect_prefill_workspace_size",
     "tokenselect_prefill_select",
     "tokenselect_chunk_attn",
@@ -104,6 +105,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tokenselect_decode_step.argtypes = [sp, selp, vp, vp, vp, vp, vp, ctypes.POINTER(Cache),
                                             vp, vp, vp, sz, vp]
     lib.tokenselect_decode_step.restype = ctypes.c_int
+    lib.tokenselect_decode_step_noalloc.argtypes = [sp, selp, vp, vp, vp, vp, vp, ctypes.POINTER(Cache),
+                                                    vp, vp, vp]
+    lib.tokenselect_decode_step_noalloc.restype = ctypes.c_int
     i32 = ctypes.c_int32
     lib.tokenselect_prefill_workspace_size.argtypes = [sp, selp, i32]
     lib.tokenselect_prefill_workspace_size.restype = sz
@@ -229,6 +233,21 @@ def decode_step(shape, sel, q, k_pool, v_pool, block_table, seq_lens, cache: Cac
                                        _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                                        _ptr(seq_lens), ctypes.byref(cs), _ptr(hit), _ptr(out),
                                        _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# Bytes of the static scratch behind decode_step_noalloc (TS_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_step_noalloc(shape, sel, q, k_pool, v_pool, block_table, seq_lens, cache: CacheState, hit,
+                        out, stream=None):
+    """tokenselect_decode_step_noalloc: the decode step on the library's static scratch."""
+    lib = load_library()
+    cs = cache.c_struct()
+    _check(lib.tokenselect_decode_step_noalloc(ctypes.byref(shape), ctypes.byref(sel), _ptr(q),
+                                               _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                               _ptr(seq_lens), ctypes.byref(cs), _ptr(hit), _ptr(out),
+                                               _stream(stream)))
 
 
 # ---------------------------------------------------------------- chunk-wise prefill

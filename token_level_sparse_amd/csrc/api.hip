@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -574,18 +575,30 @@ ts_status tokenselect_sparse_attn(const ts_shape* shape, const ts_select* sel, c
   return device_status(ts::launch_attn(p, stream), "sparse attention launch");
 }
 
-ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel, const void* q,
-                                  const void* k_pool, const void* v_pool,
-                                  const int32_t* block_table, const int32_t* seq_lens,
-                                  const ts_cache* cache, int32_t* hit, void* out, void* ws,
-                                  size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+ts_status check_decode_args(const ts_shape* shape, const ts_select* sel, const void* q,
+                            const void* k_pool, const void* v_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, const ts_cache* cache, const int32_t* hit,
+                            const void* out) {
   ts_status st = check_shape(shape, sel);
   if (st != TS_OK) return st;
   TS_REQUIRE16(q); TS_REQUIRE16(k_pool); TS_REQUIRE16(v_pool); TS_REQUIRE(block_table);
   TS_REQUIRE(seq_lens); TS_REQUIRE(cache); TS_REQUIRE(hit); TS_REQUIRE(out);
   TS_REQUIRE16(cache->cached_q); TS_REQUIRE(cache->cached_idx); TS_REQUIRE(cache->cached_count);
   TS_REQUIRE(cache->valid);
-  if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
+  return TS_OK;
+}
+
+// Launches of one decode step on a checked workspace.
+ts_status decode_step_launch(const ts_shape* shape, const ts_select* sel, const void* q,
+                             const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const ts_cache* cache, int32_t* hit, void* out, void* ws,
+                             hipStream_t stream) {
+  ts_status st;
   const Layout L = layout(*shape, *sel);
   float* logits = at<float>(ws, L.logits);
   float* stats = at<float>(ws, L.stats);
@@ -610,6 +623,72 @@ ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel, c
   const ts::AttnParams ap = attn_params(*shape, *sel, q, k_pool, v_pool, block_table, seq_lens,
                                         cache->cached_idx, cache->cached_count, out, ws);
   return device_status(ts::launch_attn(ap, stream), "sparse attention launch");
+}
+
+// Static scratch of tokenselect_decode_step_noalloc. In host code `scratch` is only
+// a stand-in for the symbol: its device address on the current device comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kScratchBytes = TS_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+ts_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TS_ERR_UNSUPPORTED, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p || reinterpret_cast<uintptr_t>(p) % kAlign)
+      return fail(TS_ERR_DEVICE, "static scratch address %p is not %zu-byte aligned", p, kAlign);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return TS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ts_status tokenselect_decode_step(const ts_shape* shape, const ts_select* sel, const void* q,
+                                  const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  const ts_cache* cache, int32_t* hit, void* out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  ts_status st = check_decode_args(shape, sel, q, k_pool, v_pool, block_table, seq_lens, cache, hit,
+                                   out);
+  if (st != TS_OK) return st;
+  if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
+  return decode_step_launch(shape, sel, q, k_pool, v_pool, block_table, seq_lens, cache, hit, out,
+                            ws, stream);
+}
+
+ts_status tokenselect_decode_step_noalloc(const ts_shape* shape, const ts_select* sel,
+                                          const void* q, const void* k_pool, const void* v_pool,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          const ts_cache* cache, int32_t* hit, void* out,
+                                          hipStream_t stream) {
+  ts_status st = check_decode_args(shape, sel, q, k_pool, v_pool, block_table, seq_lens, cache, hit,
+                                   out);
+  if (st != TS_OK) return st;
+  const size_t need = layout(*shape, *sel).total;
+  if (need > kScratchBytes)
+    return fail(TS_ERR_WORKSPACE,
+                "this shape needs %zu bytes of scratch, above the %zu-byte static scratch of "
+                "tokenselect_decode_step_noalloc (lower max_total_tokens, or call "
+                "tokenselect_decode_step with a caller workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != TS_OK) return st;
+  return decode_step_launch(shape, sel, q, k_pool, v_pool, block_table, seq_lens, cache, hit, out,
+                            ws, stream);
 }
 
 ts_status tokenselect_validate(const ts_shape* shape, const int32_t* block_table,
