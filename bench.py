@@ -30,6 +30,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -345,6 +347,28 @@ def time_ablations(geo, dev, reps=10):
     return {"workload": geo.name, "N": total, "top_k": geo.top_k, "selectors": res}
 
 
+def time_score_launches(shape, sel, b, H, B, reps, dev, ws):
+    """Mean time of tokenselect_score launches (score + stats kernels) over a batch,
+    each between its own events on the current stream."""
+    import torch
+    import token_level_sparse_amd as ts
+    logits = torch.empty(H * b.total_tokens, dtype=torch.float32, device=dev)
+    stats = torch.empty(B * H * 2, dtype=torch.float32, device=dev)
+    ts.score(shape, sel, b.q, b.k_pool, b.block_table, b.seq_lens, logits, stats, ws)
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ts.score(shape, sel, b.q, b.k_pool, b.block_table, b.seq_lens, logits, stats, ws)
+        e.record()
+        evs.append((a, e))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(e) for a, e in evs) / reps
+    del logits, stats
+    return ms
+
+
 def time_ragged(geo, steps, warmup, dev):
     """Ragged batch: 16 requests in one shared shuffled pool, one launch per kernel per step."""
     import torch
@@ -373,10 +397,17 @@ def time_ragged(geo, steps, warmup, dev):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     kbytes = geo.num_kv_heads * geo.head_dim * 2 * b.total_tokens
-    log(f"[{geo.name}] batch of {B}, sum N = {b.total_tokens}: decode step {ms:.4f} ms")
+    score_ms = time_score_launches(shape, sel, b, H, B, steps, dev, ws)
+    algo = score_bytes_per_token(geo) * b.total_tokens
+    log(f"[{geo.name}] batch of {B}, sum N = {b.total_tokens}: decode step {ms:.4f} ms; score launch "
+        f"{score_ms:.4f} ms -> {algo / (score_ms * 1e-3) / 1e9:.0f} GB/s")
     res = {"workload": geo.name, "batch": B, "total_tokens": b.total_tokens,
            "decode_steps_per_s": 1e3 / ms, "ms_per_step": ms,
-           "k_stream_gbps_whole_step": kbytes / (ms * 1e-3) / 1e9}
+           "k_stream_gbps_whole_step": kbytes / (ms * 1e-3) / 1e9,
+           "score_ms": score_ms, "score_bytes": algo, "score_gbps": algo / (score_ms * 1e-3) / 1e9,
+           "score_frac_of_peak": algo / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+           "score_what": "one tokenselect_score launch over the whole batch (about 3.7 GB of K, "
+                         "beyond the 256 MB MALL)"}
     del b, ws
     torch.cuda.empty_cache()
     return res
@@ -434,11 +465,38 @@ def time_cache_sequence(geo, dev):
     miss_sets = [set(snaps[t][0][0, :int(snaps[t][1][0])].tolist()) for t in range(steps) if hv3[t] == 0]
     overlaps = [len(a & b) / max(1, len(b)) for a, b in zip(miss_sets, miss_sets[1:])]
     overlap = sum(overlaps) / len(overlaps) if overlaps else None
+    # untimed fourth pass, each step between its own events: hit and miss steps apart
+    cache.valid.zero_()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for t, (a, e) in enumerate(evs):
+        a.record()
+        ts.decode_step(shape, sel, qs[t], batch.k_pool, batch.v_pool, batch.block_table, lens[t],
+                       cache, hits[t:t + 1], out, ws)
+        e.record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(e) for a, e in evs]
+    hit_ms = [x for x, h in zip(per, hv) if h]
+    miss_ms = [x for x, h in zip(per, hv) if not h]
+    # the scoring pass of a miss step at the first step's length: K is 128 MiB, which the
+    # 256 MB MALL holds across steps, so its bandwidth is an effective (cache-assisted) one
+    from types import SimpleNamespace
+    b1 = SimpleNamespace(q=qs[0], k_pool=batch.k_pool, block_table=batch.block_table, seq_lens=lens[0],
+                         total_tokens=geo.seq_len + steps - 1)
+    score_ms = time_score_launches(shape, sel, b1, H, 1, 32, dev, ws)
+    algo = score_bytes_per_token(geo) * geo.seq_len
     log(f"[{geo.name}] {steps} steps: {ms:.4f} ms/step, hit rate {sum(hv) / steps:.3f}, "
-        f"mean overlap of consecutive reselections {overlap if overlap is None else round(overlap, 4)}")
+        f"mean overlap of consecutive reselections {overlap if overlap is None else round(overlap, 4)}; "
+        f"hit steps {sum(hit_ms) / max(1, len(hit_ms)):.4f} ms, miss steps {sum(miss_ms) / max(1, len(miss_ms)):.4f} ms; "
+        f"score launch {score_ms:.4f} ms")
     res = {"workload": geo.name, "steps": steps, "decode_steps_per_s": 1e3 / ms, "ms_per_step": ms,
            "hit_rate": sum(hv) / steps, "hits": "".join(str(h) for h in hv),
-           "miss_topk_overlap": overlap, "same_hits_on_rerun": hv3 == hv}
+           "miss_topk_overlap": overlap, "same_hits_on_rerun": hv3 == hv,
+           "hit_step_ms": sum(hit_ms) / max(1, len(hit_ms)), "miss_step_ms": sum(miss_ms) / max(1, len(miss_ms)),
+           "score_ms": score_ms, "score_bytes": algo,
+           "score_gbps_effective": algo / (score_ms * 1e-3) / 1e9,
+           "score_frac_of_peak_effective": algo / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+           "score_what": "effective: tokenselect_score over the sequence's first step (N = 131072, "
+                         "128 MiB of K, held by the 256 MB MALL between launches)"}
     del batch, ws
     torch.cuda.empty_cache()
     return res
@@ -608,27 +666,110 @@ def counter_run(geo, dev, launches=4, layers=4):
     log(f"[counters] {launches} score launches and {launches} 1 GiB copies done")
 
 
-def cpu_baseline(geo, host, min_seconds=10.0, max_steps=30):
-    """The fp64 oracle, as it stands, on whole decode steps of layer 0, repeated until
-    at least min_seconds of host work (a bounded sample of the headline workload)."""
+def _host(t):
+    return t.float().cpu().numpy()
+
+
+def cpu_baseline(geo, host, dev):
+    """The fp64 oracle, as it stands, timed on the host cores beside the GPU figures.
+
+    Every workload is run through the oracle's own entry points (select, window,
+    attention; decode_sequence with the Selection Cache for the 256-step sequence):
+    the tiny fp32 workload, the 128K request, the 16-request ragged batch (one step of
+    the whole batch) and the 256-step Selection Cache sequence in full, and one decode
+    step of layer 0 of the 1M workload (the headline's unit). The matmuls run on a
+    BLAS pool set to every core of the process's CPU affinity; numpy's elementwise
+    steps (exp, sums, sorts) run on one thread. Each workload is also timed with the
+    BLAS pool limited to one thread (the sequence on its first 16 steps). Inputs are
+    generated on the GPU by the same seeded generators and copied to the host; no
+    input is shared with the GPU timings."""
+    import torch
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import tokenselect_oracle as ora
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:
-        threads = 1
+    from synth import workloads as wl
+    cores = len(os.sched_getaffinity(0))
+
+    def step_fn(g, q, K, V):
+        return lambda: ora.decode_step(q, K, V, g.top_k, g.n_local, 1.0, g.attn_scale)
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def both(fn, one_thread_fn=None):
+        with threadpool_limits(limits=cores, user_api="blas"):
+            blas = max([i.get("num_threads") or 1 for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+            t_all = timed(fn)
+        with threadpool_limits(limits=1, user_api="blas"):
+            t_one = timed(one_thread_fn or fn)
+        return t_all, t_one, blas
+
+    out = {}
+    # one untimed small step first, so no figure below carries numpy's first-call costs
+    g0 = wl.workload("tiny-f32-8k", seq_len=2048, top_k=64, n_local=16)
+    b0 = wl.make_batch(g0, device=dev)
+    r0 = b0.requests[0]
+    step_fn(g0, _host(r0.q), _host(r0.k), _host(r0.v))()
+    del b0, r0
+    # c2: one decode step of layer 0 of the 1M workload (the headline unit)
     q, K, V = host
-    n = 0
-    t0 = time.perf_counter()
-    while n < max_steps and (n == 0 or time.perf_counter() - t0 < min_seconds):
-        ora.decode_step(q, K, V, geo.top_k, geo.n_local, 1.0, geo.attn_scale)
-        n += 1
-    dt = time.perf_counter() - t0
-    log(f"[cpu oracle] {n} decode steps in {dt:.2f}s with {threads} threads")
-    return {"value": n / dt, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} full decode steps (select + attention, numpy fp64) of layer 0 of "
-                      f"{geo.name} (N={K.shape[1]}), {dt:.1f} s of host work"}
+    t_all, t_one, blas = both(step_fn(geo, q, K, V))
+    out[geo.name] = {"decode_steps_per_s": 1.0 / t_all, "decode_steps_per_s_1thread": 1.0 / t_one,
+                     "sample": f"one decode step of layer 0 (N = {K.shape[1]})", "seconds": t_all + t_one}
+    del host, q, K, V
+    # c0, c1: one full decode step of the tiny fp32 and the 128K workloads
+    for name in ("tiny-f32-8k", "llama3-8b-128k"):
+        g = wl.workload(name)
+        b = wl.make_batch(g, device=dev)
+        r = b.requests[0]
+        args = (_host(r.q), _host(r.k), _host(r.v))
+        del b, r
+        t_all, t_one, _ = both(step_fn(g, *args))
+        out[name] = {"decode_steps_per_s": 1.0 / t_all, "decode_steps_per_s_1thread": 1.0 / t_one,
+                     "sample": f"one decode step (N = {args[1].shape[1]})", "seconds": t_all + t_one}
+    # c3: one decode step of the whole 16-request batch
+    g = wl.workload("llama3-8b-ragged16")
+    b = wl.make_batch(g, device=dev)
+    reqs = [(_host(r.q), _host(r.k), _host(r.v)) for r in b.requests]
+    total = b.total_tokens
+    del b
+    run = lambda rs: [ora.decode_step(q, K, V, g.top_k, g.n_local, 1.0, g.attn_scale) for q, K, V in rs]
+    sub = reqs[:4]
+    sub_tokens = sum(K.shape[1] for _, K, _ in sub)
+    t_all, t_one, _ = both(lambda: run(reqs), lambda: run(sub))
+    out[g.name] = {"decode_steps_per_s": 1.0 / t_all,
+                   "decode_steps_per_s_1thread": sub_tokens / total / t_one,
+                   "sample": f"one decode step of all {len(reqs)} requests (sum N = {total}); 1 thread: "
+                             f"the first 4 requests ({sub_tokens} tokens), scaled to the whole batch",
+                   "seconds": t_all + t_one}
+    del reqs
+    # c4: the 256-step Selection Cache sequence (oracle decode_sequence: fp64 cosine, the
+    # selection on misses, the attention every step)
+    g = wl.workload("qwen2-7b-cache256")
+    gen = torch.Generator(device=dev).manual_seed(g.seed)
+    req = wl.make_request(gen, g, g.seq_len, dev, extra_tokens=g.steps - 1)
+    qs, _ = wl.ar1_queries(g, req.q_master, g.steps, seed=g.seed + 1, device=dev)
+    qs, K, V = _host(qs), _host(req.k), _host(req.v)
+    del req
+    lens = np.arange(g.seq_len, g.seq_len + g.steps)
+    seq = lambda n: ora.decode_sequence(qs[:n], K, V, lens[:n], g.top_k, g.n_local, g.cos_threshold,
+                                        1.0, g.attn_scale)
+    t_all, t_one, _ = both(lambda: seq(g.steps), lambda: seq(16))
+    out[g.name] = {"decode_steps_per_s": g.steps / t_all, "decode_steps_per_s_1thread": 16 / t_one,
+                   "sample": f"all {g.steps} steps (1 thread: the first 16 steps)", "seconds": t_all + t_one}
+    del qs, K, V
+    spent = sum(v["seconds"] for v in out.values())
+    log("[cpu oracle] " + ", ".join(f"{k} {v['decode_steps_per_s']:.3g} steps/s "
+                                    f"({v['decode_steps_per_s_1thread']:.3g} on 1 thread)" for k, v in out.items())
+        + f"; {spent:.1f} s on {cores} cores")
+    head = out[geo.name]
+    return {"value": head["decode_steps_per_s"], "unit": "decode steps/s", "cores": cores,
+            "threads": blas, "kind": "oracle",
+            "sample": f"{head['sample']} of {geo.name} with every core of the CPU affinity "
+                      f"({cores}) in the BLAS pool; per-config figures (all cores and 1 thread) in "
+                      f"configs; {spent:.0f} s of host work in total",
+            "value_1thread": head["decode_steps_per_s_1thread"], "configs": out}
 
 
 def guarded(name, fn):
@@ -692,20 +833,37 @@ def main():
     topp_run = None if args.no_secondary else (
         lambda layers: guarded("top_p", lambda: time_topp(geo, 8, max(16, args.steps // 2), 4, dev,
                                                             layers=layers)))
-    main_res, host = time_workload(geo, args.layers, args.steps, args.warmup, dev,
+    # every generated layer is timed at least once: with fewer timed steps than layers,
+    # only as many layers as steps are generated (and reported)
+    n_layers = max(1, min(args.layers, args.steps))
+    main_res, host = time_workload(geo, n_layers, args.steps, args.warmup, dev,
                                    keep_host=not args.no_cpu_baseline, ceiling=True, then=topp_run)
-    secondary = None
+    secondary = tiny = None
     if not args.no_secondary:
         def run_128k():
             g1 = wl.workload("llama3-8b-128k")
             # 8 rotating layers: 8 x 256 MiB of K, so no step finds its pool in the 256 MB MALL
-            r1, _ = time_workload(g1, 8, max(args.steps, 32), args.warmup, dev)
+            r1, _ = time_workload(g1, 8, max(args.steps, 32), args.warmup, dev, ceiling=True)
             return {"workload": g1.name, "N": g1.seq_len, "decode_steps_per_s": 1e3 / r1["ms_per_step"],
                     "ms_per_step": r1["ms_per_step"],
                     "step_ms_percentiles": {q: r1[f"step_ms_p{q}"] for q in (10, 50, 90)},
-                    "score_ms": r1["score_ms"],
-                    "score_gbps": r1["score_gbps"], "k_gbps": r1["k_gbps"], "rotating_layers": 8}
+                    "score_ms": r1["score_ms"], "score_bytes": r1["score_bytes"],
+                    "score_gbps": r1["score_gbps"], "score_frac_of_peak": r1["score_gbps"] / PEAK_HBM_GBPS,
+                    "k_gbps": r1["k_gbps"], "rotating_layers": 8, "ceiling": ceiling_line(r1)}
         secondary = guarded("llama3-8b-128k", run_128k)
+
+        def run_tiny():
+            g0 = wl.workload("tiny-f32-8k")
+            r0, _ = time_workload(g0, 1, max(args.steps, 32), args.warmup, dev)
+            return {"workload": g0.name, "N": g0.seq_len, "dtype": "f32",
+                    "decode_steps_per_s": 1e3 / r0["ms_per_step"], "ms_per_step": r0["ms_per_step"],
+                    "step_ms_percentiles": {q: r0[f"step_ms_p{q}"] for q in (10, 50, 90)},
+                    "score_ms": r0["score_ms"], "score_bytes": r0["score_bytes"],
+                    "score_gbps_effective": r0["score_gbps"],
+                    "score_frac_of_peak_effective": r0["score_gbps"] / PEAK_HBM_GBPS,
+                    "what": "correctness-sized workload (8 MiB of fp32 K, cache-resident): "
+                            "latency-bound, its bandwidth is an effective one"}
+        tiny = guarded("tiny-f32-8k", run_tiny)
     ragged = cache_seq = prefill = topp = ablations = dense = None
     if not args.no_secondary:
         ceil = main_res.get("ceiling") or {}
@@ -720,7 +878,7 @@ def main():
                                                                  max(16, args.steps // 2), 4, dev)),
                    guarded("prefill-1m", lambda: time_prefill(wl.workload("prefill-llama3-1m"), 4,
                                                                max(8, args.steps // 8), 2, dev))]
-    cpu = guarded("cpu_baseline", lambda: cpu_baseline(geo, host)) if host is not None else None
+    cpu = guarded("cpu_baseline", lambda: cpu_baseline(geo, host, dev)) if host is not None else None
 
     ms = main_res["ms_per_step"]
     line = {
@@ -740,7 +898,7 @@ def main():
         "config": {"workload": geo.name, "N": geo.seq_len, "batch": 1,
                    "heads": f"{geo.num_q_heads}/{geo.num_kv_heads}/{geo.head_dim}",
                    "top_k": geo.top_k, "n_local": geo.n_local, "page_size": geo.page_size,
-                   "layers": args.layers, "cache": "every step reselects"},
+                   "layers": n_layers, "cache": "every step reselects"},
         "roofline": {"bound": "hbm", "achieved": main_res["score_gbps"], "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": main_res["score_gbps"] / PEAK_HBM_GBPS,
                      "traffic": measured_traffic(),
@@ -750,6 +908,7 @@ def main():
         "k_stream_gbps": main_res["k_gbps"],
         "scored_tokens_per_s": main_res["tokens"] * 1e3 / ms,
         "secondary": secondary,
+        "tiny": tiny,
         "ragged_batch": ragged,
         "selection_cache": cache_seq,
         "prefill": prefill,

@@ -2,8 +2,9 @@
 
 Every kernel source under csrc/ is compiled by hipcc into one shared library
 exporting the C ABI declared in include/tokenselect.h. The streaming-bandwidth
-probe under csrc/probe/ (measurement only, include/ts_stream_probe.h) is built
-into libts_stream_probe.so beside it.
+probe under csrc/probe/ (measurement only, declared in csrc/probe/ts_stream_probe.h,
+outside the method's ABI directory include/) is built into libts_stream_probe.so
+beside it.
 """
 from __future__ import annotations
 
@@ -39,10 +40,10 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def _compile(out: str, srcs, verbose: bool) -> str:
+def _compile(out: str, srcs, verbose: bool, extra_inc=()) -> str:
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           "-o", tmp, *srcs]
+    inc = [os.path.join(ROOT, "include"), os.path.join(PKG, "csrc"), *extra_inc]
+    cmd = [hipcc(), *HIP_FLAGS, *[a for d in inc for a in ("-I", d)], "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,7 +61,8 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source into libtokenselect.so (and the bandwidth probe into
     libts_stream_probe.so); returns the main library path."""
     _compile(LIB, sources(), verbose)
-    _compile(PROBE_LIB, sorted(glob.glob(os.path.join(PKG, "csrc", "probe", "*.hip"))), verbose)
+    probe = os.path.join(PKG, "csrc", "probe")
+    _compile(PROBE_LIB, sorted(glob.glob(os.path.join(probe, "*.hip"))), verbose, extra_inc=(probe,))
     return LIB
 
 
