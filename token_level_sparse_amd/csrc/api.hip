@@ -59,7 +59,7 @@ constexpr int kMaxGrid = 2048;
 
 // Byte offsets of the workspace regions.
 struct Layout {
-  size_t logits, partials, stats, vote, hist, mass, mstate, state, tiles, attn, total;
+  size_t logits, partials, stats, vote, hist, mass, mstate, state, tiles, cand, attn, total;
 };
 
 int64_t max_chunks(const ts_shape& s) {
@@ -95,6 +95,7 @@ Layout layout(const ts_shape& s, const ts_select& sel) {
   L.mstate = off;   off += align_up(sizeof(uint64_t) * 4 * (size_t)s.batch);
   L.state = off;    off += align_up(sizeof(int32_t) * 8 * (size_t)s.batch);
   L.tiles = off;    off += align_up(sizeof(int32_t) * 2 * (size_t)max_tiles(s));
+  L.cand = off;     off += align_up(sizeof(int2) * ts::kCandCap * (size_t)s.batch);
   const int S = ts::attn_splits(eff_top_k(s, sel), decode_window(s, sel));
   L.attn = off;     off += align_up(sizeof(float) * (ts::kHeadDim + 2) * (size_t)s.batch * H * S);
   L.total = off;
@@ -200,6 +201,7 @@ ts::VoteParams vote_params(const ts_shape& s, const ts_select& sel, const float*
   p.top_p = sel.top_p;
   p.state = at<int32_t>(ws, L.state);
   p.tile_counts = at<int32_t>(ws, L.tiles);
+  p.cand = at<int2>(ws, L.cand);
   p.sel_idx = sel_idx; p.sel_count = sel_count;
   p.H = s.num_q_heads; p.G = s.num_q_heads / s.num_kv_heads; p.b = s.batch; p.top_k = sel.top_k;
   p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxGrid, max_tiles(s)));
@@ -338,7 +340,7 @@ ts_status prefill_select_launch(const ts_shape& s, const ts_select& sel, int max
 
 // ---------------------------------------------------------------- ablations
 struct AblLayout {
-  size_t vote, score, head_scores, head_sel, head_cnt, seg_lens, hist, mstate, state, tiles, total;
+  size_t vote, score, head_scores, head_sel, head_cnt, seg_lens, hist, mstate, state, tiles, cand, total;
   int segs, stride;
   int64_t positions;           // positions the radix select may see in one call
 };
@@ -362,6 +364,7 @@ AblLayout abl_layout(const ts_shape& s, const ts_select& sel, int fn, int block)
   L.mstate = off;      off += align_up(sizeof(uint64_t) * 4 * (size_t)L.segs);
   L.state = off;       off += align_up(sizeof(int32_t) * 8 * (size_t)L.segs);
   L.tiles = off;       off += align_up(sizeof(int32_t) * 2 * (size_t)(cdiv(L.positions, ts::kVoteTile) + L.segs));
+  L.cand = off;        off += align_up(sizeof(int2) * ts::kCandCap * (size_t)L.segs);
   L.total = off;
   return L;
 }
@@ -389,6 +392,7 @@ ts::VoteParams abl_vote_params(const AblLayout& L, void* ws, const float* score,
   p.mstate = at<unsigned long long>(ws, L.mstate);
   p.state = at<int32_t>(ws, L.state);
   p.tile_counts = at<int32_t>(ws, L.tiles);
+  p.cand = at<int2>(ws, L.cand);
   p.sel_idx = sel_idx; p.sel_count = sel_count;
   p.b = segs; p.top_k = top_k;
   p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxGrid, cdiv(L.positions, ts::kVoteTile) + segs));

@@ -11,6 +11,9 @@ constexpr int kVoteTile = 1024;
 // Radix digits of the top-k select over the 32-bit vote keys, most significant first.
 constexpr int kDigitBits0 = 11, kDigitBits1 = 11, kDigitBits2 = 10;
 constexpr int kHistBins = 1 << 11;
+// Keys that share the top 22 bits of the TopK threshold key are listed per request
+// (key, position) up to this many; past it, the write pass counts them in the tiles.
+constexpr int kCandCap = 2048;
 // Selected tokens per attention wavefront and per attention workgroup (4 waves).
 #ifndef TS_ATTN_SPLIT
 #define TS_ATTN_SPLIT 32
@@ -56,8 +59,9 @@ struct VoteParams {
   uint32_t* hist;             // [b][3][kHistBins]
   unsigned long long* mass;   // [b][3][kHistBins] integer vote mass per bin (top-p)
   unsigned long long* mstate; // [b][4] top-p state (target, mass left after digits 0, 1)
-  int32_t* state;             // [b][8] select state (digits found, counts left)
-  int32_t* tile_counts;       // [tiles][2] (greater, equal) per tile
+  int32_t* state;             // [b][8] select state (digits found, counts left, candidates)
+  int32_t* tile_counts;       // [tiles][2] keys above the 22-bit threshold prefix, keys on it
+  int2* cand;                 // [b][kCandCap] (key, position) of the keys on the prefix
   int32_t* sel_idx;           // [b][top_k]
   int32_t* sel_count;         // [b]
   int H, G, b, top_k;

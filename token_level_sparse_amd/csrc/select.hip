@@ -21,10 +21,13 @@
 //   digit's histogram (LDS, then global atomics); each later pass reads the
 //   previous histogram, finds the digit holding the k-th largest key (every
 //   workgroup redoes this scan instead of paying a launch), and histograms the
-//   next digit of the keys sharing the prefix. The last two kernels count, per
-//   tile, keys above the exact threshold and keys equal to it, and write
-//   positions through a prefix over tiles; equal keys are taken in position
-//   order until k is reached, so the result is deterministic.
+//   next digit of the keys sharing the prefix. The second pass also counts, per
+//   tile, the keys above the 22-bit prefix it fixes and lists the keys on that
+//   prefix with their positions (a handful near the k-th vote); the write pass
+//   then knows, for any tile, how many keys of the earlier tiles sort before its
+//   own without a counting pass of its own, and writes positions through a prefix
+//   over tiles; equal keys are taken in position order until k is reached, so the
+//   result is deterministic.
 // * Dynamic top-p budget (RTPurbo team post: dynamic token selection and its
 //   histogram-based top-p decode kernel; UniPrefill page: the minimal set holding
 //   99% of the importance). Each vote also carries an integer mass
@@ -316,7 +319,8 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
 }
 
 // ---------------------------------------------------------------- TopK phases
-// Four kernels, one per phase; every workgroup loops over its share of the tiles.
+// Three kernels (refine digit 1, refine digit 2, write); every workgroup loops over
+// its share of the tiles.
 // (A single cooperative kernel with grid barriers between the phases was measured
 // on MI355X at 321 us per 1M-token step against 26 us for the four launches.)
 template <bool kTopP>
@@ -358,7 +362,7 @@ __device__ void refine_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
   };
   auto record = [&](int r) {
     int32_t* st = p.state + r * 8;
-    if (kPass == 1) { st[0] = sh.dig[0]; st[1] = sh.dig[1]; }
+    if (kPass == 1) { st[0] = sh.dig[0]; st[1] = sh.dig[1]; st[7] = 0; }
     else { st[2] = sh.dig[0]; st[3] = sh.dig[1]; }
     if (kTopP) p.mstate[r * 4 + kPass] = sh.mres;
   };
@@ -422,6 +426,44 @@ __device__ void refine_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
         if (kTopP) atomicAdd(&sh.mass[bin], vote_mass(key_value(key[e])));
       }
     }
+    if (kPass == 2) {
+      // The threshold key shares the 22-bit prefix found here. For the write pass:
+      // how many of this tile's keys lie above the prefix (all selected) and on it,
+      // and the keys on it with their positions, appended to the request's list
+      // (one atomic per wavefront and slot group; entries past kCandCap are counted,
+      // not stored).
+      const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+      int above = 0, on = 0;
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) {
+        const int i = i0 + e * kThreads;
+        const bool in = i < N;
+        const uint32_t top = key[e] >> kShift;
+        above += (in && top > prefix) ? 1 : 0;
+        const bool m = in && top == prefix;
+        on += m ? 1 : 0;
+        const unsigned long long mask = __ballot(m);
+        if (mask) {
+          const int leader = __ffsll((long long)mask) - 1;
+          int base = 0;
+          if (lane == leader) base = atomicAdd(&p.state[r * 8 + 7], __popcll(mask));
+          base = __shfl(base, leader);
+          if (m) {
+            const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
+            if (slot < kCandCap) p.cand[(int64_t)r * kCandCap + slot] = make_int2((int)key[e], i);
+          }
+        }
+      }
+      above = wave_sum_i(above);
+      on = wave_sum_i(on);
+      if (lane == 0) { sh.cnt[0][wave] = above; sh.cnt[1][wave] = on; }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        p.tile_counts[(int64_t)tile * 2 + 0] = sh.cnt[0][0] + sh.cnt[0][1] + sh.cnt[0][2] + sh.cnt[0][3];
+        p.tile_counts[(int64_t)tile * 2 + 1] = sh.cnt[1][0] + sh.cnt[1][1] + sh.cnt[1][2] + sh.cnt[1][3];
+      }
+      __syncthreads();
+    }
   }
   if (cur_r >= 0) flush(cur_r);
 }
@@ -457,41 +499,6 @@ __device__ void threshold(const VoteParams& p, int r, int N, uint32_t& key_t, in
   if (record && threadIdx.x == 0) { st[4] = sh.dig[0]; st[5] = take_eq; st[6] = m_sel; }
 }
 
-// Per tile: keys above the exact threshold and keys equal to it.
-template <bool kTopP>
-__device__ void count_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
-  const int total = sh.tb.tile[p.b];
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int r = find_segment(sh.tb.tile, p.b, tile);
-    const int t = tile - sh.tb.tile[r];
-    const int N = p.seq_lens[r];
-    if (!kTopP && p.top_k >= N) continue;
-    const int i0 = t * kVoteTile + threadIdx.x;
-    uint32_t key[kPerThread];
-    load_keys(p.vote + sh.tb.tok[r], i0, N, key);
-    __syncthreads();
-    uint32_t key_t;
-    int take_eq, m_sel;
-    threshold<kTopP>(p, r, N, key_t, take_eq, m_sel, sh, t == 0);
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const bool in = i0 + e * kThreads < N;
-      gt += in && key[e] > key_t;
-      eq += in && key[e] == key_t;
-    }
-    gt = wave_sum_i(gt);
-    eq = wave_sum_i(eq);
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { sh.cnt[0][wave] = gt; sh.cnt[1][wave] = eq; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      p.tile_counts[(int64_t)tile * 2 + 0] = sh.cnt[0][0] + sh.cnt[0][1] + sh.cnt[0][2] + sh.cnt[0][3];
-      p.tile_counts[(int64_t)tile * 2 + 1] = sh.cnt[1][0] + sh.cnt[1][1] + sh.cnt[1][2] + sh.cnt[1][3];
-    }
-  }
-}
-
 // Ascending positions through a prefix over the request's tiles.
 template <bool kTopP>
 __device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
@@ -520,8 +527,14 @@ __device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
     float x[kPerThread];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) x[e] = lv[min(i0 + e, N - 1)];
-    // counts of the request's earlier tiles
-    // (8-byte loads, four in flight per thread before they are added)
+    // Keys of the request's earlier tiles that sort before this tile's: every key
+    // above the threshold's 22-bit prefix (counted per tile by the previous pass;
+    // 8-byte loads, four in flight per thread before they are added), plus the keys
+    // on the prefix that are greater than or equal to the exact threshold (from the
+    // request's list of prefix keys, or, when the list overflowed, by reading the
+    // earlier tiles that hold prefix keys again).
+    const int n_cand = p.state[r * 8 + 7];
+    const int tile_lo = t * kVoteTile;
     int gtb = 0, eqb = 0;
     typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
     const i32x2_t* tc = reinterpret_cast<const i32x2_t*>(p.tile_counts) + sh.tb.tile[r];
@@ -531,18 +544,51 @@ __device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) v[u] = tc[tt + u * kThreads];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) { gtb += v[u].x; eqb += v[u].y; }
+      for (int u = 0; u < 4; ++u) gtb += v[u].x;
     }
-    for (; tt < t; tt += kThreads) {
-      const i32x2_t v = tc[tt];
-      gtb += v.x;
-      eqb += v.y;
+    for (; tt < t; tt += kThreads) gtb += tc[tt].x;
+    int2 cnd[kCandCap / kThreads];
+    if (n_cand <= kCandCap) {
+#pragma unroll
+      for (int u = 0; u < kCandCap / kThreads; ++u) {
+        const int j = threadIdx.x + u * kThreads;
+        cnd[u] = (j < n_cand) ? p.cand[(int64_t)r * kCandCap + j] : make_int2(0, 0x7fffffff);
+      }
     }
     __syncthreads();
     uint32_t key_t;
     int take_eq, m_sel;
     threshold<kTopP>(p, r, N, key_t, take_eq, m_sel, sh, false);
     if (kTopP && t == 0 && threadIdx.x == 0) p.sel_count[r] = m_sel;
+    if (n_cand <= kCandCap) {
+#pragma unroll
+      for (int u = 0; u < kCandCap / kThreads; ++u) {
+        if (cnd[u].y < tile_lo) {
+          gtb += ((uint32_t)cnd[u].x > key_t) ? 1 : 0;
+          eqb += ((uint32_t)cnd[u].x == key_t) ? 1 : 0;
+        }
+      }
+    } else {
+      // overflow (many keys within 2^-13 of the threshold, e.g. exact ties): read
+      // the earlier tiles that hold prefix keys again, four tiles a round
+      const uint32_t pre22 = key_t >> kDigitBits2;
+      for (int t0 = 0; t0 < t; t0 += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int t1 = t0 + u;
+          if (t1 < t && tc[t1].y > 0) {
+            uint32_t k2[kPerThread];
+            load_keys(lv, t1 * kVoteTile + threadIdx.x, N, k2);
+#pragma unroll
+            for (int e = 0; e < kPerThread; ++e) {
+              const bool on = (t1 * kVoteTile + threadIdx.x + e * kThreads < N) && (k2[e] >> kDigitBits2) == pre22;
+              gtb += (on && k2[e] > key_t) ? 1 : 0;
+              eqb += (on && k2[e] == key_t) ? 1 : 0;
+            }
+          }
+        }
+      }
+    }
     gtb = wave_sum_i(gtb);
     eqb = wave_sum_i(eqb);
     const int wave = threadIdx.x >> 6;
@@ -581,7 +627,6 @@ __global__ __launch_bounds__(kThreads) void select_phase_kernel(VoteParams p) {
   build_tables(sh.tb, p);
   if (kPhase == 1) refine_phase<1, kTopP>(p, sh);
   if (kPhase == 2) refine_phase<2, kTopP>(p, sh);
-  if (kPhase == 3) count_phase<kTopP>(p, sh);
   if (kPhase == 4) write_phase<kTopP>(p, sh);
 }
 
@@ -650,7 +695,6 @@ hipError_t launch_vote_topk_t(const VoteParams& p, hipStream_t s, bool zero_hist
   const dim3 rgrid(std::min(p.grid, kRefineMaxGrid));
   hipLaunchKernelGGL((select_phase_kernel<1, kTopP>), rgrid, block, 0, s, p);
   hipLaunchKernelGGL((select_phase_kernel<2, kTopP>), grid, block, 0, s, p);
-  hipLaunchKernelGGL((select_phase_kernel<3, kTopP>), grid, block, 0, s, p);
   hipLaunchKernelGGL((select_phase_kernel<4, kTopP>), grid, block, 0, s, p);
   return hipGetLastError();
 }
@@ -686,7 +730,6 @@ hipError_t launch_score_select(const VoteParams& p, hipStream_t s) {
   hipLaunchKernelGGL(hist0_kernel, dim3(std::min(p.grid, kVoteMaxGrid)), block, 0, s, p);
   hipLaunchKernelGGL((select_phase_kernel<1, false>), dim3(std::min(p.grid, kRefineMaxGrid)), block, 0, s, p);
   hipLaunchKernelGGL((select_phase_kernel<2, false>), grid, block, 0, s, p);
-  hipLaunchKernelGGL((select_phase_kernel<3, false>), grid, block, 0, s, p);
   hipLaunchKernelGGL((select_phase_kernel<4, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
