@@ -126,6 +126,30 @@ class Layer:
         self.out = torch.empty(1, H, d, dtype=geo.torch_dtype, device=dev)
 
 
+class StepCall:
+    """One tokenselect_decode_step call with its ctypes arguments built once, so a timed
+    loop of short steps spends its host time in the library call alone (the binding's
+    per-call marshalling is tens of microseconds, as long as a Selection Cache hit step
+    on the GPU)."""
+
+    def __init__(self, shape, sel, q, k_pool, v_pool, block_table, seq_lens, cache, hit, out, ws):
+        import ctypes
+        import torch
+        import token_level_sparse_amd as ts
+        self.fn = ts.load_library().tokenselect_decode_step
+        self.cs = cache.c_struct()
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.args = (ctypes.byref(shape), ctypes.byref(sel), P(q), P(k_pool), P(v_pool), P(block_table),
+                     P(seq_lens), ctypes.byref(self.cs), P(hit), P(out), P(ws), ws.numel(),
+                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        self._keep = (shape, sel, q, k_pool, v_pool, block_table, seq_lens, cache, hit, out, ws)
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != 0:
+            raise RuntimeError(f"tokenselect_decode_step failed ({rc})")
+
+
 def stream_ceiling(pools, steps, dev):
     """Time the streaming-bandwidth probe (libts_stream_probe.so) over the same K
     pools the scoring launches read: a plain read of each pool, and the same read
@@ -191,10 +215,11 @@ def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False, ceiling=Fa
     sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, 2.0)
     ws = ts.alloc_workspace(shape, sel, dev)
 
+    calls = [StepCall(shape, sel, L.q, L.k_pool, L.v_pool, L.block_table, L.seq_lens, L.cache,
+                      L.hit, L.out, ws) for L in layers]
+
     def step(s):
-        L = layers[s % n_layers]
-        ts.decode_step(shape, sel, L.q, L.k_pool, L.v_pool, L.block_table, L.seq_lens, L.cache,
-                       L.hit, L.out, ws)
+        calls[s % n_layers]()
 
     for s in range(warmup):
         step(s)
@@ -252,7 +277,7 @@ def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False, ceiling=Fa
     if then is not None:
         res["then"] = then(layers)
     host = L0.host
-    del layers, ws, logits, KC, VC
+    del calls, layers, ws, logits, KC, VC
     torch.cuda.empty_cache()
     return res, host
 
@@ -276,10 +301,11 @@ def time_topp(geo, n_layers, steps, warmup, dev, top_p=0.9, layers=None):
     sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, 2.0, top_p)
     ws = ts.alloc_workspace(shape, sel, dev)
 
+    calls = [StepCall(shape, sel, L.q, L.k_pool, L.v_pool, L.block_table, L.seq_lens, L.cache,
+                      L.hit, L.out, ws) for L in layers]
+
     def step(s):
-        L = layers[s % n_layers]
-        ts.decode_step(shape, sel, L.q, L.k_pool, L.v_pool, L.block_table, L.seq_lens, L.cache,
-                       L.hit, L.out, ws)
+        calls[s % n_layers]()
 
     for s in range(warmup):
         step(s)
@@ -296,7 +322,7 @@ def time_topp(geo, n_layers, steps, warmup, dev, top_p=0.9, layers=None):
     res = {"workload": geo.name, "top_p": top_p, "top_k_cap": geo.top_k, "layers": n_layers,
            "decode_steps_per_s": 1e3 / ms, "ms_per_step": ms,
            "mean_budget": sum(budgets) / len(budgets), "budgets": budgets}
-    del layers, ws, KC, VC
+    del calls, layers, ws, KC, VC
     torch.cuda.empty_cache()
     return res
 
@@ -349,22 +375,22 @@ def time_ablations(geo, dev, reps=10):
 
 def time_score_launches(shape, sel, b, H, B, reps, dev, ws):
     """Mean time of tokenselect_score launches (score + stats kernels) over a batch,
-    each between its own events on the current stream."""
+    launched back to back between two events on the current stream."""
     import torch
     import token_level_sparse_amd as ts
     logits = torch.empty(H * b.total_tokens, dtype=torch.float32, device=dev)
     stats = torch.empty(B * H * 2, dtype=torch.float32, device=dev)
     ts.score(shape, sel, b.q, b.k_pool, b.block_table, b.seq_lens, logits, stats, ws)
     torch.cuda.synchronize()
-    evs = []
+    # back to back between two events: a host stall while the queue still holds work
+    # does not enter the figure
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
     for _ in range(reps):
-        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
         ts.score(shape, sel, b.q, b.k_pool, b.block_table, b.seq_lens, logits, stats, ws)
-        e.record()
-        evs.append((a, e))
+    e.record()
     torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(e) for a, e in evs) / reps
+    ms = a.elapsed_time(e) / reps
     del logits, stats
     return ms
 
@@ -383,8 +409,7 @@ def time_ragged(geo, steps, warmup, dev):
     hit = torch.zeros(B, dtype=torch.int32, device=dev)
     out = torch.empty(B, H, d, dtype=geo.torch_dtype, device=dev)
 
-    def step():
-        ts.decode_step(shape, sel, b.q, b.k_pool, b.v_pool, b.block_table, b.seq_lens, cache, hit, out, ws)
+    step = StepCall(shape, sel, b.q, b.k_pool, b.v_pool, b.block_table, b.seq_lens, cache, hit, out, ws)
 
     for _ in range(warmup):
         step()
@@ -408,7 +433,7 @@ def time_ragged(geo, steps, warmup, dev):
            "score_frac_of_peak": algo / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
            "score_what": "one tokenselect_score launch over the whole batch (about 3.7 GB of K, "
                          "beyond the 256 MB MALL)"}
-    del b, ws
+    del step, b, ws
     torch.cuda.empty_cache()
     return res
 
@@ -437,10 +462,12 @@ def time_cache_sequence(geo, dev):
     hits = torch.zeros(steps, dtype=torch.int32, device=dev)
     out = torch.empty(1, H, d, dtype=geo.torch_dtype, device=dev)
 
+    calls = [StepCall(shape, sel, qs[t], batch.k_pool, batch.v_pool, batch.block_table, lens[t],
+                      cache, hits[t:t + 1], out, ws) for t in range(steps)]
+
     def run():
-        for t in range(steps):
-            ts.decode_step(shape, sel, qs[t], batch.k_pool, batch.v_pool, batch.block_table, lens[t],
-                           cache, hits[t:t + 1], out, ws)
+        for c in calls:
+            c()
 
     run()
     torch.cuda.synchronize()
@@ -470,8 +497,7 @@ def time_cache_sequence(geo, dev):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for t, (a, e) in enumerate(evs):
         a.record()
-        ts.decode_step(shape, sel, qs[t], batch.k_pool, batch.v_pool, batch.block_table, lens[t],
-                       cache, hits[t:t + 1], out, ws)
+        calls[t]()
         e.record()
     torch.cuda.synchronize()
     per = [a.elapsed_time(e) for a, e in evs]
@@ -497,7 +523,7 @@ def time_cache_sequence(geo, dev):
            "score_frac_of_peak_effective": algo / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
            "score_what": "effective: tokenselect_score over the sequence's first step (N = 131072, "
                          "128 MiB of K, held by the 256 MB MALL between launches)"}
-    del batch, ws
+    del calls, batch, ws
     torch.cuda.empty_cache()
     return res
 
