@@ -696,6 +696,45 @@ def _host(t):
     return t.float().cpu().numpy()
 
 
+def kernel_counter_run(dev, steps=4):
+    """Short program for rocprofv3 --pmc passes over the decode-step kernels and the
+    chunk attention: decode steps on the 128K workload (every step reselects), then
+    prefill chunks of 512 queries at 128K; no timing."""
+    import torch
+    import token_level_sparse_amd as ts
+    from synth import workloads as wl
+    geo = wl.workload("llama3-8b-128k")
+    KC, VC = kv_cache(geo, 2, dev)
+    layers = [Layer(geo, l, dev, pools=(KC[l], VC[l])) for l in range(2)]
+    L0 = layers[0]
+    shape = ts.make_shape(geo.num_q_heads, geo.num_kv_heads, 1, L0.block_table.shape[1], L0.total,
+                          geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, 2.0)
+    ws = ts.alloc_workspace(shape, sel, dev)
+    for s in range(steps + 1):
+        L = layers[s % 2]
+        ts.decode_step(shape, sel, L.q, L.k_pool, L.v_pool, L.block_table, L.seq_lens, L.cache, L.hit,
+                       L.out, ws)
+    torch.cuda.synchronize()
+    del layers, ws, KC, VC
+    torch.cuda.empty_cache()
+    g = wl.workload("prefill-llama3-128k")
+    KC, VC = kv_cache(g, 1, dev)
+    cb = wl.make_chunk_batch(g, dev, layer=0, pools=(KC[0], VC[0]))
+    shape = ts.make_shape(g.num_q_heads, g.num_kv_heads, 1, cb.paged.block_table.shape[1], g.seq_len,
+                          g.torch_dtype)
+    sel = ts.make_select(g.top_k, g.n_local, 1.0, g.attn_scale, 2.0)
+    ws = ts.alloc_prefill_workspace(shape, sel, g.chunk, dev)
+    si = torch.empty(1, g.top_k, dtype=torch.int32, device=dev)
+    sc = torch.empty(1, dtype=torch.int32, device=dev)
+    out = torch.empty(1, g.chunk, g.num_q_heads, g.head_dim, dtype=g.torch_dtype, device=dev)
+    for _ in range(steps + 1):
+        ts.prefill_chunk(shape, sel, g.chunk, cb.q_chunk, cb.chunk_lens, cb.paged.k_pool, cb.paged.v_pool,
+                         cb.paged.block_table, cb.seq_lens, si, sc, out, ws)
+    torch.cuda.synchronize()
+    log(f"[kernel counters] {steps + 1} decode steps at 128K and {steps + 1} prefill chunks done")
+
+
 def cpu_baseline(geo, host, dev):
     """The fp64 oracle, as it stands, timed on the host cores beside the GPU figures.
 
@@ -839,6 +878,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="short program for rocprofv3 --pmc passes (scoring launches + a 1 GiB copy)")
+    ap.add_argument("--kernel-counters", action="store_true",
+                    help="short program for rocprofv3 --pmc passes over the decode-step kernels at "
+                         "128K and the prefill chunk attention")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -855,6 +897,9 @@ def main():
     geo = wl.workload("llama3-8b-1m")
     if args.counters:
         counter_run(geo, dev)
+        return
+    if args.kernel_counters:
+        kernel_counter_run(dev)
         return
     topp_run = None if args.no_secondary else (
         lambda layers: guarded("top_p", lambda: time_topp(geo, 8, max(16, args.steps // 2), 4, dev,
