@@ -158,9 +158,11 @@ ts_status tokenselect_vote_topk(const ts_shape* shape, const ts_select* sel,
    [max(0, N_r - max(n_local, 1)), N_r), without duplicates: out[r][h] = sum_{i in S_r}
    softmax_i(attn_scale * <q_h, K_{h/G}[i]>) V_{h/G}[i] (deepnotes selective
    sparse attention formalisation: the selected keys plus the current one, so the
-   current token N_r - 1 is in S_r even with n_local = 0). sel_idx entries outside
-   [0, N_r) are ignored. A request with N_r = 0 has an empty S_r and gets
-   out[r] = 0; its block-table row is not read. */
+   current token N_r - 1 is in S_r even with n_local = 0). The first sel_count[r]
+   entries of row r must be strictly ascending (a repeated entry would be attended
+   twice); entries outside [0, N_r) are ignored. tokenselect_validate_selection checks
+   this on request. A request with N_r = 0 has an empty S_r and gets out[r] = 0; its
+   block-table row is not read. */
 ts_status tokenselect_sparse_attn(const ts_shape* shape, const ts_select* sel,
                                   const void* q, const void* k_pool, const void* v_pool,
                                   const int32_t* block_table, const int32_t* seq_lens,
@@ -310,6 +312,20 @@ ts_status tokenselect_select_ablation(const ts_shape* shape, const ts_select* se
 ts_status tokenselect_validate(const ts_shape* shape, const int32_t* block_table,
                                const int32_t* seq_lens, int64_t num_pool_pages, uint64_t* report,
                                hipStream_t stream);
+
+/* Check of a selection handed to tokenselect_sparse_attn (or kept as Selection
+   Cache state), for callers that build or keep selections themselves: for every
+   request r, 0 <= sel_count[r] <= min(top_k, max(N_r, 0)) and the first sel_count[r]
+   entries of sel_idx[r] lie in [0, N_r) and are strictly ascending. `report` (device
+   uint64[4], caller-owned, 8-byte aligned) receives: [0] the number of violations,
+   [1] the smallest key (r << 32) | e over them, e the entry index or 0xffffffff for a
+   count violation (all ones if there is none), [2] the number of count violations,
+   [3] the sum of the in-range counts. Only batch of `shape` and top_k of `sel` are
+   used. Asynchronous on `stream`: read the report after synchronising. */
+ts_status tokenselect_validate_selection(const ts_shape* shape, const ts_select* sel,
+                                         const int32_t* seq_lens, const int32_t* sel_idx,
+                                         const int32_t* sel_count, uint64_t* report,
+                                         hipStream_t stream);
 
 /* Static text for a status code. */
 const char* tokenselect_status_string(ts_status status);

@@ -270,3 +270,15 @@ def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define TS_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == ts.NOALLOC_SCRATCH_BYTES
+
+
+def test_validate_selection_arguments_checked_before_launch(lib):
+    shape, sel = _shape(batch=4), _sel()
+    f = lib.tokenselect_validate_selection
+    assert f(None, ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, None) == ts.TS_ERR_INVALID_ARG
+    assert f(ctypes.byref(shape), ctypes.byref(sel), FAKE, None, FAKE, FAKE, None) == ts.TS_ERR_INVALID_ARG
+    assert "sel_idx" in lib.tokenselect_last_error().decode()
+    assert f(ctypes.byref(shape), ctypes.byref(_sel(top_k=0)), FAKE, FAKE, FAKE, FAKE, None) == ts.TS_ERR_INVALID_ARG
+    assert f(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE, ctypes.c_void_p(4100), None) == \
+        ts.TS_ERR_INVALID_ARG
+    assert f(ctypes.byref(_shape(batch=0)), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, None) == ts.TS_ERR_INVALID_ARG

@@ -70,3 +70,62 @@ def test_validate_clean_and_planted_violations():
     gh.log(f"  report {got}")
     assert got == want
     assert got[0] >= 4 and got[2] == 2 and got[1] == (1 << 32) | 2
+
+
+def _expected_selection(idx, cnt, lens, top_k):
+    viol, keys, nc, total = 0, [], 0, 0
+    for r in range(len(lens)):
+        n, c = int(lens[r]), int(cnt[r])
+        cap = min(top_k, max(n, 0))
+        ok = 0 <= c <= cap
+        if not ok:
+            viol += 1
+            nc += 1
+            keys.append((r << 32) | 0xFFFFFFFF)
+        else:
+            total += c
+        m = c if ok else min(max(c, 0), top_k)
+        for e in range(m):
+            v = int(idx[r, e])
+            if not (0 <= v < n) or (e > 0 and not int(idx[r, e - 1]) < v):
+                viol += 1
+                keys.append((r << 32) | e)
+    first = min(keys) if keys else (1 << 64) - 1
+    return [viol, first, nc, total]
+
+
+def test_validate_selection_clean_and_planted_violations():
+    # the decode TopK of a ragged batch is a valid selection; then planted faults:
+    # an entry past N_r, a repeated entry, a descending pair, a negative entry, a count
+    # above top_k and a count above N_r
+    geo = wl.workload("llama3-8b-ragged16", batch=6, min_len=100, max_len=6000, top_k=128, seed=4500)
+    gh.log("[validate selection] 6 ragged requests")
+    batch = wl.make_batch(geo, device=DEV)
+    po = gh.run_path(batch, geo)
+    si, sc = po.raw["sel_idx"], po.raw["sel_count"]
+    b = si.shape[0]
+    shape = ts.make_shape(geo.num_q_heads, geo.num_kv_heads, b, batch.block_table.shape[1],
+                          batch.total_tokens, geo.torch_dtype)
+    sel = ts.make_select(geo.top_k, geo.n_local)
+    rep = ts.validate_selection(shape, sel, batch.seq_lens, si, sc)
+    torch.cuda.synchronize()
+    got = _report(rep)
+    lens_h = batch.seq_lens.cpu().numpy()
+    assert got == _expected_selection(si.cpu().numpy(), sc.cpu().numpy(), lens_h, geo.top_k)
+    assert got[0] == 0 and got[3] == sum(min(geo.top_k, int(n)) for n in lens_h)
+
+    si2, sc2 = si.clone(), sc.clone()
+    si2[0, 5] = int(lens_h[0]) + 3          # past N_0 (and breaks ascending after it)
+    si2[1, 7] = si2[1, 6]                   # repeated
+    si2[2, 10], si2[2, 11] = si2[2, 11].clone(), si2[2, 10].clone()   # descending pair
+    si2[3, 0] = -1                          # negative
+    sc2[4] = geo.top_k + 1                  # above top_k
+    lens2 = batch.seq_lens.clone()
+    lens2[5] = 3                            # count above N_5
+    rep = ts.validate_selection(shape, sel, lens2, si2, sc2, report=rep)
+    torch.cuda.synchronize()
+    got = _report(rep)
+    want = _expected_selection(si2.cpu().numpy(), sc2.cpu().numpy(), lens2.cpu().numpy(), geo.top_k)
+    gh.log(f"  report {got}")
+    assert got == want
+    assert got[2] == 2 and got[1] == (0 << 32) | 5

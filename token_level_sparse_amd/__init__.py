@@ -36,6 +36,7 @@ ENTRY_POINTS = (
     "tokenselect_ablation_workspace_size",
     "tokenselect_select_ablation",
     "tokenselect_validate",
+    "tokenselect_validate_selection",
     "tokenselect_status_string",
     "tokenselect_last_error",
 )
@@ -125,6 +126,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tokenselect_select_ablation.restype = ctypes.c_int
     lib.tokenselect_validate.argtypes = [sp, vp, vp, ctypes.c_int64, vp, vp]
     lib.tokenselect_validate.restype = ctypes.c_int
+    lib.tokenselect_validate_selection.argtypes = [sp, selp, vp, vp, vp, vp, vp]
+    lib.tokenselect_validate_selection.restype = ctypes.c_int
     lib.tokenselect_status_string.argtypes = [ctypes.c_int]
     lib.tokenselect_status_string.restype = ctypes.c_char_p
     lib.tokenselect_last_error.argtypes = []
@@ -328,4 +331,16 @@ def validate(shape, block_table, seq_lens, num_pool_pages: int, report=None, str
         report = torch.empty(4, dtype=torch.int64, device=seq_lens.device)
     _check(lib.tokenselect_validate(ctypes.byref(shape), _ptr(block_table), _ptr(seq_lens),
                                     int(num_pool_pages), _ptr(report), _stream(stream)))
+    return report
+
+
+def validate_selection(shape, sel, seq_lens, sel_idx, sel_count, report=None, stream=None) -> torch.Tensor:
+    """tokenselect_validate_selection: returns the device report (int64 [4]: violations,
+    first (request << 32 | entry) key, count violations, sum of the in-range counts);
+    read it after synchronising."""
+    lib = load_library()
+    if report is None:
+        report = torch.empty(4, dtype=torch.int64, device=seq_lens.device)
+    _check(lib.tokenselect_validate_selection(ctypes.byref(shape), ctypes.byref(sel), _ptr(seq_lens),
+                                              _ptr(sel_idx), _ptr(sel_count), _ptr(report), _stream(stream)))
     return report

@@ -715,6 +715,23 @@ ts_status tokenselect_validate(const ts_shape* shape, const int32_t* block_table
   return device_status(ts::launch_validate(p, stream), "validate launch");
 }
 
+ts_status tokenselect_validate_selection(const ts_shape* shape, const ts_select* sel,
+                                         const int32_t* seq_lens, const int32_t* sel_idx,
+                                         const int32_t* sel_count, uint64_t* report,
+                                         hipStream_t stream) {
+  if (!shape || !sel) return fail(TS_ERR_INVALID_ARG, "shape and select must not be NULL");
+  TS_REQUIRE(seq_lens); TS_REQUIRE(sel_idx); TS_REQUIRE(sel_count); TS_REQUIRE(report);
+  if (shape->batch < 1 || shape->batch > ts::kMaxBatch)
+    return fail(TS_ERR_INVALID_ARG, "batch %d outside [1, %d]", shape->batch, ts::kMaxBatch);
+  if (sel->top_k < 1) return fail(TS_ERR_INVALID_ARG, "top_k %d < 1", sel->top_k);
+  if (reinterpret_cast<uintptr_t>(report) % 8) return fail(TS_ERR_INVALID_ARG, "report must be 8-byte aligned");
+  ts::SelValidateParams p{};
+  p.seq_lens = seq_lens; p.sel_idx = sel_idx; p.sel_count = sel_count;
+  p.b = shape->batch; p.top_k = sel->top_k;
+  p.report = reinterpret_cast<unsigned long long*>(report);
+  return device_status(ts::launch_validate_selection(p, stream), "validate_selection launch");
+}
+
 const char* tokenselect_status_string(ts_status s) {
   switch (s) {
     case TS_OK: return "ok";

@@ -198,6 +198,16 @@ struct ValidateParams {
 };
 hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
 
+// Selection checks (tokenselect_validate_selection).
+struct SelValidateParams {
+  const int32_t* seq_lens;
+  const int32_t* sel_idx;     // [b][top_k]
+  const int32_t* sel_count;   // [b]
+  int b, top_k;
+  unsigned long long* report; // [4]
+};
+hipError_t launch_validate_selection(const SelValidateParams& p, hipStream_t s);
+
 hipError_t launch_chunk_mean(const ChunkParams& p, hipStream_t s);
 hipError_t launch_chunk_attn(const ChunkParams& p, hipStream_t s);
 
