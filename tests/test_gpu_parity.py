@@ -204,14 +204,16 @@ def test_attention_given_oracle_selection():
     assert np.max(np.abs(po.out[0] - ref)) <= 2e-2
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_attention_over_every_position(dtype):
+@pytest.mark.parametrize("dtype,H,Hkv", [("bf16", 32, 8), ("f32", 32, 8), ("bf16", 28, 4)])
+def test_attention_over_every_position(dtype, H, Hkv):
     # k = N selects everything: step 5 is then dense attention over the whole cache
-    # (the dense reference the benchmark times at 1M), here at 40000 positions
-    # (313 selection slices of 128 and the window overlapping the selection)
+    # (the dense reference the benchmark times at 1M), here at 40000 positions: 313
+    # selection slices of 128 (626 of 64 at G = 7) and the window overlapping the
+    # selection, so the partials go through both merge launches
     n = 40000
-    geo = wl.workload("llama3-8b-128k", seq_len=n, top_k=n, n_local=512, n_planted=4, dtype=dtype)
-    gh.log(f"[attn over all {n} positions, {dtype}]")
+    geo = wl.workload("llama3-8b-128k", seq_len=n, top_k=n, n_local=512, n_planted=4, dtype=dtype,
+                      num_q_heads=H, num_kv_heads=Hkv)
+    gh.log(f"[attn over all {n} positions, {dtype}, G = {H // Hkv}]")
     batch = wl.make_batch(geo, device=DEV)
     r = batch.requests[0]
     q, K, V = gh.np32(r.q), gh.np32(r.k), gh.np32(r.v)

@@ -59,7 +59,7 @@ constexpr int kMaxGrid = 2048;
 
 // Byte offsets of the workspace regions.
 struct Layout {
-  size_t logits, partials, stats, vote, hist, mass, mstate, state, tiles, cand, attn, total;
+  size_t logits, partials, stats, vote, hist, mass, mstate, state, tiles, cand, attn, attn2, total;
 };
 
 int64_t max_chunks(const ts_shape& s) {
@@ -96,8 +96,10 @@ Layout layout(const ts_shape& s, const ts_select& sel) {
   L.state = off;    off += align_up(sizeof(int32_t) * 8 * (size_t)s.batch);
   L.tiles = off;    off += align_up(sizeof(int32_t) * 2 * (size_t)max_tiles(s));
   L.cand = off;     off += align_up(sizeof(int2) * ts::kCandCap * (size_t)s.batch);
-  const int S = ts::attn_splits(eff_top_k(s, sel), decode_window(s, sel));
+  const int S = ts::attn_splits(eff_top_k(s, sel), decode_window(s, sel), s.num_q_heads / s.num_kv_heads);
   L.attn = off;     off += align_up(sizeof(float) * (ts::kHeadDim + 2) * (size_t)s.batch * H * S);
+  L.attn2 = off;    off += align_up(sizeof(float) * (ts::kHeadDim + 2) * (size_t)s.batch * H *
+                                    ts::attn_combine_chunks(S));
   L.total = off;
   return L;
 }
@@ -128,12 +130,13 @@ ts_status check_shape(const ts_shape* s, const ts_select* sel) {
   if (sel->n_local < 0) return fail(TS_ERR_INVALID_ARG, "n_local %d < 0", sel->n_local);
   if (!(sel->top_p >= 0.0 && sel->top_p <= 1.0))
     return fail(TS_ERR_INVALID_ARG, "top_p %g outside [0, 1] (0 turns the top-p budget off)", sel->top_p);
-  // the attention grid has one workgroup per (request, KV head, slice of 128 selected
-  // or window positions)
-  const int64_t slices = (int64_t)ts::attn_splits(eff_top_k(*s, *sel), decode_window(*s, *sel));
+  // the attention grid has one workgroup per (request, KV head, slice of 128 or 64
+  // selected or window positions)
+  const int64_t slices = (int64_t)ts::attn_splits(eff_top_k(*s, *sel), decode_window(*s, *sel),
+                                                  s->num_q_heads / s->num_kv_heads);
   if ((int64_t)s->batch * s->num_kv_heads * slices > INT32_MAX)
-    return fail(TS_ERR_UNSUPPORTED, "batch x num_kv_heads x (top_k + n_local) / 128 too large for "
-                "the attention grid");
+    return fail(TS_ERR_UNSUPPORTED, "batch x num_kv_heads x attention slices of (top_k + n_local) too "
+                "large for the attention grid");
   return TS_OK;
 }
 
@@ -217,6 +220,7 @@ ts::AttnParams attn_params(const ts_shape& s, const ts_select& sel, const void* 
   p.q = q; p.k_pool = k_pool; p.v_pool = v_pool; p.block_table = bt; p.seq_lens = seq;
   p.sel_idx = sel_idx; p.sel_count = sel_count; p.out = out;
   p.partials = at<float>(ws, L.attn);
+  p.partials2 = at<float>(ws, L.attn2);
   p.H = s.num_q_heads; p.Hkv = s.num_kv_heads; p.b = s.batch; p.stride = s.block_table_stride;
   p.sel_stride = sel.top_k;
   p.top_k = eff_top_k(s, sel);
