@@ -190,6 +190,13 @@ ts::ScoreParams score_params(const ts_shape& s, const ts_select& sel, const void
   return p;
 }
 
+// Decode step: the vote kernel folds the score kernel's per-unit pairs itself (no stats
+// kernel launch) when no request can have more than kFoldMaxPairs of them.
+bool vote_folds_pairs(const ts_shape& s, const ts::ScoreParams& sp) {
+  const int64_t units = std::max<int64_t>(1, cdiv(s.max_total_tokens, (int64_t)sp.chunk_pages * ts::kPage));
+  return units * s.num_q_heads <= ts::kFoldMaxPairs;
+}
+
 ts::VoteParams vote_params(const ts_shape& s, const ts_select& sel, const float* logits,
                            const float* stats, const int32_t* seq, const int32_t* skip,
                            float* vote, int32_t* sel_idx, int32_t* sel_count, void* ws) {
@@ -611,9 +618,10 @@ ts_status decode_step_launch(const ts_shape* shape, const ts_select* sel, const 
   float* logits = at<float>(ws, L.logits);
   float* stats = at<float>(ws, L.stats);
 
-  // Step 0 runs inside the score kernels: the score kernel decides hit[r] and skips
-  // the hits; the stats kernel applies each miss (C_Q <- Q, valid <- 1, cleared
-  // radix histograms) after every read of C_Q.
+  // Step 0 runs inside the score kernel: it decides hit[r] and skips the hits. Each
+  // miss (C_Q <- Q, valid <- 1, cleared radix histograms) is applied after every read
+  // of C_Q: by the stats kernel, or in fold mode by the score kernel (histograms) and
+  // the vote kernel (C_Q, valid), which then also folds the per-unit pairs itself.
   ts::ScoreParams sp = score_params(*shape, *sel, q, k_pool, block_table, seq_lens, nullptr,
                                     logits, stats, ws);
   sp.cache = 1;
@@ -621,10 +629,20 @@ ts_status decode_step_launch(const ts_shape* shape, const ts_select* sel, const 
   sp.hist = at<uint32_t>(ws, L.hist);
   sp.mass = sel->top_p > 0.0 ? at<unsigned long long>(ws, L.mass) : nullptr;
   sp.theta = sel->cos_threshold;
+  ts::VoteParams vp = vote_params(*shape, *sel, logits, stats, seq_lens, hit, nullptr,
+                                  cache->cached_idx, cache->cached_count, ws);
+  if (vote_folds_pairs(*shape, sp)) {
+    sp.fold = 1;
+    vp.fold = 1;
+    vp.partials = sp.partials;
+    vp.chunk_tokens = sp.chunk_pages * ts::kPage;
+    vp.q = q;
+    vp.cached_q = cache->cached_q;
+    vp.valid = cache->valid;
+    vp.q_chunks = shape->num_q_heads * ts::kHeadDim * (shape->dtype == TS_BF16 ? 2 : 4) / 16;
+  }
   if ((st = device_status(ts::launch_score(sp, stream), "score launch")) != TS_OK) return st;
 
-  const ts::VoteParams vp = vote_params(*shape, *sel, logits, stats, seq_lens, hit, nullptr,
-                                        cache->cached_idx, cache->cached_count, ws);
   if ((st = device_status(ts::launch_vote_topk(vp, stream, false), "vote/top-k launch")) != TS_OK)
     return st;
 

@@ -52,6 +52,9 @@ struct ScoreParams {
   int bf16;                   // element type of the pool (and of q unless q_f32)
   int q_f32;                  // q is fp32 whatever the pool type (the chunk mean query)
   int grid;                   // workgroups of the score kernel
+  // Decode step with the pairs folded by the vote kernel (vote_folds_pairs): no stats
+  // kernel runs; the score kernel clears the radix histograms of each request it scores.
+  int fold;
 };
 
 struct VoteParams {
@@ -72,7 +75,22 @@ struct VoteParams {
   int topp;                   // nonzero: dynamic top-p budget with fraction top_p, capped at top_k
   double top_p;
   int grid;                   // workgroups of the tile kernels
+  // Decode step, fold mode: each vote workgroup folds the score kernel's per-unit
+  // pairs of its request itself (head_stats unused) and the workgroup of a request's
+  // first tile applies its Selection Cache miss (C_Q <- Q, valid <- 1).
+  int fold;
+  const float* partials;      // [H][chunks][2] per-unit (max, sum exp), chunks of all requests
+  int chunk_tokens;           // positions per score unit
+  const void* q;              // [b][H * d]
+  void* cached_q;             // [b][H * d]
+  int32_t* valid;             // [b]
+  int q_chunks;               // 16-byte chunks of one request's query
 };
+
+// The vote kernel folds the pairs itself when a request has at most this many
+// (heads x score units): every vote workgroup of the request reads them, and at this
+// size the fold hides under its first logit loads.
+constexpr int kFoldMaxPairs = 16384;
 
 // Integer vote mass of the top-p budget: rint(v * 2^kMassBits) with v = 2^lv. Votes
 // are at most H <= 256, so a request's total stays below 2^48 + N; integer sums are

@@ -270,6 +270,17 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
 
   const int b = p.b;
   const int chunk_tokens = p.chunk_pages * kPage;
+  if (p.fold) {
+    // fold mode runs no stats kernel: the workgroups clear the radix histograms (and
+    // top-p masses) of the TopK that follows, every request's (a cache hit's are
+    // not read)
+    uint4* hg = reinterpret_cast<uint4*>(p.hist);
+    const int64_t nh = (int64_t)b * 3 * kHistBins / 4, nm = p.mass ? 2 * nh : 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nh + nm; i += (int64_t)gridDim.x * 256) {
+      uint4* dst = (i < nh) ? hg + i : reinterpret_cast<uint4*>(p.mass) + (i - nh);
+      *dst = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
   block_prefix(s_tok, b, [&](int r) -> int64_t { return p.seq_lens[r]; });
   block_prefix(s_chunk, b, [&](int r) -> int32_t { return score_chunks(p, r, chunk_tokens); });
 
@@ -500,7 +511,7 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t st) {
                  : p.q_f32 ? launch_score_t<true, true>(p, st)
                            : launch_score_t<true, false>(p, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(stats_kernel, dim3(p.b * p.H), dim3(256), 0, st, p);
+  if (!p.fold) hipLaunchKernelGGL(stats_kernel, dim3(p.b * p.H), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -225,13 +225,122 @@ __device__ __forceinline__ void load_group(const float* zg, int i, float (&x)[G]
   }
 }
 
-template <int G, bool kTopP>
+// KV heads whose logits a thread requests at once (about 128 values in registers).
+template <int G> struct VoteBatch { static constexpr int kB = G == 1 ? 8 : 32 / G; };
+
+// Logits of KV heads [g0, g0 + kB) below Hkv at this thread's positions.
+// `head_stride` = N * G floats per KV head.
+template <int G, int kB>
+__device__ __forceinline__ void load_batch(float (&x)[kB][kPerThread][G], const float* z, int64_t head_stride,
+                                           const int (&idx)[kPerThread], int g0, int Hkv) {
+#pragma unroll
+  for (int j = 0; j < kB; ++j) {
+    if (g0 + j < Hkv) {
+      const float* zg = z + (int64_t)(g0 + j) * head_stride;
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) load_group<G>(zg, idx[e], x[j][e]);
+    }
+  }
+}
+
+// Selection Cache miss of request r in fold mode (every score wave has read C_Q):
+// C_Q <- Q, valid <- 1, by the calling workgroup.
+__device__ __forceinline__ void apply_cache_miss(const VoteParams& p, int r) {
+  const uint4* src = static_cast<const uint4*>(p.q) + (int64_t)r * p.q_chunks;
+  uint4* dst = static_cast<uint4*>(p.cached_q) + (int64_t)r * p.q_chunks;
+  for (int i = threadIdx.x; i < p.q_chunks; i += kThreads) dst[i] = src[i];
+  if (threadIdx.x == 0) p.valid[r] = 1;
+}
+
+// Fold mode: (M_h, log2 Z_h) of every head of request r from the score kernel's
+// per-unit pairs [h][c0, c1) (s_chunk: prefix of the units per request). 8 lanes per
+// head; a lane takes every 8th unit, kIn at a time in registers: their maximum,
+// then one independent exp per pair for the sum, merged into the lane's running
+// pair; a butterfly over the 8 lanes ends it. Every thread must call it.
+__device__ void fold_pairs(const VoteParams& p, const int32_t* s_chunk, int r, float* s_m, float* s_l) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  constexpr int kL = 8, kIn = 40;
+  const int c0 = s_chunk[r], c1 = s_chunk[r + 1], nch = s_chunk[p.b];
+  const int l = threadIdx.x % kL;
+  for (int h0 = 0; h0 < p.H; h0 += kThreads / kL) {
+    const int h = h0 + (int)threadIdx.x / kL;
+    float M = kNegInf, S = 0.f;
+    if (h < p.H) {
+      const f32x2_t* src = reinterpret_cast<const f32x2_t*>(p.partials) + (int64_t)h * nch;
+      for (int c = c0 + l; c < c1; c += kIn * kL) {
+        f32x2_t v[kIn];
+#pragma unroll
+        for (int k = 0; k < kIn; ++k) {
+          const int ck = c + k * kL;
+          v[k] = ck < c1 ? src[ck] : f32x2_t{kNegInf, 0.f};
+        }
+        float mr = kNegInf;
+#pragma unroll
+        for (int k = 0; k < kIn; ++k) mr = fmaxf(mr, v[k].x);
+        float sr = 0.f;
+        if (mr != kNegInf) {
+#pragma unroll
+          for (int k = 0; k < kIn; ++k) sr += v[k].y * exp_via2(v[k].x - mr);
+        }
+        merge_ms(M, S, mr, sr);
+      }
+    }
+#pragma unroll
+    for (int x = 1; x < kL; x <<= 1) merge_ms(M, S, __shfl_xor(M, x), __shfl_xor(S, x));
+    if (l == 0 && h < p.H) {
+      s_m[h] = M;
+      s_l[h] = __builtin_amdgcn_logf(S);
+    }
+  }
+}
+
+// One KV-head group g of a thread's positions: online log-sum-exp in base 2 over the
+// group's G terms at once (one rescale of the running sum per group, then one exp
+// per term); x_hi = (z_hi - M_h) log2e - log2 Z_h, where z - M is exact near the
+// head maximum.
+template <int G>
+__device__ __forceinline__ void vote_group(const float (&x)[kPerThread][G], const float* s_m, const float* s_l,
+                                           int g, float (&m)[kPerThread], float (&s)[kPerThread]) {
+  float mh[G], lh[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) { mh[j] = s_m[g * G + j]; lh[j] = s_l[g * G + j]; }
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    float xv[G];
+    float gm = m[e];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      xv[j] = fmaf(x[e][j] - mh[j], kLog2eF, -lh[j]);
+      gm = fmaxf(gm, xv[j]);
+    }
+    float acc = s[e] * fast_exp2(m[e] - gm);   // 0 while m is -inf (gm is finite)
+#pragma unroll
+    for (int j = 0; j < G; ++j) acc += fast_exp2(xv[j] - gm);
+    s[e] = acc;
+    m[e] = gm;
+  }
+}
+
+// kFold (decode step, small selections): the head statistics come from folding the
+// score kernel's pairs here instead of a stats kernel, the first kB KV heads' logits
+// are requested before that fold so the two overlap, and Selection Cache misses are
+// applied here. Otherwise the statistics are loaded and the logits read group by group.
+template <int G, bool kTopP, bool kFold>
 __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
   __shared__ Tables tb;
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ u64 s_mass[kTopP ? kHistBins : 1];
   __shared__ float s_m[256], s_l[256];
+  __shared__ int32_t s_chunk[kFold ? kMaxBatch + 1 : 1];
   build_tables(tb, p);
+  if (kFold && p.cached_q) {
+    // a request without positions has no vote tile: its Selection Cache miss is
+    // applied here, by workgroup r mod grid
+    for (int r = blockIdx.x; r < p.b; r += gridDim.x) {
+      if (tb.tok[r + 1] != tb.tok[r] || (p.skip && p.skip[r])) continue;
+      apply_cache_miss(p, r);
+    }
+  }
   const int H = p.H, Hkv = H / G;
   const int total = tb.tile[p.b];
   // The LDS histogram accumulates every tile this workgroup takes of one request
@@ -253,20 +362,6 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
     const int r = find_segment(tb.tile, p.b, tile);
     const int t = tile - tb.tile[r];
     const int N = p.seq_lens[r];
-    if (r != cur_r) {
-      if (cur_r >= 0) flush(cur_r);
-      __syncthreads();
-      for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_hist[i] = 0;
-      if (kTopP)
-        for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_mass[i] = 0;
-      // x_hi = (z_hi - M_h) log2e - log2 Z_h; z - M is exact near the head maximum
-      for (int h = threadIdx.x; h < H; h += kThreads) {
-        s_m[h] = p.head_stats[((int64_t)r * H + h) * 2 + 0];
-        s_l[h] = __builtin_amdgcn_logf(p.head_stats[((int64_t)r * H + h) * 2 + 1]);
-      }
-      __syncthreads();
-      cur_r = r;
-    }
     const int i0 = t * kVoteTile + threadIdx.x;
     const float* z = p.logits + tb.tok[r] * H;
     int idx[kPerThread];
@@ -275,31 +370,48 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
     float m[kPerThread], s[kPerThread];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) { m[e] = kNegInf; s[e] = 0.f; }
-#pragma unroll 2
-    for (int g = 0; g < Hkv; ++g) {
-      const float* zg = z + (int64_t)g * N * G;
-      float x[kPerThread][G];
-#pragma unroll
-      for (int e = 0; e < kPerThread; ++e) load_group<G>(zg, idx[e], x[e]);
-      float mh[G], lh[G];
-#pragma unroll
-      for (int j = 0; j < G; ++j) { mh[j] = s_m[g * G + j]; lh[j] = s_l[g * G + j]; }
-#pragma unroll
-      for (int e = 0; e < kPerThread; ++e) {
-        // online log-sum-exp in base 2 over the group's G terms at once: one rescale
-        // of the running sum per group, then one exp per term
-        float xv[G];
-        float gm = m[e];
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          xv[j] = fmaf(x[e][j] - mh[j], kLog2eF, -lh[j]);
-          gm = fmaxf(gm, xv[j]);
+    // fold mode: the first kB KV heads' logits are requested before the head
+    // statistics are folded, so the two overlap
+    constexpr int kB = kFold ? VoteBatch<G>::kB : 1;
+    float x[kB][kPerThread][G];
+    if (kFold) load_batch(x, z, (int64_t)N * G, idx, 0, Hkv);
+    if (r != cur_r) {
+      // a new request: flush the last one's histogram, stage this one's head statistics
+      if (cur_r >= 0) flush(cur_r);
+      __syncthreads();
+      for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_hist[i] = 0;
+      if (kTopP)
+        for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_mass[i] = 0;
+      if (kFold) {
+        if (cur_r < 0)   // score units per request, as the score kernel counts them
+          block_prefix(s_chunk, p.b, [&](int rr) -> int32_t {
+            return max(1, (p.seq_lens[rr] + p.chunk_tokens - 1) / p.chunk_tokens);
+          });
+        fold_pairs(p, s_chunk, r, s_m, s_l);
+        if (p.cached_q && t == 0) apply_cache_miss(p, r);
+      } else {
+        for (int h = threadIdx.x; h < H; h += kThreads) {
+          s_m[h] = p.head_stats[((int64_t)r * H + h) * 2 + 0];
+          s_l[h] = __builtin_amdgcn_logf(p.head_stats[((int64_t)r * H + h) * 2 + 1]);
         }
-        float acc = s[e] * fast_exp2(m[e] - gm);   // 0 while m is -inf (gm is finite)
+      }
+      __syncthreads();
+      cur_r = r;
+    }
+    if constexpr (kFold) {
+      for (int g0 = 0; g0 < Hkv; g0 += kB) {
+        if (g0 > 0) load_batch(x, z, (int64_t)N * G, idx, g0, Hkv);
 #pragma unroll
-        for (int j = 0; j < G; ++j) acc += fast_exp2(xv[j] - gm);
-        s[e] = acc;
-        m[e] = gm;
+        for (int j = 0; j < kB; ++j) {
+          if (g0 + j >= Hkv) break;
+          vote_group<G>(x[j], s_m, s_l, g0 + j, m, s);
+        }
+      }
+    } else {
+#pragma unroll 2
+      for (int g = 0; g < Hkv; ++g) {
+        load_batch(x, z + (int64_t)g * N * G, 0, idx, 0, 1);
+        vote_group<G>(x[0], s_m, s_l, g, m, s);
       }
     }
     float* vout = p.vote + tb.tok[r];
@@ -670,6 +782,23 @@ __global__ void zero_u32(uint32_t* x, int64_t n) {
     x[i] = 0u;
 }
 
+template <bool kTopP, bool kFold>
+hipError_t launch_vote_kernel(const VoteParams& p, hipStream_t s) {
+  const dim3 vgrid(std::min(p.grid, kVoteMaxGrid)), block(kThreads);
+  switch (p.G) {
+    case 1: hipLaunchKernelGGL((vote_kernel<1, kTopP, kFold>), vgrid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((vote_kernel<2, kTopP, kFold>), vgrid, block, 0, s, p); break;
+    case 3: hipLaunchKernelGGL((vote_kernel<3, kTopP, kFold>), vgrid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((vote_kernel<4, kTopP, kFold>), vgrid, block, 0, s, p); break;
+    case 5: hipLaunchKernelGGL((vote_kernel<5, kTopP, kFold>), vgrid, block, 0, s, p); break;
+    case 6: hipLaunchKernelGGL((vote_kernel<6, kTopP, kFold>), vgrid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL((vote_kernel<7, kTopP, kFold>), vgrid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((vote_kernel<8, kTopP, kFold>), vgrid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
 template <bool kTopP>
 hipError_t launch_vote_topk_t(const VoteParams& p, hipStream_t s, bool zero_hist) {
   if (zero_hist) {
@@ -680,18 +809,8 @@ hipError_t launch_vote_topk_t(const VoteParams& p, hipStream_t s, bool zero_hist
                          reinterpret_cast<uint32_t*>(p.mass), 2 * n);
   }
   const dim3 grid(p.grid), block(kThreads);
-  const dim3 vgrid(std::min(p.grid, kVoteMaxGrid));
-  switch (p.G) {
-    case 1: hipLaunchKernelGGL((vote_kernel<1, kTopP>), vgrid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((vote_kernel<2, kTopP>), vgrid, block, 0, s, p); break;
-    case 3: hipLaunchKernelGGL((vote_kernel<3, kTopP>), vgrid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((vote_kernel<4, kTopP>), vgrid, block, 0, s, p); break;
-    case 5: hipLaunchKernelGGL((vote_kernel<5, kTopP>), vgrid, block, 0, s, p); break;
-    case 6: hipLaunchKernelGGL((vote_kernel<6, kTopP>), vgrid, block, 0, s, p); break;
-    case 7: hipLaunchKernelGGL((vote_kernel<7, kTopP>), vgrid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((vote_kernel<8, kTopP>), vgrid, block, 0, s, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  const hipError_t e = p.fold ? launch_vote_kernel<kTopP, true>(p, s) : launch_vote_kernel<kTopP, false>(p, s);
+  if (e != hipSuccess) return e;
   const dim3 rgrid(std::min(p.grid, kRefineMaxGrid));
   hipLaunchKernelGGL((select_phase_kernel<1, kTopP>), rgrid, block, 0, s, p);
   hipLaunchKernelGGL((select_phase_kernel<2, kTopP>), grid, block, 0, s, p);
@@ -708,18 +827,8 @@ hipError_t launch_vote_topk(const VoteParams& p, hipStream_t s, bool zero_hist) 
 hipError_t launch_vote_only(const VoteParams& p, hipStream_t s) {
   const int64_t n = (int64_t)p.b * 3 * kHistBins;
   hipLaunchKernelGGL(zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.hist, n);
-  const dim3 vgrid(std::min(p.grid, kVoteMaxGrid)), block(kThreads);
-  switch (p.G) {
-    case 1: hipLaunchKernelGGL((vote_kernel<1, false>), vgrid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((vote_kernel<2, false>), vgrid, block, 0, s, p); break;
-    case 3: hipLaunchKernelGGL((vote_kernel<3, false>), vgrid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((vote_kernel<4, false>), vgrid, block, 0, s, p); break;
-    case 5: hipLaunchKernelGGL((vote_kernel<5, false>), vgrid, block, 0, s, p); break;
-    case 6: hipLaunchKernelGGL((vote_kernel<6, false>), vgrid, block, 0, s, p); break;
-    case 7: hipLaunchKernelGGL((vote_kernel<7, false>), vgrid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((vote_kernel<8, false>), vgrid, block, 0, s, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  const hipError_t e = launch_vote_kernel<false, false>(p, s);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
