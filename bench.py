@@ -44,7 +44,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-SCORE_SOURCES = ("score.hip", "cache.h", "common.h", "kernels.h")
+SCORE_SOURCES = ("score.hip", "cache.h", "common.h", "kernels.h", "timeline.h")
 
 
 def score_source_digest() -> str:
@@ -735,6 +735,193 @@ def kernel_counter_run(dev, steps=4):
     log(f"[kernel counters] {steps + 1} decode steps at 128K and {steps + 1} prefill chunks done")
 
 
+TIMELINE_KERNELS = {("score", 0): "score_kernel", ("score", 1): "stats_kernel", ("select", 2): "vote_kernel",
+                    ("select", 3): "refine digit 1", ("select", 4): "refine digit 2", ("select", 6): "write",
+                    ("attn", 8): "attn_kernel", ("attn", 9): "combine_kernel", ("prefill", 7): "chunk_attn_bf16"}
+
+
+def timeline_run(dev, reps=5):
+    """Per-wave timeline (libtokenselect_timeline.so, the kernels built with the wall-clock
+    records of csrc/timeline.h): the kernels of one decode step, one after another,
+    with the gaps between them, at 128K (a miss step and a Selection Cache hit step),
+    on the 28/4-head 128K geometry of the cache sequence (miss and hit) and at 1M;
+    the 128K scoring launch without the cache (tokenselect_score; one dispatch round
+    of workgroups) split into dispatch ramp, request tables, stream and tail, and the
+    cosine prologue the decode step adds; and the 128K prefill chunk attention.
+    Medians over `reps` launches; prints a markdown report."""
+    import ctypes
+    import numpy as np
+    import torch
+    import token_level_sparse_amd as ts
+    from token_level_sparse_amd import build as tb
+    from synth import workloads as wl
+    if not os.path.exists(tb.TIMELINE_LIB):
+        log("[timeline] libtokenselect_timeline.so not built")
+        return
+    lib = ts.load_library(tb.TIMELINE_LIB)
+    tus = ("score", "select", "attn", "prefill")
+    for t in tus:
+        getattr(lib, f"ts_timeline_read_{t}").argtypes = [ctypes.c_void_p]
+    KT, KW, KWD = 10, 16384, 10
+    us = lambda x: x * 0.01                                     # s_memrealtime ticks (100 MHz) -> us
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def capture(fn):
+        for t in tus:
+            assert getattr(lib, f"ts_timeline_clear_{t}")() == 0
+        torch.cuda.synchronize()
+        fn()
+        torch.cuda.synchronize()
+        recs = {}
+        for t in tus:
+            buf = np.zeros(KT * KW * KWD, dtype=np.uint64)
+            assert getattr(lib, f"ts_timeline_read_{t}")(ctypes.c_void_p(buf.ctypes.data)) == 0
+            buf = buf.reshape(KT, KW, KWD)
+            for k in range(KT):
+                v = buf[k][buf[k][:, 9] == 1]
+                if len(v) and (t, k) in TIMELINE_KERNELS:
+                    recs[TIMELINE_KERNELS[(t, k)]] = v.astype(np.int64)
+        return recs
+
+    def kernel_rows(runs):
+        """Median over runs of each kernel's first entry, entry spread, span, wave
+        duration p50 / p90, last exit, relative to the first kernel's first entry."""
+        rows = {}
+        for recs in runs:
+            t0 = min(v[:, 0].min() for v in recs.values())
+            for name, v in recs.items():
+                ent, ex = v[:, 0] - t0, v[:, 1] - t0
+                dur = v[:, 1] - v[:, 0]
+                rows.setdefault(name, []).append((ent.min(), ent.max() - ent.min(), ex.max() - ent.min(),
+                                                  np.median(dur), np.percentile(dur, 90), ex.max(), len(v),
+                                                  np.median(ex)))
+        out = []
+        for name, vals in sorted(rows.items(), key=lambda kv: np.median([x[0] for x in kv[1]])):
+            a = np.array(vals, dtype=np.float64)
+            out.append((name, *np.median(a, axis=0)))
+        return out
+
+    def print_step(title, runs):
+        rows = kernel_rows(runs)
+        print(f"\n### {title}\n")
+        print("| kernel | waves | first entry µs | entry spread µs | span µs | wave p50 µs | wave p90 µs | gap before µs |")
+        print("|---|---|---|---|---|---|---|---|")
+        prev = None
+        for name, first, spread, span, d50, d90, last, nw, ex50 in rows:
+            gap = "" if prev is None else f"{us(first - prev):.2f}"
+            print(f"| {name} | {int(nw)} | {us(first):.2f} | {us(spread):.2f} | {us(span):.2f} | {us(d50):.2f} | "
+                  f"{us(d90):.2f} | {gap} |")
+            prev = last
+        print(f"\nstep (first entry to last exit): {us(max(r[6] for r in rows)):.2f} µs; kernel time "
+              f"{us(sum(r[3] for r in rows)):.2f} µs, gaps {us(max(r[6] for r in rows) - sum(r[3] for r in rows)):.2f} µs")
+
+    def score_split(title, runs_nc, runs_c):
+        """tokenselect_score without the cache (runs_nc) and the decode step's score
+        kernel with it (runs_c, a miss step)."""
+        def stats(runs):
+            vals = []
+            for recs in runs:
+                v = recs["score_kernel"]
+                ent = v[:, 0] - v[:, 0].min()
+                ex = v[:, 1] - v[:, 0].min()
+                tables = v[:, 2] - v[:, 0]
+                vals.append((ent.max(), np.median(ent), np.median(tables), np.median(v[:, 1] - v[:, 2]),
+                             np.median(ex), ex.max()))
+            return np.median(np.array(vals, dtype=np.float64), axis=0)
+        ramp, ent50, tables, rest, ex50, span = stats(runs_nc)
+        _, _, tables_c, rest_c, _, span_c = stats(runs_c)
+        print(f"\n### scoring launch split, {title}\n")
+        print("| part | µs |\n|---|---|")
+        print(f"| dispatch ramp: last wave entry after the first (median entry {us(ent50):.2f}) | {us(ramp):.2f} |")
+        print(f"| request tables (entry to tables ready, wave median) | {us(tables):.2f} |")
+        print(f"| stream: tables ready to exit, wave median (no cache) | {us(rest):.2f} |")
+        print(f"| tail: last exit after the median exit | {us(span - ex50):.2f} |")
+        print(f"| kernel span, first entry to last exit (no cache) | {us(span):.2f} |")
+        print(f"| cosine prologue: wave median with the cache minus without (decode miss step) | "
+              f"{us(rest_c - rest):.2f} |")
+        print(f"| kernel span in the decode miss step | {us(span_c):.2f} |")
+
+    print("# Decode-step and scoring-launch timeline (per-wave wall clock, timeline build)")
+    for wname, nl in (("llama3-8b-128k", 8), ("qwen2-7b-cache256", 2), ("llama3-8b-1m", 4)):
+        geo = wl.workload(wname)
+        KC, VC = kv_cache(geo, nl, dev)
+        layers = [Layer(geo, l, dev, False, (KC[l], VC[l])) for l in range(nl)]
+        L0 = layers[0]
+        shape = ts.make_shape(geo.num_q_heads, geo.num_kv_heads, 1, L0.block_table.shape[1], L0.total,
+                              geo.torch_dtype)
+        H = geo.num_q_heads
+        logits = torch.empty(H * L0.total, dtype=torch.float32, device=dev)
+        stats_t = torch.empty(H * 2, dtype=torch.float32, device=dev)
+        runs = {}
+        for tag, theta in (("miss", 2.0), ("hit", -2.0)):
+            sel = ts.make_select(geo.top_k, geo.n_local, 1.0, geo.attn_scale, theta)
+            need = lib.tokenselect_workspace_size(ctypes.byref(shape), ctypes.byref(sel))
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+            def step(L):
+                cs = L.cache.c_struct()
+                assert lib.tokenselect_decode_step(ctypes.byref(shape), ctypes.byref(sel), P(L.q), P(L.k_pool),
+                                                   P(L.v_pool), P(L.block_table), P(L.seq_lens), ctypes.byref(cs),
+                                                   P(L.hit), P(L.out), P(ws), ws.numel(), st) == 0
+
+            def score(L):
+                assert lib.tokenselect_score(ctypes.byref(shape), ctypes.byref(sel), P(L.q), P(L.k_pool),
+                                             P(L.block_table), P(L.seq_lens), P(logits), P(stats_t), P(ws),
+                                             ws.numel(), st) == 0
+            for i in range(2 * nl):
+                step(layers[i % nl])
+            torch.cuda.synchronize()
+            runs[tag] = [capture(lambda: step(layers[i % nl])) for i in range(reps)]
+            if tag == "miss" and wname == "llama3-8b-128k":
+                runs["score"] = [capture(lambda: score(layers[i % nl])) for i in range(reps)]
+            del ws
+        print_step(f"{wname}: decode miss step (every step reselects)", runs["miss"])
+        print_step(f"{wname}: decode Selection Cache hit step", runs["hit"])
+        if wname == "llama3-8b-128k":   # one dispatch round (512 workgroups); 1M has two
+            score_split(wname, runs["score"], runs["miss"])
+        del layers, KC, VC, logits
+        torch.cuda.empty_cache()
+    g = wl.workload("prefill-llama3-128k")
+    KC, VC = kv_cache(g, 2, dev)
+    cbs = [wl.make_chunk_batch(g, dev, layer=l, pools=(KC[l], VC[l])) for l in range(2)]
+    shape = ts.make_shape(g.num_q_heads, g.num_kv_heads, 1, cbs[0].paged.block_table.shape[1], g.seq_len,
+                          g.torch_dtype)
+    sel = ts.make_select(g.top_k, g.n_local, 1.0, g.attn_scale, 2.0)
+    need = lib.tokenselect_prefill_workspace_size(ctypes.byref(shape), ctypes.byref(sel), g.chunk)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    si = [torch.empty(1, g.top_k, dtype=torch.int32, device=dev) for _ in range(2)]
+    sc = [torch.empty(1, dtype=torch.int32, device=dev) for _ in range(2)]
+    out = torch.empty(1, g.chunk, g.num_q_heads, g.head_dim, dtype=g.torch_dtype, device=dev)
+
+    def chunk(l, attn_only):
+        cb = cbs[l]
+        fn = lib.tokenselect_chunk_attn if attn_only else lib.tokenselect_prefill_chunk
+        assert fn(ctypes.byref(shape), ctypes.byref(sel), g.chunk, P(cb.q_chunk), P(cb.chunk_lens),
+                  P(cb.paged.k_pool), P(cb.paged.v_pool), P(cb.paged.block_table), P(cb.seq_lens), P(si[l]),
+                  P(sc[l]), P(out), P(ws), ws.numel(), st) == 0
+    for l in (0, 1, 0, 1):
+        chunk(l, False)
+    torch.cuda.synchronize()
+    pruns = [capture(lambda: chunk(i % 2, True))["chunk_attn_bf16"] for i in range(reps)]
+    vals = []
+    for v in pruns:
+        ent = v[:, 0] - v[:, 0].min()
+        vals.append((ent.max(), np.median(v[:, 2] - v[:, 0]), np.median(v[:, 3] - v[:, 2]),
+                     np.median(v[:, 1] - v[:, 3]), np.median(v[:, 1] - v[:, 0]), (v[:, 1] - v[:, 0].min()).max()))
+    ramp, setup, pro, loop, dur, span = np.median(np.array(vals, dtype=np.float64), axis=0)
+    print("\n### prefill-llama3-128k: chunk attention (chunk of 512, k = 3072, L = 512)\n")
+    print("| part | µs |\n|---|---|")
+    print(f"| dispatch ramp: last wave entry after the first | {us(ramp):.2f} |")
+    print(f"| setup: the split's key list into LDS (wave median) | {us(setup):.2f} |")
+    print(f"| prologue: first blocks staged, first scores (wave median) | {us(pro):.2f} |")
+    print(f"| block loop and partial stores (wave median) | {us(loop):.2f} |")
+    print(f"| wave duration (median) | {us(dur):.2f} |")
+    print(f"| kernel span, first entry to last exit | {us(span):.2f} |")
+    del cbs, KC, VC, ws
+    torch.cuda.empty_cache()
+
+
 def cpu_baseline(geo, host, dev):
     """The fp64 oracle, as it stands, timed on the host cores beside the GPU figures.
 
@@ -881,6 +1068,9 @@ def main():
     ap.add_argument("--kernel-counters", action="store_true",
                     help="short program for rocprofv3 --pmc passes over the decode-step kernels at "
                          "128K and the prefill chunk attention")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-wave timeline of the decode-step kernels, the scoring launch and the chunk "
+                         "attention (libtokenselect_timeline.so); prints a markdown report")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -900,6 +1090,9 @@ def main():
         return
     if args.kernel_counters:
         kernel_counter_run(dev)
+        return
+    if args.timeline:
+        timeline_run(dev)
         return
     topp_run = None if args.no_secondary else (
         lambda layers: guarded("top_p", lambda: time_topp(geo, 8, max(16, args.steps // 2), 4, dev,

@@ -282,3 +282,24 @@ def test_validate_selection_arguments_checked_before_launch(lib):
     assert f(ctypes.byref(shape), ctypes.byref(sel), FAKE, FAKE, FAKE, ctypes.c_void_p(4100), None) == \
         ts.TS_ERR_INVALID_ARG
     assert f(ctypes.byref(_shape(batch=0)), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, None) == ts.TS_ERR_INVALID_ARG
+
+
+def test_timeline_readers_only_in_the_timeline_build():
+    # the per-wave timeline (csrc/timeline.h) is compiled into the measurement library
+    # alone: the product library exports no reader and every instrumented source file
+    # has one in the timeline build
+    import subprocess
+    from token_level_sparse_amd import build as tb
+    if not os.path.exists(tb.TIMELINE_LIB):
+        pytest.skip("timeline library not built")
+
+    def exported(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+        return {l.split()[-1] for l in out.splitlines() if l.strip()}
+    product = exported(tb.LIB)
+    timeline = exported(tb.TIMELINE_LIB)
+    assert not any(n.startswith("ts_timeline_") for n in product)
+    for f in ("score", "select", "attn", "prefill"):
+        assert f"ts_timeline_read_{f}" in timeline and f"ts_timeline_clear_{f}" in timeline
+    # both libraries export the same C ABI
+    assert {n for n in timeline if n.startswith("tokenselect_")} == {n for n in product if n.startswith("tokenselect_")}

@@ -26,6 +26,9 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "timeline.h"
+
+TS_TIMELINE_DEFINE(attn)
 
 namespace ts {
 namespace {
@@ -103,6 +106,7 @@ __device__ __forceinline__ void store_o(float* dst, int col, const float (&o)[8]
 
 template <bool kBf16, int G>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
+  TS_TIMELINE_SCOPE(attn, kTlAttn);
   using T = typename std::conditional<kBf16, uint16_t, float>::type;
   constexpr int kWaves = attn_waves(G), kTile = attn_tile(G);
   constexpr int kAttnRows = 4 * kWaves;              // 4 rows per wave
@@ -267,6 +271,7 @@ constexpr int kCombineChunk = 1024;
 template <bool kBf16, int kPre, bool kFinal>
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(AttnParams p, const float* src, int S_src,
                                                            int n_chunks) {
+  TS_TIMELINE_SCOPE(attn, kTlCombine);
   __shared__ float s_w[kCombineChunk];
   __shared__ float s_red[2];
   const int rh = kFinal ? blockIdx.x : blockIdx.x / n_chunks;

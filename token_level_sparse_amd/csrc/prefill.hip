@@ -47,6 +47,9 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "timeline.h"
+
+TS_TIMELINE_DEFINE(prefill)
 
 namespace ts {
 namespace {
@@ -410,6 +413,7 @@ static_assert(kThreads32 / 64 * 32 == kRows32, "32 rows per wave");
 static_assert(kThreads32 / 64 * 8 == Tile<true>::kKeys, "each wave stages 8 rows of a block");
 __global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void chunk_attn_bf16_kernel(ChunkParams p) {
+  TS_TIMELINE_SCOPE(prefill, kTlChunkAttn);
   constexpr int KB = Tile<true>::kKeys;
   __shared__ __align__(16) char s_k0[Tile<true>::kKeys * Tile<true>::kRow];
   __shared__ __align__(16) char s_k1[Tile<true>::kKeys * Tile<true>::kRow];
@@ -419,6 +423,7 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
   __shared__ int s_geom[5];
   UnitWork w;
   if (!chunk_unit(p, kRows32, s_geom, s_keys, w)) return;
+  TS_TIMELINE_MARK();                            // mark 0: key list of the split in LDS
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l32 = lane & 31, lg = lane >> 5;
   const int rho = w.row0 + 32 * wave + l32;
@@ -527,6 +532,7 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
   f32x16_t sa[2], sb[2];
   qk_block32(s_k0, q, l32, lg, sa);
   __syncthreads();
+  TS_TIMELINE_MARK();                            // mark 1: first blocks staged, S_0 computed
   // Even blocks use the buffers named 0, odd blocks those named 1, fixed per unrolled
   // step: with the staging writes and the reads of an iteration in distinct LDS
   // objects, the compiler does not wait for the staging before the reads.

@@ -22,6 +22,9 @@
 #include "cache.h"
 #include "common.h"
 #include "kernels.h"
+#include "timeline.h"
+
+TS_TIMELINE_DEFINE(score)
 
 namespace ts {
 namespace {
@@ -260,6 +263,7 @@ __device__ __forceinline__ int32_t score_chunks(const ScoreParams& p, int r, int
 
 template <bool kBf16, bool kQ32, int G>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
+  TS_TIMELINE_SCOPE(score, kTlScore);
   using T = typename std::conditional<kBf16, uint16_t, float>::type;
   constexpr int S = Slots<G>::kN;
   using QR = typename QSel<kBf16, kQ32, S>::type;
@@ -283,6 +287,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
   }
   block_prefix(s_tok, b, [&](int r) -> int64_t { return p.seq_lens[r]; });
   block_prefix(s_chunk, b, [&](int r) -> int32_t { return score_chunks(p, r, chunk_tokens); });
+  TS_TIMELINE_MARK_HERE();                     // mark 0: request tables ready (after a barrier)
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __shared__ double s_red[3][4];
@@ -422,6 +427,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
 
 // One workgroup per (request, head): fold the per-unit (max, sum exp) pairs.
 __global__ __launch_bounds__(256) void stats_kernel(ScoreParams p) {
+  TS_TIMELINE_SCOPE(score, kTlStats);
   __shared__ int32_t s_chunk[kMaxBatch + 1];
   __shared__ float s_m[4], s_s[4];
   const int b = p.b, H = p.H;

@@ -41,6 +41,9 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "timeline.h"
+
+TS_TIMELINE_DEFINE(select)
 
 namespace ts {
 namespace {
@@ -327,6 +330,7 @@ __device__ __forceinline__ void vote_group(const float (&x)[kPerThread][G], cons
 // applied here. Otherwise the statistics are loaded and the logits read group by group.
 template <int G, bool kTopP, bool kFold>
 __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
+  TS_TIMELINE_SCOPE(select, kTlVote);
   __shared__ Tables tb;
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ u64 s_mass[kTopP ? kHistBins : 1];
@@ -735,6 +739,7 @@ __device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
 
 template <int kPhase, bool kTopP>
 __global__ __launch_bounds__(kThreads) void select_phase_kernel(VoteParams p) {
+  TS_TIMELINE_SCOPE(select, kTlVote + kPhase);
   __shared__ SelectShared<kTopP> sh;
   build_tables(sh.tb, p);
   if (kPhase == 1) refine_phase<1, kTopP>(p, sh);
