@@ -66,30 +66,36 @@ static_assert(kChunkPartStride == kHeadDim + 4, "partial row layout");
 // Geometry of request r's chunk. Out-of-contract lengths are clamped so that no
 // access leaves the request's pages (results are then unspecified).
 struct ChunkGeom {
-  int c, P, w0, n_sel, base, N;
+  int c, P, w0, N;
 };
 
-__device__ int lower_bound_i32(const int32_t* a, int n, int x) {
+// Number of entries of the ascending a[0, n) below x, found by one wave (every lane
+// returns it): each round probes the 64 entries lo + step (l + 1) - 1 of the run
+// [lo, hi) the answer lies in; the probes below x form a prefix of k lanes, so the
+// answer is in [lo + k step, min(hi, lo + (k + 1) step - 1)]. A round shrinks the run
+// 64-fold; with step 1 the probes cover it and the answer is exact.
+__device__ int count_below(const int32_t* a, int n, int x) {
+  const int lane = threadIdx.x & (kWave - 1);
   int lo = 0, hi = n;
   while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a[mid] < x) lo = mid + 1; else hi = mid;
+    const int step = (hi - lo + kWave - 1) / kWave;
+    const int pos = lo + step * (lane + 1) - 1;
+    const bool below = pos < hi && a[pos] < x;
+    const int k = __popcll(__ballot(below));
+    const int nlo = lo + step * k;
+    hi = min(hi, nlo + step - 1);
+    lo = nlo;
+    if (step == 1) hi = lo;
   }
   return lo;
 }
 
-__device__ ChunkGeom chunk_geom(const ChunkParams& p, int r, bool with_sel) {
+__device__ ChunkGeom chunk_geom(const ChunkParams& p, int r) {
   ChunkGeom gm;
   gm.N = max(0, p.seq_lens[r]);
   gm.c = min(max(p.chunk_lens[r], 0), min(p.max_chunk, gm.N));
   gm.P = gm.N - gm.c;
   gm.w0 = max(0, gm.P - p.n_local);
-  gm.n_sel = 0;
-  if (with_sel) {
-    const int cnt = min(max(p.sel_count[r], 0), min(p.sel_stride, gm.P));
-    gm.n_sel = lower_bound_i32(p.sel_idx + (int64_t)r * p.sel_stride, cnt, gm.w0);
-  }
-  gm.base = gm.n_sel + gm.P - gm.w0;
   return gm;
 }
 
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(kMeanThreads) void chunk_mean_kernel(ChunkParams p)
   __shared__ double s_acc[kMeanGroups][kHeadDim];
   __shared__ double s_part[kMeanSlices][kHeadDim];
   const int r = blockIdx.x / p.H, h = blockIdx.x - (blockIdx.x / p.H) * p.H;
-  const ChunkGeom gm = chunk_geom(p, r, false);
+  const ChunkGeom gm = chunk_geom(p, r);
   const int dc = threadIdx.x & 15, rg = threadIdx.x >> 4;
   double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
   const int64_t row_stride = (int64_t)p.H * kHeadDim;
@@ -349,15 +355,21 @@ __device__ bool chunk_unit(const ChunkParams& p, int rows_per_wg, int* s_geom, i
   w.split = u % p.splits;
   w.g = (u / p.splits) % Hkv;
   w.r = u / (p.splits * Hkv);
-  if (threadIdx.x == 0) {
-    const ChunkGeom gm = chunk_geom(p, w.r, true);
-    s_geom[0] = gm.c; s_geom[1] = gm.base; s_geom[2] = gm.w0; s_geom[3] = gm.n_sel; s_geom[4] = gm.N;
-    // for the combine kernel (every workgroup of the request writes the same value)
-    if (w.split == 0 && tile == 0) p.key_base[w.r] = gm.base;
-  }
-  __syncthreads();
-  const int c = s_geom[0];
-  w.base = s_geom[1];
+  // The request's geometry (uniform scalar loads in every thread); the number of
+  // TopK entries below the window start w0 is found by every wave with a 64-way
+  // search of the ascending TopK: each round probes 64 evenly spaced entries at once
+  // and keeps the run between the last probe below w0 and the first one not below
+  // (two rounds for a few thousand entries, instead of a binary search of dependent
+  // loads).
+  const ChunkGeom g0 = chunk_geom(p, w.r);
+  const int cnt = min(max(p.sel_count[w.r], 0), min(p.sel_stride, g0.P));
+  const int32_t* sel_r = p.sel_idx + (int64_t)w.r * p.sel_stride;
+  const int n_sel = count_below(sel_r, cnt, g0.w0);
+  const int gbase = n_sel + g0.P - g0.w0;
+  // for the combine kernel (every workgroup of the request writes the same value)
+  if (w.split == 0 && tile == 0 && threadIdx.x == 0) p.key_base[w.r] = gbase;
+  const int c = g0.c;
+  w.base = gbase;
   w.rows = c * w.G;
   w.row0 = tile * rows_per_wg;
   if (w.row0 >= w.rows) return false;
@@ -368,11 +380,10 @@ __device__ bool chunk_unit(const ChunkParams& p, int rows_per_wg, int* s_geom, i
   w.x_end = min(w.x_begin + p.split_keys, n_vis);
   // key-list entry x: the x-th selected position below the window (the TopK is
   // ascending), then the window and the chunk [w0, P + c); its row of this KV head
-  const int w0 = s_geom[2], n_sel = s_geom[3], N = s_geom[4];
-  const int32_t* sel = p.sel_idx + (int64_t)w.r * p.sel_stride;
+  const int w0 = g0.w0, N = g0.N;
   const int32_t* bt = p.block_table + (int64_t)w.r * p.stride;
   for (int x = w.x_begin + (int)threadIdx.x; x < w.x_end; x += blockDim.x) {
-    int pos = x < n_sel ? sel[x] : w0 + (x - n_sel);
+    int pos = x < n_sel ? sel_r[x] : w0 + (x - n_sel);
     pos = min(max(pos, 0), max(N - 1, 0));
     const int64_t page = bt[pos >> 4];
     s_keys[x - w.x_begin] = ((page * Hkv + w.g) * kPage + (pos & (kPage - 1))) * kHeadDim;
@@ -648,7 +659,7 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkParams p) {
   if (row >= rows) return;
   const int j = (int)((row / p.H) % p.max_chunk);
   const int r = (int)(row / ((int64_t)p.H * p.max_chunk));
-  const ChunkGeom gm = chunk_geom(p, r, false);
+  const ChunkGeom gm = chunk_geom(p, r);
   if (j >= gm.c) return;
   // splits that hold entries visible to chunk query j (the attention kernel stored the
   // request's key-list base, so no search of the TopK list here)
