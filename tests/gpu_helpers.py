@@ -167,7 +167,12 @@ def check_request(po: PathOut, r: int, req: wl.Request, geo: wl.Geometry, top_k=
     n_diff = check_topk(po.T[r], po.vote[r], sel, rel, k)
     err = check_attention(po.out[r], q, K, V, po.T[r], K.shape[1], L, geo.attn_scale,
                           geo.dtype == "f32")
-    return dict(n_loose=n_loose, n_diff=n_diff, attn_err=err)
+    # n_loose: votes outside a strict relative 1e-4 (inside band (a) through the fp32
+    # budget r_i); max_r: the largest finite r_i of the request; n_under: positions whose
+    # fp64 vote underflows to 0 (their r_i is unbounded: only the log-domain band applies)
+    fin = np.isfinite(rel)
+    return dict(n_loose=n_loose, max_r=float(np.max(rel[fin])) if fin.any() else 0.0,
+                n_under=int((~fin).sum()), n_diff=n_diff, attn_err=err)
 
 
 # ---------------------------------------------------------------- chunk-wise prefill
