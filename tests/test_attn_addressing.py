@@ -13,24 +13,19 @@ import pytest
 
 PAGE = 16
 ATTN_SPLIT = 32            # selected slots per wave
+ATTN_TILE = 4 * ATTN_SPLIT  # slots per workgroup
 
 
-def attn_waves(G):
-    return 2 if G > 4 else 4
+def attn_splits(top_k, window):
+    return -(-top_k // ATTN_TILE) + -(-window // ATTN_TILE)
 
 
-def attn_splits(top_k, window, G):
-    tile = attn_waves(G) * ATTN_SPLIT           # slots per workgroup
-    return -(-top_k // tile) + -(-window // tile)
-
-
-def kernel_gathers(seq_lens, sel_idx, sel_count, block_table, Hkv, top_k, n_local, G=4):
+def kernel_gathers(seq_lens, sel_idx, sel_count, block_table, Hkv, top_k, n_local):
     """Yield (r, bt_index) for every block-table read and (r, phys) for every row
     gather the attention kernel issues, following its slot-to-token rule."""
     b, sel_stride = sel_idx.shape
     window = max(1, n_local)                    # the library's decode window
-    S = attn_splits(top_k, window, G)
-    ATTN_TILE = attn_waves(G) * ATTN_SPLIT
+    S = attn_splits(top_k, window)
     nT = -(-top_k // ATTN_TILE)
     reads, gathers = [], []
     for blk in range(b * Hkv * S):
@@ -41,7 +36,7 @@ def kernel_gathers(seq_lens, sel_idx, sel_count, block_table, Hkv, top_k, n_loca
             continue                            # the workgroup writes the empty partial only
         lstart = max(0, N - window)
         cnt = min(int(sel_count[r]), sel_stride) if s < nT else 0
-        for wave in range(attn_waves(G)):
+        for wave in range(4):
             for lane in range(ATTN_SPLIT):
                 tok = N - 1
                 if s < nT:
@@ -58,9 +53,8 @@ def kernel_gathers(seq_lens, sel_idx, sel_count, block_table, Hkv, top_k, n_loca
     return reads, gathers
 
 
-@pytest.mark.parametrize("G", [4, 7])
 @pytest.mark.parametrize("n_local", [0, 1, 8, 512])
-def test_every_gather_stays_in_reached_pages(n_local, G):
+def test_every_gather_stays_in_reached_pages(n_local):
     rng = np.random.default_rng(5)
     pool_pages, stride, top_k = 400, 40, 300
     lens = np.array([0, 17, 1, 640, 0, 300])
@@ -74,7 +68,7 @@ def test_every_gather_stays_in_reached_pages(n_local, G):
         used += pages
     sel_idx = rng.integers(-50, 1000, size=(b, top_k))  # stale, negative and past-N entries
     sel_count = np.array([top_k, 5, 0, top_k, 7, 299])
-    reads, gathers = kernel_gathers(lens, sel_idx, sel_count, bt, 2, top_k, n_local, G)
+    reads, gathers = kernel_gathers(lens, sel_idx, sel_count, bt, 2, top_k, n_local)
     assert reads, "no gathers emulated"
     for (r, p), (_, phys) in zip(reads, gathers):
         assert lens[r] > 0

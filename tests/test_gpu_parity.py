@@ -212,8 +212,8 @@ def test_attention_given_oracle_selection():
 def test_attention_over_every_position(dtype, H, Hkv):
     # k = N selects everything: step 5 is then dense attention over the whole cache
     # (the dense reference the benchmark times at 1M), here at 40000 positions: 313
-    # selection slices of 128 (626 of 64 at G = 7) and the window overlapping the
-    # selection, so the partials go through both merge launches
+    # selection slices of 128 and the window overlapping the selection, so the
+    # partials go through both merge launches
     n = 40000
     geo = wl.workload("llama3-8b-128k", seq_len=n, top_k=n, n_local=512, n_planted=4, dtype=dtype,
                       num_q_heads=H, num_kv_heads=Hkv)

@@ -96,7 +96,7 @@ Layout layout(const ts_shape& s, const ts_select& sel) {
   L.state = off;    off += align_up(sizeof(int32_t) * 8 * (size_t)s.batch);
   L.tiles = off;    off += align_up(sizeof(int32_t) * 2 * (size_t)max_tiles(s));
   L.cand = off;     off += align_up(sizeof(int2) * ts::kCandCap * (size_t)s.batch);
-  const int S = ts::attn_splits(eff_top_k(s, sel), decode_window(s, sel), s.num_q_heads / s.num_kv_heads);
+  const int S = ts::attn_splits(eff_top_k(s, sel), decode_window(s, sel));
   L.attn = off;     off += align_up(sizeof(float) * (ts::kHeadDim + 2) * (size_t)s.batch * H * S);
   L.attn2 = off;    off += align_up(sizeof(float) * (ts::kHeadDim + 2) * (size_t)s.batch * H *
                                     ts::attn_combine_chunks(S));
@@ -130,10 +130,9 @@ ts_status check_shape(const ts_shape* s, const ts_select* sel) {
   if (sel->n_local < 0) return fail(TS_ERR_INVALID_ARG, "n_local %d < 0", sel->n_local);
   if (!(sel->top_p >= 0.0 && sel->top_p <= 1.0))
     return fail(TS_ERR_INVALID_ARG, "top_p %g outside [0, 1] (0 turns the top-p budget off)", sel->top_p);
-  // the attention grid has one workgroup per (request, KV head, slice of 128 or 64
-  // selected or window positions)
-  const int64_t slices = (int64_t)ts::attn_splits(eff_top_k(*s, *sel), decode_window(*s, *sel),
-                                                  s->num_q_heads / s->num_kv_heads);
+  // the attention grid has one workgroup per (request, KV head, slice of 128 selected
+  // or window positions)
+  const int64_t slices = (int64_t)ts::attn_splits(eff_top_k(*s, *sel), decode_window(*s, *sel));
   if ((int64_t)s->batch * s->num_kv_heads * slices > INT32_MAX)
     return fail(TS_ERR_UNSUPPORTED, "batch x num_kv_heads x attention slices of (top_k + n_local) too "
                 "large for the attention grid");

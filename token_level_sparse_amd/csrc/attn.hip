@@ -11,17 +11,17 @@
 // united with the window [N - L, N), L >= 1 (with a window size of 0 the window is
 // the current token alone); TopK entries inside the window are skipped
 // because the window covers them, so no sort or merge is needed. A workgroup
-// covers 128 selected slots (4 waves of 32; 64 slots in 2 waves at G > 4) of the
-// TopK list or of the window, for one KV head and all G query heads of its group:
-// each key and value row (256 B in bf16) is gathered once through the block table.
-// Lane = 16 * row + col: the 4 rows of a wave take every 4th token and col picks 8
-// dims; the inner products run on bf16 pairs (v_dot2_f32_bf16) and DPP sums finish
-// them, and each row keeps a (max, sum, o[8 dims]) online softmax in registers. The
-// rows of the workgroup leave their partials in LDS and merge there in one pass
+// covers 128 selected slots (4 waves of 32) of the TopK list or of the window, for
+// one KV head and all G query heads of its group: each key and value row (256 B in
+// bf16) is gathered once through the block table. Lane = 16 * row + col: the 4 rows
+// of a wave take every 4th token and col picks 8 dims; the inner products run on
+// bf16 pairs (v_dot2_f32_bf16) and DPP sums finish them, and each row keeps a
+// (max, sum, o[8 dims]) online softmax in registers. The 16 rows of the workgroup
+// leave their partials in LDS (G x 16 x 132 floats) and merge there in one pass
 // into one partial per workgroup (no cross-row shuffles); a small kernel merges
-// the partials of each (request, head) and rounds the output. (Merging in
-// the last workgroup behind an atomic ticket was measured slower: the device-scope
-// release each workgroup then needs writes back its XCD's whole L2.)
+// the partials of each (request, head) and rounds the output. (Merging in the last
+// workgroup behind an atomic ticket was measured slower: the device-scope release
+// each workgroup then needs writes back its XCD's whole L2.)
 #include <type_traits>
 
 #include "common.h"
@@ -108,12 +108,12 @@ template <bool kBf16, int G>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   TS_TIMELINE_SCOPE(attn, kTlAttn);
   using T = typename std::conditional<kBf16, uint16_t, float>::type;
-  constexpr int kWaves = attn_waves(G), kTile = attn_tile(G);
-  constexpr int kAttnRows = 4 * kWaves;              // 4 rows per wave
+  constexpr int kTile = kAttnTile;
+  constexpr int kAttnRows = 16;                      // 4 waves x 4 rows
   __shared__ __align__(16) float s_part[kAttnRows][G][kPartStride];
   __shared__ float s_w[G][kAttnRows];
   __shared__ float s_max[G];
-  const int S = attn_splits(p.top_k, p.n_local, G);
+  const int S = attn_splits(p.top_k, p.n_local);
   const int nT = (p.top_k + kTile - 1) / kTile;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = lane >> 4, col = lane & 15;
@@ -345,7 +345,7 @@ void launch_final_combine(const AttnParams& p, const float* src, int S, hipStrea
 template <bool kBf16>
 hipError_t launch_attn_t(const AttnParams& p, hipStream_t st) {
   const int G = p.H / p.Hkv;
-  dim3 grid(p.b * p.Hkv * attn_splits(p.top_k, p.n_local, G)), block(64 * attn_waves(G));
+  dim3 grid(p.b * p.Hkv * attn_splits(p.top_k, p.n_local)), block(256);
   switch (G) {
     case 1: hipLaunchKernelGGL((attn_kernel<kBf16, 1>), grid, block, 0, st, p); break;
     case 2: hipLaunchKernelGGL((attn_kernel<kBf16, 2>), grid, block, 0, st, p); break;
@@ -357,7 +357,7 @@ hipError_t launch_attn_t(const AttnParams& p, hipStream_t st) {
     case 8: hipLaunchKernelGGL((attn_kernel<kBf16, 8>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
-  const int S = attn_splits(p.top_k, p.n_local, G);
+  const int S = attn_splits(p.top_k, p.n_local);
   if (S <= kAttnCombineSpan) {
     launch_final_combine<kBf16>(p, p.partials, S, st);
   } else {

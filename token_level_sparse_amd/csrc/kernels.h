@@ -14,16 +14,12 @@ constexpr int kHistBins = 1 << 11;
 // Keys that share the top 22 bits of the TopK threshold key are listed per request
 // (key, position) up to this many; past it, the write pass counts them in the tiles.
 constexpr int kCandCap = 2048;
-// Selected tokens per attention wavefront.
+// Selected tokens per attention wavefront and per attention workgroup (4 waves).
 #ifndef TS_ATTN_SPLIT
 #define TS_ATTN_SPLIT 32
 #endif
 constexpr int kAttnSplit = TS_ATTN_SPLIT;
-// Waves per attention workgroup: 4, or 2 at G > 4, where the LDS partials of 16 rows
-// (4 per wave, G heads each) would pass 34 KiB; workgroups with about 60 KiB of LDS
-// were measured to start up to 5 us late. Selected slots per workgroup: waves x split.
-__host__ __device__ constexpr int attn_waves(int G) { return G > 4 ? 2 : 4; }
-__host__ __device__ constexpr int attn_tile(int G) { return attn_waves(G) * kAttnSplit; }
+constexpr int kAttnTile = 4 * kAttnSplit;
 
 struct ScoreParams {
   const void* q;              // [b][H][d]
@@ -177,9 +173,8 @@ __host__ __device__ inline int chunk_splits(int top_k, int n_local, int max_chun
   return (int)((chunk_max_keys(top_k, n_local, max_chunk) + split_keys - 1) / split_keys);
 }
 
-__host__ __device__ inline int attn_splits(int top_k, int n_local, int G) {
-  const long long t = attn_tile(G);
-  return (int)(((long long)top_k + t - 1) / t + ((long long)n_local + t - 1) / t);
+__host__ __device__ inline int attn_splits(int top_k, int n_local) {
+  return (int)(((long long)top_k + kAttnTile - 1) / kAttnTile + ((long long)n_local + kAttnTile - 1) / kAttnTile);
 }
 // Partials one workgroup of the first merge launch takes when a selection has more
 // than this many; the partials that launch leaves (0 when the final merge reads the
