@@ -65,7 +65,10 @@ struct Layout {
 int64_t max_chunks(const ts_shape& s) {
   return cdiv(s.max_total_tokens, (int64_t)kMinChunkPages * ts::kPage) + s.batch;
 }
-int64_t max_tiles(const ts_shape& s) { return cdiv(s.max_total_tokens, ts::kVoteTile) + s.batch; }
+// Most vote tiles a batch can have: sum_r ceil(N_r / V) <= floor((T + b (V - 1)) / V).
+int64_t max_tiles(const ts_shape& s) {
+  return cdiv(s.max_total_tokens + (int64_t)(s.batch - 1) * (ts::kVoteTile - 1), ts::kVoteTile);
+}
 
 // Attention work items per (request, KV head): TopK list plus window, capped by
 // the largest possible N.
@@ -178,6 +181,7 @@ ts::ScoreParams score_params(const ts_shape& s, const ts_select& sel, const void
   ts::ScoreParams p{};
   p.q = q; p.k_pool = k_pool; p.block_table = bt; p.seq_lens = seq; p.skip = skip;
   p.logits = logits; p.head_stats = stats; p.partials = at<float>(ws, L.partials);
+  p.pair_stride = (int)max_chunks(s);
   p.H = s.num_q_heads; p.Hkv = s.num_kv_heads; p.b = s.batch; p.stride = s.block_table_stride;
   p.chunk_pages = score_chunk_pages(s);
   p.score_scale = sel.score_scale;
@@ -212,6 +216,9 @@ ts::VoteParams vote_params(const ts_shape& s, const ts_select& sel, const float*
   p.tile_counts = at<int32_t>(ws, L.tiles);
   p.cand = at<int2>(ws, L.cand);
   p.sel_idx = sel_idx; p.sel_count = sel_count;
+  // the select kernels may read the workspace vote buffer (max_total_tokens floats) up to
+  // its end before they know N; a caller's buffer is read only below N
+  p.max_tokens = vote ? 0 : (int)std::min<int64_t>(s.max_total_tokens, INT32_MAX);
   p.H = s.num_q_heads; p.G = s.num_q_heads / s.num_kv_heads; p.b = s.batch; p.top_k = sel.top_k;
   p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxGrid, max_tiles(s)));
   return p;
@@ -634,6 +641,10 @@ ts_status decode_step_launch(const ts_shape* shape, const ts_select* sel, const 
     sp.fold = 1;
     vp.fold = 1;
     vp.partials = sp.partials;
+    vp.pair_stride = sp.pair_stride;
+    // most 512-position tiles a batch can have: sum_r ceil(N_r / 512)
+    vp.fold_grid = (int)std::min<int64_t>(
+        2048, cdiv(shape->max_total_tokens + (int64_t)(shape->batch - 1) * 511, 512));
     vp.chunk_tokens = sp.chunk_pages * ts::kPage;
     vp.q = q;
     vp.cached_q = cache->cached_q;

@@ -40,7 +40,8 @@ struct ScoreParams {
   unsigned long long* mass;   // [b][3][kHistBins] or null
   double theta;
   float* logits;              // ragged [H][N_r] per request
-  float* partials;            // [H][chunks][2] per-chunk (max, sum exp), chunks of all requests
+  float* partials;            // [H][pair_stride][2] per-unit (max, sum exp), units of all requests
+  int pair_stride;            // units per head row of partials (at least the launch's units)
   float* head_stats;          // [b][H][2]
   int H, Hkv, b, stride;
   int chunk_pages;            // pages per work unit
@@ -67,6 +68,7 @@ struct VoteParams {
   int2* cand;                 // [b][kCandCap] (key, position) of the keys on the prefix
   int32_t* sel_idx;           // [b][top_k]
   int32_t* sel_count;         // [b]
+  int max_tokens;             // positions the vote buffer holds (first-tile loads before the tables)
   int H, G, b, top_k;
   int topp;                   // nonzero: dynamic top-p budget with fraction top_p, capped at top_k
   double top_p;
@@ -75,8 +77,10 @@ struct VoteParams {
   // pairs of its request itself (head_stats unused) and the workgroup of a request's
   // first tile applies its Selection Cache miss (C_Q <- Q, valid <- 1).
   int fold;
-  const float* partials;      // [H][chunks][2] per-unit (max, sum exp), chunks of all requests
+  const float* partials;      // [H][pair_stride][2] per-unit (max, sum exp), units of all requests
+  int pair_stride;
   int chunk_tokens;           // positions per score unit
+  int fold_grid;              // workgroups of the fold-mode vote kernel (512-position tiles)
   const void* q;              // [b][H * d]
   void* cached_q;             // [b][H * d]
   int32_t* valid;             // [b]

@@ -274,6 +274,17 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
 
   const int b = p.b;
   const int chunk_tokens = p.chunk_pages * kPage;
+  __shared__ double s_red[3][4];
+  // One request: its length is a scalar load at the start (no wait behind vector
+  // loads), and the Selection Cache test needs no request table, so its query chunks
+  // go out at once and the request is decided once, before the units.
+  // (Unconditional scalar loads: a null skip or valid array reads seq_lens instead.)
+  const int n0 = p.seq_lens[0];
+  const int skip0 = (p.skip ? p.skip : p.seq_lens)[0];
+  const int valid0 = (p.valid ? p.valid : p.seq_lens)[0];
+  const bool decide_first = p.cache && b == 1;
+  CachePre cpre;
+  if (decide_first && p.theta <= kCacheNeverHit) cache_preload<kBf16>(p.q, p.cached_q, 0, p.H * kHeadDim, cpre);
   if (p.fold) {
     // fold mode runs no stats kernel: the workgroups clear the radix histograms (and
     // top-p masses) of the TopK that follows, every request's (a cache hit's are
@@ -285,14 +296,30 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
       *dst = make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  block_prefix(s_tok, b, [&](int r) -> int64_t { return p.seq_lens[r]; });
-  block_prefix(s_chunk, b, [&](int r) -> int32_t { return score_chunks(p, r, chunk_tokens); });
+  if (b == 1) {
+    if (threadIdx.x == 0) {
+      s_tok[0] = 0;
+      s_tok[1] = n0;
+      const int32_t c = (n0 + chunk_tokens - 1) / chunk_tokens;
+      s_chunk[0] = 0;
+      s_chunk[1] = p.cache ? (c > 1 ? c : 1) : ((p.skip && skip0) ? 0 : c);
+    }
+    __syncthreads();
+  } else {
+    block_prefix(s_tok, b, [&](int r) -> int64_t { return p.seq_lens[r]; });
+    block_prefix(s_chunk, b, [&](int r) -> int32_t { return score_chunks(p, r, chunk_tokens); });
+  }
   TS_TIMELINE_MARK_HERE();                     // mark 0: request tables ready (after a barrier)
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __shared__ double s_red[3][4];
   int dec_lo = -1, dec_hi = -1;                // requests of the last decided block (uniform)
   int hit_v = 0;                               // the cache decision of this wave's request
+  if (decide_first) {
+    hit_v = cache_hit_wg<kBf16>(p.q, p.cached_q, 0, p.H * kHeadDim, valid0, p.theta, s_red, &cpre);
+    if (threadIdx.x == 0) p.hit[0] = hit_v;
+    dec_lo = dec_hi = 0;
+    TS_TIMELINE_MARK_HERE();                   // mark 1: Selection Cache decided
+  }
   const int row = lane >> 4, col = lane & 15;
   const int H = p.H, Hkv = p.Hkv;
   const int total_units = s_chunk[b] * Hkv;
@@ -336,12 +363,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
         }
         dec_lo = r_lo;
         dec_hi = r_hi;
+        TS_TIMELINE_MARK_HERE();                 // mark 1: Selection Cache decided
       }
     }
     if (u >= total_units) break;                 // only in the workgroup's last block
     if (p.cache && hit_v) continue;
     const int c0 = cg - __builtin_amdgcn_readfirstlane(s_chunk[r]);
-    const int N = p.seq_lens[r];
+    const int N = (int)(s_tok[r + 1] - s_tok[r]);
     const int n_pages = (N + kPage - 1) / kPage;
     const int pg0 = c0 * p.chunk_pages;
     const int pg1 = min(n_pages, pg0 + p.chunk_pages);
@@ -417,7 +445,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
 #pragma unroll
       for (int x = 16; x <= 32; x <<= 1) merge_ms(mm, ss, __shfl_xor(mm, x), __shfl_xor(ss, x));
       if (row == 0 && (col & 3) == 0 && hd[c] < G) {
-        float* dst = p.partials + ((int64_t)(g * G + hd[c]) * s_chunk[b] + cg) * 2;
+        float* dst = p.partials + ((int64_t)(g * G + hd[c]) * p.pair_stride + cg) * 2;
         dst[0] = mm;
         dst[1] = ss;
       }
@@ -464,7 +492,7 @@ __global__ __launch_bounds__(256) void stats_kernel(ScoreParams p) {
   // [H][chunks] pairs: coalesced 8-byte loads, 8 per thread in flight before they are
   // merged in chunk order
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  const f32x2_t* src = reinterpret_cast<const f32x2_t*>(p.partials) + (int64_t)h * s_chunk[b];
+  const f32x2_t* src = reinterpret_cast<const f32x2_t*>(p.partials) + (int64_t)h * p.pair_stride;
   const int step = blockDim.x;
   int c = c0 + threadIdx.x;
   for (; c + 7 * step < c1; c += 8 * step) {

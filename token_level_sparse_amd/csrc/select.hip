@@ -54,6 +54,7 @@ constexpr int kThreads = 256;
 #endif
 // Vote workgroups: each takes several tiles and flushes its histogram once.
 constexpr int kVoteMaxGrid = TS_VOTE_MAX_GRID;
+constexpr int kMaxFoldGrid = 2048;   // fold-mode vote workgroups (they loop over the tiles)
 #ifndef TS_REFINE_MAX_GRID
 #define TS_REFINE_MAX_GRID 256
 #endif
@@ -80,7 +81,33 @@ struct Tables {
   int32_t tile[kMaxBatch + 1];
 };
 
-__device__ void build_tables(Tables& t, const VoteParams& p) {
+// Request 0's length and skip flag, read by every thread at the kernel's start with
+// uniform addresses: scalar loads, which do not queue behind the vector loads issued
+// after them. Both are unconditional (a null skip array reads seq_lens instead and
+// is ignored), so nothing waits for them before they are used.
+struct OneReq {
+  int n, skip;
+  bool has_skip;
+};
+__device__ __forceinline__ OneReq one_request(const VoteParams& p) {
+  OneReq o;
+  o.n = p.seq_lens[0];
+  o.has_skip = p.skip != nullptr;
+  o.skip = (o.has_skip ? p.skip : p.seq_lens)[0];
+  return o;
+}
+
+__device__ void build_tables(Tables& t, const VoteParams& p, const OneReq& o) {
+  if (p.b == 1) {
+    if (threadIdx.x == 0) {
+      t.tok[0] = 0;
+      t.tok[1] = o.n;
+      t.tile[0] = 0;
+      t.tile[1] = (o.has_skip && o.skip) ? 0 : (o.n + kVoteTile - 1) / kVoteTile;
+    }
+    __syncthreads();
+    return;
+  }
   block_prefix(t.tok, p.b, [&](int r) -> int64_t { return p.seq_lens[r]; });
   block_prefix(t.tile, p.b, [&](int r) -> int32_t {
     if (p.skip && p.skip[r]) return 0;
@@ -175,14 +202,22 @@ __device__ void find_digit_pk(const uint32_t* hist, const u64* mhist, int kk, u6
 // Digit holding the kk-th largest key among the counts in hist[0..kBins) (bins in
 // increasing key order): s_out = {bin, kk - count(keys in higher bins)}.
 // 1 <= kk <= total count is required; exactly one thread finds the crossing.
+// Thread t owns bins [kBins - kPer (t + 1), kBins - kPer t), highest first (thread 0
+// owns the top bins); load_counts reads them, find_digit_c finds the digit.
 template <int kBins>
-__device__ void find_digit(const uint32_t* hist, int kk, int* s_out, uint32_t* s_w) {
+__device__ __forceinline__ void load_counts(const uint32_t* hist, uint32_t (&c)[kBins / kThreads]) {
+  constexpr int kPer = kBins / kThreads;
+  const int hi = kBins - kPer * threadIdx.x;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) c[e] = hist[hi - 1 - e];
+}
+template <int kBins>
+__device__ void find_digit_c(const uint32_t (&c)[kBins / kThreads], int kk, int* s_out, uint32_t* s_w) {
   constexpr int kPer = kBins / kThreads;            // 8 or 4 bins per thread
   const int hi = kBins - kPer * threadIdx.x;        // thread 0 owns the top bins
-  uint32_t c[kPer];
   uint32_t sum = 0;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) { c[e] = hist[hi - 1 - e]; sum += c[e]; }
+  for (int e = 0; e < kPer; ++e) sum += c[e];
   const uint32_t above = block_excl_scan(sum, s_w);
   if (above < (uint32_t)kk && (uint32_t)kk <= above + sum) {
     uint32_t acc = above;
@@ -198,6 +233,12 @@ __device__ void find_digit(const uint32_t* hist, int kk, int* s_out, uint32_t* s
     }
   }
   __syncthreads();
+}
+template <int kBins>
+__device__ void find_digit(const uint32_t* hist, int kk, int* s_out, uint32_t* s_w) {
+  uint32_t c[kBins / kThreads];
+  load_counts<kBins>(hist, c);
+  find_digit_c<kBins>(c, kk, s_out, s_w);
 }
 
 // Keys of this thread's positions i0 + e * kThreads (clamped addresses; positions
@@ -231,18 +272,17 @@ __device__ __forceinline__ void load_group(const float* zg, int i, float (&x)[G]
 // KV heads whose logits a thread requests at once (about 128 values in registers).
 template <int G> struct VoteBatch { static constexpr int kB = G == 1 ? 8 : 32 / G; };
 
-// Logits of KV heads [g0, g0 + kB) below Hkv at this thread's positions.
-// `head_stride` = N * G floats per KV head.
-template <int G, int kB>
-__device__ __forceinline__ void load_batch(float (&x)[kB][kPerThread][G], const float* z, int64_t head_stride,
-                                           const int (&idx)[kPerThread], int g0, int Hkv) {
+// Logits of KV heads [g0, g0 + kB) at this thread's positions; heads past Hkv - 1
+// reload the last one (unused), so every load is unconditional and the waits of
+// whatever was requested before them stay exact. `head_stride` = N * G floats per KV head.
+template <int G, int kB, int kP>
+__device__ __forceinline__ void load_batch(float (&x)[kB][kP][G], const float* z, int64_t head_stride,
+                                           const int (&idx)[kP], int g0, int Hkv) {
 #pragma unroll
   for (int j = 0; j < kB; ++j) {
-    if (g0 + j < Hkv) {
-      const float* zg = z + (int64_t)(g0 + j) * head_stride;
+    const float* zg = z + (int64_t)min(g0 + j, Hkv - 1) * head_stride;
 #pragma unroll
-      for (int e = 0; e < kPerThread; ++e) load_group<G>(zg, idx[e], x[j][e]);
-    }
+    for (int e = 0; e < kP; ++e) load_group<G>(zg, idx[e], x[j][e]);
   }
 }
 
@@ -251,45 +291,74 @@ __device__ __forceinline__ void load_batch(float (&x)[kB][kPerThread][G], const 
 __device__ __forceinline__ void apply_cache_miss(const VoteParams& p, int r) {
   const uint4* src = static_cast<const uint4*>(p.q) + (int64_t)r * p.q_chunks;
   uint4* dst = static_cast<uint4*>(p.cached_q) + (int64_t)r * p.q_chunks;
-  for (int i = threadIdx.x; i < p.q_chunks; i += kThreads) dst[i] = src[i];
+  for (int i = threadIdx.x; i < p.q_chunks; i += blockDim.x) dst[i] = src[i];
   if (threadIdx.x == 0) p.valid[r] = 1;
 }
 
 // Fold mode: (M_h, log2 Z_h) of every head of request r from the score kernel's
-// per-unit pairs [h][c0, c1) (s_chunk: prefix of the units per request). 8 lanes per
-// head; a lane takes every 8th unit, kIn at a time in registers: their maximum,
-// then one independent exp per pair for the sum, merged into the lane's running
-// pair; a butterfly over the 8 lanes ends it. Every thread must call it.
-__device__ void fold_pairs(const VoteParams& p, const int32_t* s_chunk, int r, float* s_m, float* s_l) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  constexpr int kL = 8, kIn = 40;
-  const int c0 = s_chunk[r], c1 = s_chunk[r + 1], nch = s_chunk[p.b];
-  const int l = threadIdx.x % kL;
-  for (int h0 = 0; h0 < p.H; h0 += kThreads / kL) {
-    const int h = h0 + (int)threadIdx.x / kL;
-    float M = kNegInf, S = 0.f;
+// per-unit pairs [h][c0, c1) (rows of pair_stride units), by a workgroup of
+// kFoldThreads: 16 lanes per head, 32 heads per pass; a lane takes every 16th unit,
+// kFoldIn at a time in registers: their maximum, then one independent exp per pair
+// for the sum, merged into the lane's running pair; a butterfly over the 16 lanes
+// ends it. The first round of the first 32 heads is requested by fold_issue, ahead
+// of the logits.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kFoldThreads = 512;          // fold-mode vote workgroup
+constexpr int kFoldTile = kFoldThreads;    // its positions, one per thread
+constexpr int kFoldLanes = 16, kFoldIn = 16;
+constexpr int kFoldHeads = kFoldThreads / kFoldLanes;
+struct FoldPairs {
+  f32x2_t v[kFoldIn];
+};
+
+// First round of head threadIdx.x / 16: units c0 + l + 16 k, addresses clamped below
+// c_end (>= 1); fold_finish drops the units at or past the request's end and the
+// lanes past the last head, so the loads need no mask and nothing waits for them here.
+__device__ __forceinline__ void fold_issue(const VoteParams& p, int c0, int c_end, FoldPairs& f) {
+  const int l = threadIdx.x % kFoldLanes, h = threadIdx.x / kFoldLanes;
+  const f32x2_t* src = reinterpret_cast<const f32x2_t*>(p.partials) + (int64_t)min(h, p.H - 1) * p.pair_stride;
+#pragma unroll
+  for (int k = 0; k < kFoldIn; ++k) f.v[k] = src[min(c0 + l + k * kFoldLanes, c_end - 1)];
+}
+
+// Max and sum of exp of one round of kFoldIn pairs (units at or past c1 dropped).
+__device__ __forceinline__ void fold_round(const f32x2_t (&v)[kFoldIn], int c, int c1, float& M, float& S) {
+  float mr = kNegInf;
+#pragma unroll
+  for (int k = 0; k < kFoldIn; ++k) mr = fmaxf(mr, c + k * kFoldLanes < c1 ? v[k].x : kNegInf);
+  float sr = 0.f;
+  if (mr != kNegInf) {
+#pragma unroll
+    for (int k = 0; k < kFoldIn; ++k)
+      if (c + k * kFoldLanes < c1) sr += v[k].y * exp_via2(v[k].x - mr);
+  }
+  merge_ms(M, S, mr, sr);
+}
+
+// Every thread of the kFoldThreads workgroup must call it; `f` holds the first round
+// from fold_issue (requested with any upper bound: units at or past c1 are dropped
+// here). The first round is folded in straight-line code, so it waits only for its
+// own loads and not for the logits requested after them.
+__device__ void fold_finish(const VoteParams& p, int c0, int c1, const FoldPairs& f, float* s_m, float* s_l) {
+  const int l = threadIdx.x % kFoldLanes;
+  float M = kNegInf, S = 0.f;
+  fold_round(f.v, c0 + l, c1, M, S);
+  for (int h0 = 0; h0 < p.H; h0 += kFoldHeads) {
+    const int h = h0 + (int)threadIdx.x / kFoldLanes;
+    if (h0 > 0) { M = kNegInf; S = 0.f; }
     if (h < p.H) {
-      const f32x2_t* src = reinterpret_cast<const f32x2_t*>(p.partials) + (int64_t)h * nch;
-      for (int c = c0 + l; c < c1; c += kIn * kL) {
-        f32x2_t v[kIn];
+      const f32x2_t* src = reinterpret_cast<const f32x2_t*>(p.partials) + (int64_t)h * p.pair_stride;
+      for (int c = c0 + l + (h0 == 0 ? kFoldIn * kFoldLanes : 0); c < c1; c += kFoldIn * kFoldLanes) {
+        f32x2_t v[kFoldIn];
 #pragma unroll
-        for (int k = 0; k < kIn; ++k) {
-          const int ck = c + k * kL;
-          v[k] = ck < c1 ? src[ck] : f32x2_t{kNegInf, 0.f};
-        }
-        float mr = kNegInf;
-#pragma unroll
-        for (int k = 0; k < kIn; ++k) mr = fmaxf(mr, v[k].x);
-        float sr = 0.f;
-        if (mr != kNegInf) {
-#pragma unroll
-          for (int k = 0; k < kIn; ++k) sr += v[k].y * exp_via2(v[k].x - mr);
-        }
-        merge_ms(M, S, mr, sr);
+        for (int k = 0; k < kFoldIn; ++k) v[k] = src[min(c + k * kFoldLanes, c1 - 1)];
+        fold_round(v, c, c1, M, S);
       }
+    } else {
+      M = kNegInf; S = 0.f;
     }
 #pragma unroll
-    for (int x = 1; x < kL; x <<= 1) merge_ms(M, S, __shfl_xor(M, x), __shfl_xor(S, x));
+    for (int x = 1; x < kFoldLanes; x <<= 1) merge_ms(M, S, __shfl_xor(M, x), __shfl_xor(S, x));
     if (l == 0 && h < p.H) {
       s_m[h] = M;
       s_l[h] = __builtin_amdgcn_logf(S);
@@ -301,14 +370,14 @@ __device__ void fold_pairs(const VoteParams& p, const int32_t* s_chunk, int r, f
 // group's G terms at once (one rescale of the running sum per group, then one exp
 // per term); x_hi = (z_hi - M_h) log2e - log2 Z_h, where z - M is exact near the
 // head maximum.
-template <int G>
-__device__ __forceinline__ void vote_group(const float (&x)[kPerThread][G], const float* s_m, const float* s_l,
-                                           int g, float (&m)[kPerThread], float (&s)[kPerThread]) {
+template <int G, int kP>
+__device__ __forceinline__ void vote_group(const float (&x)[kP][G], const float* s_m, const float* s_l,
+                                           int g, float (&m)[kP], float (&s)[kP]) {
   float mh[G], lh[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) { mh[j] = s_m[g * G + j]; lh[j] = s_l[g * G + j]; }
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
+  for (int e = 0; e < kP; ++e) {
     float xv[G];
     float gm = m[e];
 #pragma unroll
@@ -324,28 +393,19 @@ __device__ __forceinline__ void vote_group(const float (&x)[kPerThread][G], cons
   }
 }
 
-// kFold (decode step, small selections): the head statistics come from folding the
-// score kernel's pairs here instead of a stats kernel, the first kB KV heads' logits
-// are requested before that fold so the two overlap, and Selection Cache misses are
-// applied here. Otherwise the statistics are loaded and the logits read group by group.
-template <int G, bool kTopP, bool kFold>
+// Votes of 1024-position tiles (4 per thread) from the head statistics of the
+// stats kernel; the logits are read one KV head group at a time.
+template <int G, bool kTopP>
 __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
   TS_TIMELINE_SCOPE(select, kTlVote);
   __shared__ Tables tb;
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ u64 s_mass[kTopP ? kHistBins : 1];
   __shared__ float s_m[256], s_l[256];
-  __shared__ int32_t s_chunk[kFold ? kMaxBatch + 1 : 1];
-  build_tables(tb, p);
-  if (kFold && p.cached_q) {
-    // a request without positions has no vote tile: its Selection Cache miss is
-    // applied here, by workgroup r mod grid
-    for (int r = blockIdx.x; r < p.b; r += gridDim.x) {
-      if (tb.tok[r + 1] != tb.tok[r] || (p.skip && p.skip[r])) continue;
-      apply_cache_miss(p, r);
-    }
-  }
   const int H = p.H, Hkv = H / G;
+  float x[1][kPerThread][G];
+  build_tables(tb, p, one_request(p));
+  TS_TIMELINE_MARK_HERE();                       // mark 0: request tables ready
   const int total = tb.tile[p.b];
   // The LDS histogram accumulates every tile this workgroup takes of one request
   // and is flushed to the global histogram (atomics) when the request changes
@@ -365,20 +425,16 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int r = find_segment(tb.tile, p.b, tile);
     const int t = tile - tb.tile[r];
-    const int N = p.seq_lens[r];
+    const int N = (int)(tb.tok[r + 1] - tb.tok[r]);
     const int i0 = t * kVoteTile + threadIdx.x;
     const float* z = p.logits + tb.tok[r] * H;
+    const int64_t hs = (int64_t)N * G;
     int idx[kPerThread];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) idx[e] = min(i0 + e * kThreads, N - 1);
     float m[kPerThread], s[kPerThread];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) { m[e] = kNegInf; s[e] = 0.f; }
-    // fold mode: the first kB KV heads' logits are requested before the head
-    // statistics are folded, so the two overlap
-    constexpr int kB = kFold ? VoteBatch<G>::kB : 1;
-    float x[kB][kPerThread][G];
-    if (kFold) load_batch(x, z, (int64_t)N * G, idx, 0, Hkv);
     if (r != cur_r) {
       // a new request: flush the last one's histogram, stage this one's head statistics
       if (cur_r >= 0) flush(cur_r);
@@ -386,38 +442,20 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
       for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_hist[i] = 0;
       if (kTopP)
         for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_mass[i] = 0;
-      if (kFold) {
-        if (cur_r < 0)   // score units per request, as the score kernel counts them
-          block_prefix(s_chunk, p.b, [&](int rr) -> int32_t {
-            return max(1, (p.seq_lens[rr] + p.chunk_tokens - 1) / p.chunk_tokens);
-          });
-        fold_pairs(p, s_chunk, r, s_m, s_l);
-        if (p.cached_q && t == 0) apply_cache_miss(p, r);
-      } else {
-        for (int h = threadIdx.x; h < H; h += kThreads) {
-          s_m[h] = p.head_stats[((int64_t)r * H + h) * 2 + 0];
-          s_l[h] = __builtin_amdgcn_logf(p.head_stats[((int64_t)r * H + h) * 2 + 1]);
-        }
+      for (int h = threadIdx.x; h < H; h += kThreads) {
+        s_m[h] = p.head_stats[((int64_t)r * H + h) * 2 + 0];
+        s_l[h] = __builtin_amdgcn_logf(p.head_stats[((int64_t)r * H + h) * 2 + 1]);
       }
       __syncthreads();
       cur_r = r;
+      TS_TIMELINE_MARK_HERE();                     // mark 1: head statistics staged
     }
-    if constexpr (kFold) {
-      for (int g0 = 0; g0 < Hkv; g0 += kB) {
-        if (g0 > 0) load_batch(x, z, (int64_t)N * G, idx, g0, Hkv);
-#pragma unroll
-        for (int j = 0; j < kB; ++j) {
-          if (g0 + j >= Hkv) break;
-          vote_group<G>(x[j], s_m, s_l, g0 + j, m, s);
-        }
-      }
-    } else {
 #pragma unroll 2
-      for (int g = 0; g < Hkv; ++g) {
-        load_batch(x, z + (int64_t)g * N * G, 0, idx, 0, 1);
-        vote_group<G>(x[0], s_m, s_l, g, m, s);
-      }
+    for (int g = 0; g < Hkv; ++g) {
+      load_batch(x, z + (int64_t)g * hs, 0, idx, 0, 1);
+      vote_group<G>(x[0], s_m, s_l, g, m, s);
     }
+    TS_TIMELINE_MARK_HERE();                       // mark 2: votes of the tile computed
     float* vout = p.vote + tb.tok[r];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -430,6 +468,117 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(VoteParams p) {
         if (kTopP) atomicAdd(&s_mass[bin], vote_mass(lv));
       }
     }
+    TS_TIMELINE_MARK_HERE();                       // mark 3: stored, LDS histogram updated
+  }
+  if (cur_r >= 0) flush(cur_r);
+}
+
+// Fold mode (decode step, selections of at most kFoldMaxPairs (head, unit) pairs): the
+// head statistics come from folding the score kernel's pairs here instead of a stats
+// kernel, and Selection Cache misses are applied here. Workgroups of 512 threads
+// take 512-position tiles, one position per thread, so at 128K tokens the launch fills
+// every CU with two waves per SIMD and each workgroup's fold (a fixed cost: all
+// pairs of the request) is spread over 512 threads. A new request's pairs are
+// requested first, then the logits of its first KV heads, so the fold waits only for
+// the pairs; with one request, the first tile's pairs go out before the request table
+// is built.
+template <int G, bool kTopP>
+__global__ __launch_bounds__(kFoldThreads) void vote_fold_kernel(VoteParams p) {
+  TS_TIMELINE_SCOPE(select, kTlVote);
+  __shared__ int64_t s_tok[kMaxBatch + 1];
+  __shared__ int32_t s_sub[kMaxBatch + 1];       // prefix of the requests' 512-position tiles
+  __shared__ int32_t s_chunk[kMaxBatch + 1];     // prefix of the requests' score units
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ u64 s_mass[kTopP ? kHistBins : 1];
+  __shared__ float s_m[256], s_l[256];
+  const int H = p.H, Hkv = H / G;
+  constexpr int kB = VoteBatch<G>::kB;           // KV heads per register set (about 32 logits)
+  float x[kB][1][G], x2[kB][1][G];
+  FoldPairs fp;
+  const OneReq one = one_request(p);
+  __builtin_amdgcn_sched_barrier(0);
+  const bool pre = p.b == 1;
+  if (pre) fold_issue(p, 0, p.pair_stride, fp);
+  auto units = [&](int n) { return max(1, (n + p.chunk_tokens - 1) / p.chunk_tokens); };
+  auto subs = [&](int n, bool skip) { return skip ? 0 : (n + kFoldTile - 1) / kFoldTile; };
+  if (p.b == 1) {
+    if (threadIdx.x == 0) {
+      s_tok[0] = 0; s_tok[1] = one.n;
+      s_sub[0] = 0; s_sub[1] = subs(one.n, one.has_skip && one.skip);
+      s_chunk[0] = 0; s_chunk[1] = units(one.n);
+    }
+    __syncthreads();
+  } else {
+    block_prefix(s_tok, p.b, [&](int r) -> int64_t { return p.seq_lens[r]; });
+    block_prefix(s_sub, p.b, [&](int r) -> int32_t { return subs(p.seq_lens[r], p.skip && p.skip[r]); });
+    block_prefix(s_chunk, p.b, [&](int r) -> int32_t { return units(p.seq_lens[r]); });
+  }
+  if (p.cached_q) {
+    // a request without positions has no vote tile: its Selection Cache miss is
+    // applied here, by workgroup r mod grid
+    for (int r = blockIdx.x; r < p.b; r += gridDim.x) {
+      if (s_tok[r + 1] != s_tok[r] || (p.skip && p.skip[r])) continue;
+      apply_cache_miss(p, r);
+    }
+  }
+  TS_TIMELINE_MARK_HERE();                       // mark 0: request tables ready
+  const int total = s_sub[p.b];
+  int cur_r = -1;
+  auto flush = [&](int r) {
+    __syncthreads();
+    uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += kFoldThreads)
+      if (s_hist[i]) atomicAdd(&gh[i], s_hist[i]);
+    if (kTopP) {
+      u64* gm = p.mass + (int64_t)r * 3 * kHistBins;
+      for (int i = threadIdx.x; i < kHistBins; i += kFoldThreads)
+        if (s_mass[i]) atomicAdd(&gm[i], s_mass[i]);
+    }
+  };
+  for (int st = blockIdx.x; st < total; st += gridDim.x) {
+    const int r = find_segment(s_sub, p.b, st);
+    const int t = st - s_sub[r];
+    const int N = (int)(s_tok[r + 1] - s_tok[r]);
+    const int i = t * kFoldTile + threadIdx.x;
+    const int idx[1] = {min(i, N - 1)};
+    const float* z = p.logits + s_tok[r] * H;
+    const int64_t hs = (int64_t)N * G;
+    float m[1] = {kNegInf}, s[1] = {0.f};
+    if (r != cur_r && !(pre && st == (int)blockIdx.x)) fold_issue(p, s_chunk[r], s_chunk[r + 1], fp);
+    __builtin_amdgcn_sched_barrier(0);           // the pairs before the logits (loads return in order)
+    load_batch(x, z, hs, idx, 0, Hkv);
+    if (r != cur_r) {
+      // a new request: flush the last one's histogram, fold this one's head statistics
+      if (cur_r >= 0) flush(cur_r);
+      __syncthreads();
+      for (int j = threadIdx.x; j < kHistBins; j += kFoldThreads) s_hist[j] = 0;
+      if (kTopP)
+        for (int j = threadIdx.x; j < kHistBins; j += kFoldThreads) s_mass[j] = 0;
+      fold_finish(p, s_chunk[r], s_chunk[r + 1], fp, s_m, s_l);
+      if (p.cached_q && t == 0) apply_cache_miss(p, r);
+      __syncthreads();
+      cur_r = r;
+      TS_TIMELINE_MARK_HERE();                     // mark 1: head statistics folded
+    }
+    for (int g0 = 0; g0 < Hkv; g0 += 2 * kB) {
+      if (g0 > 0) load_batch(x, z, hs, idx, g0, Hkv);
+      if (g0 + kB < Hkv) load_batch(x2, z, hs, idx, g0 + kB, Hkv);
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+        if (g0 + j < Hkv) vote_group<G>(x[j], s_m, s_l, g0 + j, m, s);
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+        if (g0 + kB + j < Hkv) vote_group<G>(x2[j], s_m, s_l, g0 + kB + j, m, s);
+    }
+    TS_TIMELINE_MARK_HERE();                       // mark 2: votes of the tile computed
+    if (i < N) {
+      const float lv = m[0] + __builtin_amdgcn_logf(s[0]);
+      p.vote[s_tok[r] + i] = lv;
+      const uint32_t bin = order_key(lv) >> (32 - kDigitBits0);
+      atomicAdd(&s_hist[bin], 1u);
+      if (kTopP) atomicAdd(&s_mass[bin], vote_mass(lv));
+    }
+    TS_TIMELINE_MARK_HERE();                       // mark 3: stored, LDS histogram updated
   }
   if (cur_r >= 0) flush(cur_r);
 }
@@ -452,13 +601,54 @@ struct SelectShared {
   int cnt[2][4];
 };
 
+// One request without top-p: a select kernel's loads for its first tile need no
+// request table, so they go out before it is built, together with the table's own
+// loads. Addresses are clamped to the max_tokens positions the vote buffer holds;
+// positions at or past N are masked once N is known, as on the other path.
+struct SelPre {
+  float lv[kPerThread];             // log2 votes of the first tile (refine: strided; write: consecutive)
+  uint32_t c[kHistBins / kThreads]; // refine: counts of the digit's histogram; write: digit 2's (first 4)
+  int4 st[2];                       // request 0's select state
+  int2 cnd0;                        // write: candidate threadIdx.x (the list is usually short)
+  int tcv[4];                       // write: keys above the prefix of tiles t + 256 u (used below the first tile)
+};
+constexpr int kPreTiles = 4 * kThreads;   // earlier tiles whose counts are preloaded
+static_assert(kPreTiles / kThreads == 4, "SelPre::tcv holds four counts per thread");
+
+template <int kPhase>
+__device__ __forceinline__ void sel_preload(const VoteParams& p, SelPre& q) {
+  const int tile = blockIdx.x;
+  const int4* st = reinterpret_cast<const int4*>(p.state);
+  if (kPhase == 2 || kPhase == 4) { q.st[0] = st[0]; q.st[1] = st[1]; }
+  if (kPhase == 1 || kPhase == 2) {
+    const int i0 = tile * kVoteTile + threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) q.lv[e] = p.vote[min(i0 + e * kThreads, p.max_tokens - 1)];
+    load_counts<kHistBins>(p.hist + (kPhase - 1) * kHistBins, q.c);
+  } else {
+    const int i0 = tile * kVoteTile + threadIdx.x * kPerThread;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) q.lv[e] = p.vote[min(i0 + e, p.max_tokens - 1)];
+    uint32_t c2[(1 << kDigitBits2) / kThreads];
+    load_counts<1 << kDigitBits2>(p.hist + 2 * kHistBins, c2);
+#pragma unroll
+    for (int e = 0; e < (1 << kDigitBits2) / kThreads; ++e) q.c[e] = c2[e];
+    q.cnd0 = p.cand[threadIdx.x];
+    // tiles up to the first one exist in tile_counts (the grid has at most max_tiles
+    // workgroups); entries at or past it are dropped at use
+#pragma unroll
+    for (int u = 0; u < kPreTiles / kThreads; ++u)
+      q.tcv[u] = p.tile_counts[2 * min((int)threadIdx.x + u * kThreads, tile)];
+  }
+}
+
 // kPass 1: find digit 0 from hist[0], histogram digit 1 of matching keys into hist[1].
 // kPass 2: read digit 0 from state, find digit 1 from hist[1], histogram digit 2 into hist[2].
 // A workgroup finds a request's digit once, accumulates its LDS histogram over all
 // its tiles of that request and flushes it once. With kTopP the masses go along and
 // each digit comes from the count-or-mass walk.
 template <int kPass, bool kTopP>
-__device__ void refine_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
+__device__ void refine_phase(const VoteParams& p, SelectShared<kTopP>& sh, const SelPre& pq, bool pre TS_TIMELINE_PARAM) {
   const int total = sh.tb.tile[p.b];
   constexpr int kShift = (kPass == 1) ? (32 - kDigitBits0) : (32 - kDigitBits0 - kDigitBits1);
   constexpr int kNextBits = (kPass == 1) ? kDigitBits1 : kDigitBits2;
@@ -485,18 +675,32 @@ __device__ void refine_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int r = find_segment(sh.tb.tile, p.b, tile);
     const int t = tile - sh.tb.tile[r];
-    const int N = p.seq_lens[r];
+    const int N = (int)(sh.tb.tok[r + 1] - sh.tb.tok[r]);
     if (!kTopP && p.top_k >= N) continue;             // whole request selected: no radix work
     const int i0 = t * kVoteTile + threadIdx.x;
+    const bool have = pre && tile == (int)blockIdx.x;   // the first tile was preloaded
     uint32_t key[kPerThread];
-    load_keys(p.vote + sh.tb.tok[r], i0, N, key);
+    if (have) {
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) key[e] = (i0 + e * kThreads < N) ? order_key(pq.lv[e]) : 0u;
+    } else {
+      load_keys(p.vote + sh.tb.tok[r], i0, N, key);
+    }
     if (r != cur_r) {
       if (cur_r >= 0) flush(cur_r);
       __syncthreads();
       int32_t* st = p.state + r * 8;
       const uint32_t* gh = p.hist + (int64_t)r * 3 * kHistBins;
       const u64* gm = p.mass + (int64_t)r * 3 * kHistBins;
-      if (kPass == 1) {
+      if (have) {
+        if (kPass == 1) {
+          find_digit_c<1 << kDigitBits0>(pq.c, p.top_k, sh.dig, sh.w);
+          prefix = (uint32_t)sh.dig[0];
+        } else {
+          find_digit_c<1 << kDigitBits1>(pq.c, pq.st[0].y, sh.dig, sh.w);
+          prefix = ((uint32_t)pq.st[0].x << kDigitBits1) | (uint32_t)sh.dig[0];
+        }
+      } else if (kPass == 1) {
         if (kTopP) {
           // target mass: ceil(p * total mass of the request)
           u64 part = 0;
@@ -531,6 +735,7 @@ __device__ void refine_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
         for (int i = threadIdx.x; i < (1 << kNextBits); i += kThreads) sh.mass[i] = 0;
       __syncthreads();
       cur_r = r;
+      TS_TIMELINE_MARK_HERE();                     // mark 1: digit found
     } else if (t == 0 && threadIdx.x == 0) {
       record(r);
     }
@@ -542,6 +747,7 @@ __device__ void refine_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
         if (kTopP) atomicAdd(&sh.mass[bin], vote_mass(key_value(key[e])));
       }
     }
+    TS_TIMELINE_MARK_HERE();                       // mark 2: LDS histogram of the tile
     if (kPass == 2) {
       // The threshold key shares the 22-bit prefix found here. For the write pass:
       // how many of this tile's keys lie above the prefix (all selected) and on it,
@@ -588,11 +794,16 @@ __device__ void refine_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
 // size of the selection (top_k, or the top-p budget capped at min(top_k, N)).
 template <bool kTopP>
 __device__ void threshold(const VoteParams& p, int r, int N, uint32_t& key_t, int& take_eq, int& m_sel,
-                          SelectShared<kTopP>& sh, bool record) {
+                          SelectShared<kTopP>& sh, bool record, const SelPre& pq, bool pre) {
   int32_t* st = p.state + r * 8;
-  const int d0 = st[0], d1 = st[2], k1 = st[3];
+  const int d0 = pre ? pq.st[0].x : st[0], d1 = pre ? pq.st[0].z : st[2], k1 = pre ? pq.st[0].w : st[3];
   const uint32_t* h2 = p.hist + ((int64_t)r * 3 + 2) * kHistBins;
-  if (kTopP) {
+  if (pre) {
+    uint32_t c2[(1 << kDigitBits2) / kThreads];
+#pragma unroll
+    for (int e = 0; e < (1 << kDigitBits2) / kThreads; ++e) c2[e] = pq.c[e];
+    find_digit_c<1 << kDigitBits2>(c2, k1, sh.dig, sh.w);
+  } else if (kTopP) {
     find_digit_pk<1 << kDigitBits2>(h2, p.mass + ((int64_t)r * 3 + 2) * kHistBins, k1,
                                     p.mstate[r * 4 + 2], sh.dig, &sh.mres, sh.w, sh.w64, sh.bin);
   } else {
@@ -617,7 +828,7 @@ __device__ void threshold(const VoteParams& p, int r, int N, uint32_t& key_t, in
 
 // Ascending positions through a prefix over the request's tiles.
 template <bool kTopP>
-__device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
+__device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh, const SelPre& pq, bool pre TS_TIMELINE_PARAM) {
   const int total = sh.tb.tile[p.b];
   // a request with no positions (a first prefill chunk) has no tile to do it
   if (blockIdx.x == 0)
@@ -626,7 +837,7 @@ __device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int r = find_segment(sh.tb.tile, p.b, tile);
     const int t = tile - sh.tb.tile[r];
-    const int N = p.seq_lens[r];
+    const int N = (int)(sh.tb.tok[r + 1] - sh.tb.tok[r]);
     const int k = p.top_k;
     int32_t* out = p.sel_idx + (int64_t)r * k;
     // this thread owns kPerThread consecutive positions
@@ -640,21 +851,26 @@ __device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
       }
     }
     const float* lv = p.vote + sh.tb.tok[r];
+    const bool have = pre && tile == (int)blockIdx.x;   // the first tile was preloaded
     float x[kPerThread];
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) x[e] = lv[min(i0 + e, N - 1)];
+    for (int e = 0; e < kPerThread; ++e) x[e] = have ? pq.lv[e] : lv[min(i0 + e, N - 1)];
     // Keys of the request's earlier tiles that sort before this tile's: every key
     // above the threshold's 22-bit prefix (counted per tile by the previous pass;
     // 8-byte loads, four in flight per thread before they are added), plus the keys
     // on the prefix that are greater than or equal to the exact threshold (from the
     // request's list of prefix keys, or, when the list overflowed, by reading the
     // earlier tiles that hold prefix keys again).
-    const int n_cand = p.state[r * 8 + 7];
+    const int n_cand = have ? pq.st[1].w : p.state[r * 8 + 7];
     const int tile_lo = t * kVoteTile;
     int gtb = 0, eqb = 0;
+    if (have) {
+#pragma unroll
+      for (int u = 0; u < kPreTiles / kThreads; ++u) gtb += ((int)threadIdx.x + u * kThreads < t) ? pq.tcv[u] : 0;
+    }
     typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
     const i32x2_t* tc = reinterpret_cast<const i32x2_t*>(p.tile_counts) + sh.tb.tile[r];
-    int tt = threadIdx.x;
+    int tt = threadIdx.x + (have ? kPreTiles : 0);
     for (; tt + 3 * kThreads < t; tt += 4 * kThreads) {
       i32x2_t v[4];
 #pragma unroll
@@ -668,13 +884,14 @@ __device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
 #pragma unroll
       for (int u = 0; u < kCandCap / kThreads; ++u) {
         const int j = threadIdx.x + u * kThreads;
-        cnd[u] = (j < n_cand) ? p.cand[(int64_t)r * kCandCap + j] : make_int2(0, 0x7fffffff);
+        cnd[u] = (j >= n_cand) ? make_int2(0, 0x7fffffff) : (have && u == 0) ? pq.cnd0 : p.cand[(int64_t)r * kCandCap + j];
       }
     }
     __syncthreads();
     uint32_t key_t;
     int take_eq, m_sel;
-    threshold<kTopP>(p, r, N, key_t, take_eq, m_sel, sh, false);
+    threshold<kTopP>(p, r, N, key_t, take_eq, m_sel, sh, false, pq, have);
+    TS_TIMELINE_MARK_HERE();                       // mark 1: threshold found
     if (kTopP && t == 0 && threadIdx.x == 0) p.sel_count[r] = m_sel;
     if (n_cand <= kCandCap) {
 #pragma unroll
@@ -712,6 +929,7 @@ __device__ void write_phase(const VoteParams& p, SelectShared<kTopP>& sh) {
     __syncthreads();
     gtb = sh.cnt[0][0] + sh.cnt[0][1] + sh.cnt[0][2] + sh.cnt[0][3];
     eqb = sh.cnt[1][0] + sh.cnt[1][1] + sh.cnt[1][2] + sh.cnt[1][3];
+    TS_TIMELINE_MARK_HERE();                       // mark 2: keys before the tile counted
     uint32_t keys[kPerThread];
     uint32_t packed = 0;                              // (equal << 16) | greater
 #pragma unroll
@@ -741,10 +959,16 @@ template <int kPhase, bool kTopP>
 __global__ __launch_bounds__(kThreads) void select_phase_kernel(VoteParams p) {
   TS_TIMELINE_SCOPE(select, kTlVote + kPhase);
   __shared__ SelectShared<kTopP> sh;
-  build_tables(sh.tb, p);
-  if (kPhase == 1) refine_phase<1, kTopP>(p, sh);
-  if (kPhase == 2) refine_phase<2, kTopP>(p, sh);
-  if (kPhase == 4) write_phase<kTopP>(p, sh);
+  SelPre q;
+  const OneReq one = one_request(p);
+  __builtin_amdgcn_sched_barrier(0);               // the length goes out before the preloads
+  const bool pre = !kTopP && p.b == 1 && p.max_tokens > 0;
+  if (pre) sel_preload<kPhase>(p, q);
+  build_tables(sh.tb, p, one);
+  TS_TIMELINE_MARK_HERE();                         // mark 0: request tables ready
+  if (kPhase == 1) refine_phase<1, kTopP>(p, sh, q, pre TS_TIMELINE_ARG);
+  if (kPhase == 2) refine_phase<2, kTopP>(p, sh, q, pre TS_TIMELINE_ARG);
+  if (kPhase == 4) write_phase<kTopP>(p, sh, q, pre TS_TIMELINE_ARG);
 }
 
 // Digit-0 histogram of any score array (the selection-function ablations run the
@@ -752,7 +976,7 @@ __global__ __launch_bounds__(kThreads) void select_phase_kernel(VoteParams p) {
 __global__ __launch_bounds__(kThreads) void hist0_kernel(VoteParams p) {
   __shared__ Tables tb;
   __shared__ uint32_t s_hist[kHistBins];
-  build_tables(tb, p);
+  build_tables(tb, p, one_request(p));
   const int total = tb.tile[p.b];
   int cur_r = -1;
   auto flush = [&](int r) {
@@ -764,7 +988,7 @@ __global__ __launch_bounds__(kThreads) void hist0_kernel(VoteParams p) {
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int r = find_segment(tb.tile, p.b, tile);
     const int t = tile - tb.tile[r];
-    const int N = p.seq_lens[r];
+    const int N = (int)(tb.tok[r + 1] - tb.tok[r]);
     if (r != cur_r) {
       if (cur_r >= 0) flush(cur_r);
       __syncthreads();
@@ -789,16 +1013,31 @@ __global__ void zero_u32(uint32_t* x, int64_t n) {
 
 template <bool kTopP, bool kFold>
 hipError_t launch_vote_kernel(const VoteParams& p, hipStream_t s) {
+  if (kFold) {
+    const dim3 fgrid(std::max(1, std::min(p.fold_grid, kMaxFoldGrid))), fblock(kFoldThreads);
+    switch (p.G) {
+      case 1: hipLaunchKernelGGL((vote_fold_kernel<1, kTopP>), fgrid, fblock, 0, s, p); break;
+      case 2: hipLaunchKernelGGL((vote_fold_kernel<2, kTopP>), fgrid, fblock, 0, s, p); break;
+      case 3: hipLaunchKernelGGL((vote_fold_kernel<3, kTopP>), fgrid, fblock, 0, s, p); break;
+      case 4: hipLaunchKernelGGL((vote_fold_kernel<4, kTopP>), fgrid, fblock, 0, s, p); break;
+      case 5: hipLaunchKernelGGL((vote_fold_kernel<5, kTopP>), fgrid, fblock, 0, s, p); break;
+      case 6: hipLaunchKernelGGL((vote_fold_kernel<6, kTopP>), fgrid, fblock, 0, s, p); break;
+      case 7: hipLaunchKernelGGL((vote_fold_kernel<7, kTopP>), fgrid, fblock, 0, s, p); break;
+      case 8: hipLaunchKernelGGL((vote_fold_kernel<8, kTopP>), fgrid, fblock, 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipSuccess;
+  }
   const dim3 vgrid(std::min(p.grid, kVoteMaxGrid)), block(kThreads);
   switch (p.G) {
-    case 1: hipLaunchKernelGGL((vote_kernel<1, kTopP, kFold>), vgrid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((vote_kernel<2, kTopP, kFold>), vgrid, block, 0, s, p); break;
-    case 3: hipLaunchKernelGGL((vote_kernel<3, kTopP, kFold>), vgrid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((vote_kernel<4, kTopP, kFold>), vgrid, block, 0, s, p); break;
-    case 5: hipLaunchKernelGGL((vote_kernel<5, kTopP, kFold>), vgrid, block, 0, s, p); break;
-    case 6: hipLaunchKernelGGL((vote_kernel<6, kTopP, kFold>), vgrid, block, 0, s, p); break;
-    case 7: hipLaunchKernelGGL((vote_kernel<7, kTopP, kFold>), vgrid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((vote_kernel<8, kTopP, kFold>), vgrid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((vote_kernel<1, kTopP>), vgrid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((vote_kernel<2, kTopP>), vgrid, block, 0, s, p); break;
+    case 3: hipLaunchKernelGGL((vote_kernel<3, kTopP>), vgrid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((vote_kernel<4, kTopP>), vgrid, block, 0, s, p); break;
+    case 5: hipLaunchKernelGGL((vote_kernel<5, kTopP>), vgrid, block, 0, s, p); break;
+    case 6: hipLaunchKernelGGL((vote_kernel<6, kTopP>), vgrid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL((vote_kernel<7, kTopP>), vgrid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((vote_kernel<8, kTopP>), vgrid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;

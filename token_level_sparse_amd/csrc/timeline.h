@@ -86,6 +86,9 @@ struct TimelineScope {
 #define TS_TIMELINE_SCOPE(NAME, KID) ts::TimelineScope ts_timeline_(ts::g_timeline_##NAME, (KID))
 #define TS_TIMELINE_MARK() ts_timeline_.mark()
 #define TS_TIMELINE_MARK_HERE() ts_timeline_.mark_here()
+// a device function that marks takes the kernel's scope as a trailing parameter
+#define TS_TIMELINE_PARAM , ts::TimelineScope& ts_timeline_
+#define TS_TIMELINE_ARG , ts_timeline_
 
 #else
 
@@ -93,5 +96,7 @@ struct TimelineScope {
 #define TS_TIMELINE_SCOPE(NAME, KID)
 #define TS_TIMELINE_MARK()
 #define TS_TIMELINE_MARK_HERE()
+#define TS_TIMELINE_PARAM
+#define TS_TIMELINE_ARG
 
 #endif
