@@ -56,7 +56,7 @@ constexpr int kThreads = 256;
 constexpr int kVoteMaxGrid = TS_VOTE_MAX_GRID;
 constexpr int kMaxFoldGrid = 2048;   // fold-mode vote workgroups (they loop over the tiles)
 #ifndef TS_REFINE_MAX_GRID
-#define TS_REFINE_MAX_GRID 256
+#define TS_REFINE_MAX_GRID 2048
 #endif
 constexpr int kRefineMaxGrid = TS_REFINE_MAX_GRID;
 constexpr int kPerThread = kVoteTile / kThreads;   // positions per thread
