@@ -747,7 +747,7 @@ def timeline_run(dev, reps=5):
     on the 28/4-head 128K geometry of the cache sequence (miss and hit) and at 1M;
     the 128K scoring launch without the cache (tokenselect_score; one dispatch round
     of workgroups) split into dispatch ramp, request tables, stream and tail, and the
-    cosine prologue the decode step adds; and the 128K prefill chunk attention.
+    wave time the decode step's score kernel adds; and the 128K prefill chunk attention.
     Medians over `reps` launches; prints a markdown report."""
     import ctypes
     import numpy as np
@@ -838,7 +838,7 @@ def timeline_run(dev, reps=5):
         print(f"| stream: tables ready to exit, wave median (no cache) | {us(rest):.2f} |")
         print(f"| tail: last exit after the median exit | {us(span - ex50):.2f} |")
         print(f"| kernel span, first entry to last exit (no cache) | {us(span):.2f} |")
-        print(f"| cosine prologue: wave median with the cache minus without (decode miss step) | "
+        print(f"| decode miss step minus tokenselect_score, wave median (theta = 2: no cosine is computed) | "
               f"{us(rest_c - rest):.2f} |")
         print(f"| kernel span in the decode miss step | {us(span_c):.2f} |")
 
