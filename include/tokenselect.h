@@ -133,7 +133,8 @@ size_t tokenselect_workspace_size(const ts_shape* shape, const ts_select* sel);
    cached token i < N_r of every request (deepnotes appendix Algorithm 2), and the
    per-head softmax statistics (M_h, Z_h) over all N_r tokens (head soft vote
    equation). `logits` holds max_total_tokens * H floats, `head_stats`
-   batch * H * 2 floats. */
+   batch * H * 2 floats, or is NULL: then only the logits are computed (one kernel;
+   the statistics of step 2 are not folded). */
 ts_status tokenselect_score(const ts_shape* shape, const ts_select* sel,
                             const void* q, const void* k_pool,
                             const int32_t* block_table, const int32_t* seq_lens,

@@ -249,3 +249,23 @@ def test_max_batch_of_1024_requests():
     rng = np.random.default_rng(0)
     for r in sorted(set(rng.integers(0, 1024, 12).tolist()) | {0, 1023}):
         gh.check_request(po, r, batch.requests[r], geo)
+
+
+def test_score_without_statistics_gives_the_same_logits():
+    """tokenselect_score with head_stats NULL runs only the scoring kernel: the logits
+    equal, bit for bit, those of the full launch (which also folds the statistics)."""
+    geo = wl.workload("llama3-8b-128k", seq_len=20000)
+    gh.log("[score] head_stats NULL vs full launch, N=20000")
+    batch = wl.make_batch(geo, device=DEV)
+    H, total = geo.num_q_heads, batch.total_tokens
+    shape = ts.make_shape(H, geo.num_kv_heads, 1, batch.block_table.shape[1], total, geo.torch_dtype)
+    sel = gh.select_params(geo)
+    ws = ts.alloc_workspace(shape, sel, DEV)
+    a = torch.full((H * total,), float("nan"), dtype=torch.float32, device=DEV)
+    b = torch.full((H * total,), float("nan"), dtype=torch.float32, device=DEV)
+    stats = torch.full((H * 2,), float("nan"), dtype=torch.float32, device=DEV)
+    ts.score(shape, sel, batch.q, batch.k_pool, batch.block_table, batch.seq_lens, a, stats, ws)
+    ts.score(shape, sel, batch.q, batch.k_pool, batch.block_table, batch.seq_lens, b, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.isfinite(stats).all()

@@ -560,7 +560,7 @@ ts_status tokenselect_score(const ts_shape* shape, const ts_select* sel, const v
   ts_status st = check_shape(shape, sel);
   if (st != TS_OK) return st;
   TS_REQUIRE16(q); TS_REQUIRE16(k_pool); TS_REQUIRE(block_table); TS_REQUIRE(seq_lens);
-  TS_REQUIRE(logits); TS_REQUIRE(head_stats);
+  TS_REQUIRE(logits);   // head_stats may be NULL: the statistics are then not computed
   if ((st = check_ws(*shape, *sel, ws, ws_bytes)) != TS_OK) return st;
   const ts::ScoreParams p = score_params(*shape, *sel, q, k_pool, block_table, seq_lens, nullptr,
                                          logits, head_stats, ws);

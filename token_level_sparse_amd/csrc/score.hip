@@ -545,7 +545,8 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t st) {
                  : p.q_f32 ? launch_score_t<true, true>(p, st)
                            : launch_score_t<true, false>(p, st);
   if (e != hipSuccess) return e;
-  if (!p.fold) hipLaunchKernelGGL(stats_kernel, dim3(p.b * p.H), dim3(256), 0, st, p);
+  // no statistics wanted (tokenselect_score with head_stats NULL), or folded by the vote kernel
+  if (!p.fold && p.head_stats) hipLaunchKernelGGL(stats_kernel, dim3(p.b * p.H), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
