@@ -24,14 +24,15 @@
 // every K and V fragment a wave reads from LDS feeds 32 rows, and each block staged
 // in LDS serves 256 rows. Per block of keys:
 //   * bf16: K and V rows go from global memory straight into LDS as [key][d]
-//     (global_load_lds_dwordx4, one 1 KiB window per wave and load), issued at the top
-//     of the previous block's iteration so they land while it computes; fp32: staged
+//     (global_load_lds_dwordx4, one 1 KiB window per wave and load) into three
+//     buffers each, two blocks ahead (K at the top of an iteration, V after its
+//     scores), so each block has more than one iteration to land; fp32: staged
 //     through registers, K and V as [key][d];
 //   * S^T = K Q^T on MFMA (A = 32 keys x 16 dims from LDS, B = the wave's queries
 //     held in registers), so a lane ends with 16 keys of one row: row = lane % 32;
 //   * online softmax in base 2 per row (row max across the 2 lane halves); in bf16
-//     the exp2 of block n runs between the MFMAs of block n + 1's scores, so the
-//     VALU and the matrix cores work at the same time inside one wave;
+//     the exp2 of block n runs between the MFMAs of block n + 1's scores and the
+//     maximum of block n + 1 between the MFMAs of block n's P V;
 //   * O^T += V^T P^T on MFMA: the lane's probabilities are already the B operand
 //     (row = lane % 32, 8 keys per step); in bf16 the A operand (V^T) is read from the
 //     [key][d] rows with LDS transpose reads (ds_read_b64_tr_b16) in the key order of
@@ -189,6 +190,18 @@ __device__ __forceinline__ int v_pos(int x, int c) { return c ^ ((x & 3) << 1); 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
 
+// One 1 KiB LDS window per wave (global_load_lds_dwordx4, LDS address in M0): lane i's
+// 16 bytes at gptr land at window bytes 16 i. Written as inline assembly: the compiler's
+// own wait-count model treats this load as a flat access that may also touch LDS, and
+// while one is in flight it makes every LDS read wait for all outstanding LDS operations
+// (lgkmcnt(0)) instead of only the ones it needs. The compiler does not see these loads,
+// so every caller waits for them itself (vmcnt) before the barrier that publishes the
+// window; the M0 write is followed by the one wait state the load needs.
+__device__ __forceinline__ void dma16(const void* gptr, const char* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(gptr), "{m0}"(m0) : "memory");
+}
+
 // Wave w stages rows 8 w .. 8 w + 7 of the block (K into kl and/or V into vl) starting
 // at list entry x0.
 __device__ __forceinline__ void stage_direct(char* kl, char* vl, const uint16_t* kp, const uint16_t* vp,
@@ -200,9 +213,28 @@ __device__ __forceinline__ void stage_direct(char* kl, char* vl, const uint16_t*
     const int64_t off = km.row(x0 + row);
     const int at = (8 * wave + 4 * j) * Tile<true>::kRow;
     if (do_k)
-      __builtin_amdgcn_global_load_lds((global_cvoid*)(kp + off + 8 * k_pos(row, pos)), (lds_void*)(kl + at), 16, 0, 0);
+      dma16(kp + off + 8 * k_pos(row, pos), kl + at);
     if (do_v)
-      __builtin_amdgcn_global_load_lds((global_cvoid*)(vp + off + 8 * v_pos(row, pos)), (lds_void*)(vl + at), 16, 0, 0);
+      dma16(vp + off + 8 * v_pos(row, pos), vl + at);
+  }
+}
+// The staging split in two: the key-list offsets of the wave's two 4-row windows (LDS
+// reads of the split's key table, issued one iteration ahead) and the loads themselves.
+struct StageOff { int64_t off[2]; };
+__device__ __forceinline__ StageOff stage_offsets(const KeyMap& km, int x0) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  StageOff so;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) so.off[j] = km.row(x0 + 8 * wave + 4 * j + (lane >> 4));
+  return so;
+}
+template <bool kIsK>
+__device__ __forceinline__ void stage_issue(char* buf, const uint16_t* pool, const StageOff& so) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * wave + 4 * j + (lane >> 4), pos = lane & 15;
+    dma16(pool + so.off[j] + 8 * (kIsK ? k_pos(row, pos) : v_pos(row, pos)), buf + (8 * wave + 4 * j) * Tile<true>::kRow);
   }
 }
 // Every staged write of this thread has landed in LDS (the barrier that follows makes
@@ -269,31 +301,39 @@ __device__ __forceinline__ void qk_block32(const char* lds, const QOp32& q, int 
 // lane s of the group addresses key (first key + s / 4), dims (group's first dim + 4 (s % 4)).
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+__device__ __forceinline__ bf16x8_t v_frag(const char* Vs, int i, int lg, int s, int half) {
+  const int t = i >> 3, hh = (i >> 2) & 1, dt = i & 3;
+  const int x = 32 * t + 16 * hh + 4 * lg + (s >> 2);
+  const int c = 4 * dt + 2 * half + ((s & 3) >> 1), b = 8 * (s & 1);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(Vs + x * Tile<true>::kRow + 16 * v_pos(x, c) + b));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(Vs + (x + 8) * Tile<true>::kRow + 16 * v_pos(x + 8, c) + b));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+template <typename Hook>
 __device__ __forceinline__ void pv_block32(const char* lds, const f32x16_t (&pv)[2], int l32, int lg,
-                                           f32x16_t (&o)[4]) {
+                                           f32x16_t (&o)[4], Hook hook) {
   const char* Vs = lds;
   const int s = threadIdx.x & 15, half = l32 >> 4;
+  bf16x8_t av = v_frag(Vs, 0, lg, s, half);
+  bf16x8_t pb;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+  for (int i = 0; i < 16; ++i) {
+    const int t = i >> 3, hh = (i >> 2) & 1, dt = i & 3;
+    if (dt == 0) {
       const int b8 = 8 * hh;
-      // probabilities in [0, 2^8] to bf16 (round to nearest even, two per instruction)
-      const bf16x8_t pb = {(__bf16)pv[t][b8], (__bf16)pv[t][b8 + 1], (__bf16)pv[t][b8 + 2],
-                           (__bf16)pv[t][b8 + 3], (__bf16)pv[t][b8 + 4], (__bf16)pv[t][b8 + 5],
-                           (__bf16)pv[t][b8 + 6], (__bf16)pv[t][b8 + 7]};
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int x = 32 * t + 16 * hh + 4 * lg + (s >> 2);               // keys x, then x + 8
-        const int c = 4 * dt + 2 * half + ((s & 3) >> 1), b = 8 * (s & 1);
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(Vs + x * Tile<true>::kRow + 16 * v_pos(x, c) + b));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(Vs + (x + 8) * Tile<true>::kRow + 16 * v_pos(x + 8, c) + b));
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[dt], 0, 0, 0);
-      }
+      pb = bf16x8_t{(__bf16)pv[t][b8], (__bf16)pv[t][b8 + 1], (__bf16)pv[t][b8 + 2],
+                    (__bf16)pv[t][b8 + 3], (__bf16)pv[t][b8 + 4], (__bf16)pv[t][b8 + 5],
+                    (__bf16)pv[t][b8 + 6], (__bf16)pv[t][b8 + 7]};
     }
+    bf16x8_t an = av;
+    if (i + 1 < 16) an = v_frag(Vs, i + 1, lg, s, half);
+    __builtin_amdgcn_sched_barrier(0);
+    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[dt], 0, 0, 0);
+    hook(i);
+    av = an;
+  }
 }
 
 __device__ __forceinline__ void load_qop(QOpF32& q, const float* qrow, bool ok, int a) {
@@ -426,10 +466,9 @@ __global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2, 2
 void chunk_attn_bf16_kernel(ChunkParams p) {
   TS_TIMELINE_SCOPE(prefill, kTlChunkAttn);
   constexpr int KB = Tile<true>::kKeys;
-  __shared__ __align__(16) char s_k0[Tile<true>::kKeys * Tile<true>::kRow];
-  __shared__ __align__(16) char s_k1[Tile<true>::kKeys * Tile<true>::kRow];
-  __shared__ __align__(16) char s_v0[Tile<true>::kKeys * Tile<true>::kRow];
-  __shared__ __align__(16) char s_v1[Tile<true>::kKeys * Tile<true>::kRow];
+  constexpr int kBuf = Tile<true>::kKeys * Tile<true>::kRow;
+  __shared__ __align__(16) char s_kb[3 * kBuf];
+  __shared__ __align__(16) char s_vb[3 * kBuf];
   __shared__ int64_t s_keys[kChunkSplitKeys];
   __shared__ int s_geom[5];
   UnitWork w;
@@ -456,31 +495,34 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
 
-  // Online softmax of one block, first half: the block maximum and the rescale of the
-  // running state. Returns whether every key of the block is visible to every row of
-  // the wave (wave-uniform); then the scores stay raw (the maximum is taken on them:
-  // scaling by sl2 > 0 commutes with the rounded max), otherwise they are scaled, with
-  // -inf where masked.
-  auto soft_max = [&](f32x16_t (&s)[2], int x0) -> bool {
-    const bool full = x0 + KB <= w.x_end && x0 + KB - 1 <= wave_lim;
-    float mloc = kNegInf;
-    if (full) {
+  // Online softmax of one block, first half: the block maximum (max_part, two scores per
+  // call, folded in between the products of the previous block; max_done joins the lane's
+  // two key halves) and the rescale of the running state (rescale). In a block every key
+  // of which is visible to every row of the wave (wave-uniform, block_full) the scores
+  // stay raw (the maximum is taken on them: scaling by sl2 > 0 commutes with the rounded
+  // max); otherwise they are scaled, with -inf where masked.
+  auto block_full = [&](int x0) { return x0 + KB <= w.x_end && x0 + KB - 1 <= wave_lim; };
+  auto max_part = [&](auto full_c, f32x16_t (&s)[2], int x0, int i, float& mloc) {
+    constexpr bool kFull = decltype(full_c)::value;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[t][i]);
-      mloc *= sl2;
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int x = x0 + 32 * t + 8 * (i >> 2) + 4 * lg + (i & 3);
-          s[t][i] = (x < w.x_end && x <= lim) ? s[t][i] * sl2 : kNegInf;
-          mloc = fmaxf(mloc, s[t][i]);
-        }
+    for (int e = 2 * i; e < 2 * i + 2; ++e) {
+      const int t = e >> 4, ii = e & 15;
+      if (kFull) {
+        mloc = fmaxf(mloc, s[t][ii]);
+      } else {
+        // key x0 + c + 4 lg is visible iff c <= bnd (c is a constant of the element)
+        const int bnd = min(w.x_end - 1, lim) - x0 - 4 * lg;
+        const int c = 32 * t + 8 * (ii >> 2) + (ii & 3);
+        s[t][ii] = (c <= bnd) ? s[t][ii] * sl2 : kNegInf;
+        mloc = fmaxf(mloc, s[t][ii]);
+      }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  };
+  auto max_done = [&](bool full, float mloc) {
+    if (full) mloc *= sl2;
+    return fmaxf(mloc, __shfl_xor(mloc, 32));
+  };
+  auto rescale = [&](float mloc) {
     if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
@@ -489,7 +531,6 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
-    return full;
   };
 
   // Second half, fused with the scores of the next block: the probabilities of block n
@@ -502,11 +543,15 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
     const float nm = -m_run;
     f32x16_t a0 = {}, a1 = {};
     float psum = 0.f;
+    auto kread = [&](int row, int ks) {
+      return *reinterpret_cast<const bf16x8_t*>(kb + row * Tile<true>::kRow + 16 * k_pos(row, 2 * ks + lg));
+    };
+    bf16x8_t k0 = kread(l32, 0), k1 = kread(32 + l32, 0);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(kb + l32 * Tile<true>::kRow + 16 * k_pos(l32, 2 * ks + lg));
-      const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(kb + (32 + l32) * Tile<true>::kRow +
-                                                             16 * k_pos(32 + l32, 2 * ks + lg));
+      bf16x8_t n0 = k0, n1 = k1;
+      if (ks + 1 < 8) { n0 = kread(l32, ks + 1); n1 = kread(32 + l32, ks + 1); }
+      __builtin_amdgcn_sched_barrier(0);
       a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q.v[ks], a0, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -523,44 +568,74 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
         cur[ks >> 2][4 * (ks & 3) + e] = pr;
         psum += pr;
       }
+      k0 = n0; k1 = n1;
+      __builtin_amdgcn_sched_barrier(0);
     }
     nxt[0] = a0;
     nxt[1] = a1;
     l_run += psum;
   };
 
-  // Software pipeline, one barrier per block: the scores of block n + 1 go to the
-  // matrix cores before block n's softmax, so the two overlap within the wave. Block m
-  // keeps K in buffer m % 2 and V in buffer m % 2, with K staged one block ahead:
-  // entering iteration n, S_n is in registers and K_{n+1}, V_n are in LDS. Iteration n
-  // first starts the staging of K_{n+2} over K_n (read in iteration n - 1) and of V_{n+1}
-  // over V_{n-1} (read in iteration n - 1); they land while the block is computed.
+  // Software pipeline, one barrier per block, three LDS buffers each for K and V (block m
+  // in buffer m % 3). Entering iteration n, S_n and its maximum are in registers and
+  // K_{n+1}, V_n are in LDS. Iteration n starts the staging of K_{n+3} over K_n (read in
+  // iteration n - 1), computes P_n with S_{n+1} = K_{n+1} Q^T, starts the staging of
+  // V_{n+2} over V_{n-1} (read in iteration n - 1), and accumulates P_n V_n with the
+  // maximum of S_{n+1} folded in between the products. Before its barrier it waits only
+  // for the staging started one iteration earlier (K_{n+2}, V_{n+1}), so each staged block
+  // has more than one iteration to land.
   const int nb = (w.x_end - w.x_begin + KB - 1) / KB;
-  stage_direct(s_k0, s_v0, kp, vp, w.km, w.x_begin, true, true);
-  if (nb > 1) stage_direct(s_k1, s_v1, kp, vp, w.km, w.x_begin + KB, true, false);
+  auto kbuf = [&](int m) { return s_kb + (m % 3) * kBuf; };
+  auto vbuf = [&](int m) { return s_vb + (m % 3) * kBuf; };
+  for (int m = 0; m < 3 && m < nb; ++m) stage_direct(kbuf(m), vbuf(m), kp, vp, w.km, w.x_begin + m * KB, true, m < 2);
   stage_wait();
   __syncthreads();
   f32x16_t sa[2], sb[2];
-  qk_block32(s_k0, q, l32, lg, sa);
+  qk_block32(s_kb, q, l32, lg, sa);
+  bool full_n = block_full(w.x_begin);
+  float mloc_n = kNegInf;
+  if (full_n) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) max_part(std::true_type{}, sa, w.x_begin, i, mloc_n);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) max_part(std::false_type{}, sa, w.x_begin, i, mloc_n);
+  }
+  mloc_n = max_done(full_n, mloc_n);
   __syncthreads();
   TS_TIMELINE_MARK();                            // mark 1: first blocks staged, S_0 computed
-  // Even blocks use the buffers named 0, odd blocks those named 1, fixed per unrolled
-  // step: with the staging writes and the reads of an iteration in distinct LDS
-  // objects, the compiler does not wait for the staging before the reads.
-  auto step = [&](int n, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], char* kn, char* vn, char* kn1, char* vn1) {
+  StageOff off_k = stage_offsets(w.km, w.x_begin + 3 * KB), off_v = stage_offsets(w.km, w.x_begin + 2 * KB);
+  auto step = [&](int n, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
     const int x0 = w.x_begin + n * KB;
-    if (n + 2 < nb) stage_direct(kn, vn1, kp, vp, w.km, x0 + 2 * KB, true, false);   // K_{n+2}
-    if (n + 1 < nb) stage_direct(kn, vn1, kp, vp, w.km, x0 + KB, false, true);       // V_{n+1}
+    const bool sk = n + 3 < nb, sv = n + 2 < nb;
+    rescale(mloc_n);
+    if (sk) {
+      stage_issue<true>(kbuf(n + 3), kp, off_k);                                          // K_{n+3}
+      off_k = stage_offsets(w.km, x0 + 4 * KB);
+    }
     // S_{n+1} is computed even past the last block (from stale, in-bounds LDS) and unused
-    if (soft_max(cur, x0)) exp_qk(std::true_type{}, cur, nxt, kn1);
-    else exp_qk(std::false_type{}, cur, nxt, kn1);
-    pv_block32(vn, cur, l32, lg, o);
-    stage_wait();
+    if (full_n) exp_qk(std::true_type{}, cur, nxt, kbuf(n + 1));
+    else exp_qk(std::false_type{}, cur, nxt, kbuf(n + 1));
+    if (sv) {
+      stage_issue<false>(vbuf(n + 2), vp, off_v);                                         // V_{n+2}
+      off_v = stage_offsets(w.km, x0 + 3 * KB);
+    }
+    const int x1 = x0 + KB;
+    const bool full1 = block_full(x1);
+    float m1 = kNegInf;
+    if (full1) pv_block32(vbuf(n), cur, l32, lg, o, [&](int i) { max_part(std::true_type{}, nxt, x1, i, m1); });
+    else pv_block32(vbuf(n), cur, l32, lg, o, [&](int i) { max_part(std::false_type{}, nxt, x1, i, m1); });
+    mloc_n = max_done(full1, m1);
+    full_n = full1;
+    // this iteration's staging (2 windows per staged block) may still be in flight
+    if (sk && sv) __builtin_amdgcn_s_waitcnt(0x0F74);        // vmcnt(4)
+    else if (sk || sv) __builtin_amdgcn_s_waitcnt(0x0F72);   // vmcnt(2)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
     __syncthreads();
   };
   for (int n = 0; n < nb; n += 2) {
-    step(n, sa, sb, s_k0, s_v0, s_k1, s_v1);
-    if (n + 1 < nb) step(n + 1, sb, sa, s_k1, s_v1, s_k0, s_v0);
+    step(n, sa, sb);
+    if (n + 1 < nb) step(n + 1, sb, sa);
   }
 
   const float lt = l_run + __shfl_xor(l_run, 32);
