@@ -197,6 +197,50 @@ def stream_ceiling(pools, steps, dev):
     return res
 
 
+def phase_probe(dev):
+    """Time the chunk-attention phase probe (ts_chunk_phase_probe in
+    libts_stream_probe.so): the instruction mix of one phase of the bf16 chunk
+    attention's block loop repeated on LDS-resident data, 256 workgroups of 8 waves (two
+    per SIMD), no staging and no barriers. Prints a markdown table: wave time per loop
+    iteration and SIMD cycles per phase (at 2.4 GHz; each SIMD runs two waves, each
+    doing two phases per iteration)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from token_level_sparse_amd import build as tb
+    lib = ctypes.CDLL(tb.PROBE_LIB)
+    f = lib.ts_chunk_phase_probe
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    grid, iters = 256, 64
+    g = torch.Generator().manual_seed(7)
+    src = (torch.rand(2560 * 8, generator=g) * 0.05).to(torch.bfloat16).to(dev)
+    out = torch.empty(grid * 512, dtype=torch.float32, device=dev)
+    times = torch.zeros(grid * 16, dtype=torch.int64, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    names = {0: "EXP: 16 MFMA (next scores) + 32 exp2 of this block, K reads",
+             1: "PV: 16 MFMA + 32 transposed V reads + 16 cvt",
+             2: "EXP then PV (waves 0-3) / PV then EXP (waves 4-7)",
+             3: "EXP without exp2 (fma argument only)",
+             4: "EXP without MFMA (one add per product)"}
+    print("| mode | phase mix | wave time per iteration p50 / p90 (ns) | SIMD cycles per phase at 2.4 GHz |")
+    print("|---|---|---|---|")
+    for mode in range(5):
+        for rep in range(2):
+            rc = f(mode, iters, grid, ctypes.c_void_p(src.data_ptr()), src.numel() * 2, ctypes.c_void_p(out.data_ptr()),
+                   ctypes.c_void_p(times.data_ptr()), st)
+            if rc != 0:
+                raise RuntimeError(f"ts_chunk_phase_probe failed ({rc})")
+            torch.cuda.synchronize()
+        t = times.cpu().numpy().reshape(-1, 2)
+        per_it = (t[:, 1] - t[:, 0]) * 10.0 / iters
+        p50, p90 = np.percentile(per_it, [50, 90])
+        # per iteration a SIMD runs 2 waves x 2 phases
+        print(f"| {mode} | {names[mode]} | {p50:.0f} / {p90:.0f} | {p50 * 2.4 / 4:.0f} |")
+    print("(a v_mfma_f32_32x32x16_bf16 occupies the matrix core 32 cycles, so 16 of them take 512 cycles)")
+
+
 def time_workload(geo, n_layers, steps, warmup, dev, keep_host=False, ceiling=False, then=None):
     """Decode steps over n_layers rotating layers, then the score launches alone
     (and the streaming probe with ceiling=True); `then(layers)`, if given, runs on
@@ -916,6 +960,12 @@ def timeline_run(dev, reps=5):
         vals.append((ent.max(), np.median(v[:, 2] - v[:, 0]), np.median(v[:, 3] - v[:, 2]),
                      np.median(v[:, 1] - v[:, 3]), np.median(v[:, 1] - v[:, 0]), (v[:, 1] - v[:, 0].min()).max()))
     ramp, setup, pro, loop, dur, span = np.median(np.array(vals, dtype=np.float64), axis=0)
+    blk = []
+    for v in pruns:
+        v = v[(v[:, 8] & 0xff) >= 6]
+        blk.append((np.median(v[:, 5] - v[:, 4]), np.median(v[:, 6] - v[:, 5]), np.median(v[:, 7] - v[:, 6]),
+                    np.median(v[:, 7] - v[:, 4])))
+    b_qk, b_pv, b_bar, b_all = np.median(np.array(blk, dtype=np.float64), axis=0)
     print("\n### prefill-llama3-128k: chunk attention (chunk of 512, k = 3072, L = 512)\n")
     print("| part | µs |\n|---|---|")
     print(f"| dispatch ramp: last wave entry after the first | {us(ramp):.2f} |")
@@ -924,6 +974,13 @@ def timeline_run(dev, reps=5):
     print(f"| block loop and partial stores (wave median) | {us(loop):.2f} |")
     print(f"| wave duration (median) | {us(dur):.2f} |")
     print(f"| kernel span, first entry to last exit | {us(span):.2f} |")
+    print("\nOne 64-key iteration of the block loop (the ninth; wave medians; marks taken where the wave "
+          "reaches the point):\n")
+    print("| part | µs |\n|---|---|")
+    print(f"| staging of K issued, rescale, scores of the next block with this block's exp2 | {us(b_qk):.3f} |")
+    print(f"| staging of V issued, P V with the next block's maximum | {us(b_pv):.3f} |")
+    print(f"| wait for the staging started one iteration earlier, barrier | {us(b_bar):.3f} |")
+    print(f"| whole iteration | {us(b_all):.3f} |")
     del cbs, KC, VC, ws
     torch.cuda.empty_cache()
 
@@ -1074,6 +1131,8 @@ def main():
     ap.add_argument("--kernel-counters", action="store_true",
                     help="short program for rocprofv3 --pmc passes over the decode-step kernels at "
                          "128K and the prefill chunk attention")
+    ap.add_argument("--phase-probe", action="store_true",
+                    help="time the chunk-attention phase probe (libts_stream_probe.so); prints a markdown table")
     ap.add_argument("--timeline", action="store_true",
                     help="per-wave timeline of the decode-step kernels, the scoring launch and the chunk "
                          "attention (libtokenselect_timeline.so); prints a markdown report")
@@ -1096,6 +1155,9 @@ def main():
         return
     if args.kernel_counters:
         kernel_counter_run(dev)
+        return
+    if args.phase_probe:
+        phase_probe(dev)
         return
     if args.timeline:
         timeline_run(dev)

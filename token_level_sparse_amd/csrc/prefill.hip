@@ -605,9 +605,14 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
   __syncthreads();
   TS_TIMELINE_MARK();                            // mark 1: first blocks staged, S_0 computed
   StageOff off_k = stage_offsets(w.km, w.x_begin + 3 * KB), off_v = stage_offsets(w.km, w.x_begin + 2 * KB);
+  // timeline builds: marks 2-5 split iteration kTlBlock into its parts (scores of the
+  // next block with this block's exp2; P V with the next maximum; the wait for the
+  // staging and the barrier, up to the start of the next iteration)
+  constexpr int kTlBlock = 8;
   auto step = [&](int n, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
     const int x0 = w.x_begin + n * KB;
     const bool sk = n + 3 < nb, sv = n + 2 < nb;
+    if (n == kTlBlock || n == kTlBlock + 1) { TS_TIMELINE_MARK_HERE(); }
     rescale(mloc_n);
     if (sk) {
       stage_issue<true>(kbuf(n + 3), kp, off_k);                                          // K_{n+3}
@@ -616,6 +621,7 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
     // S_{n+1} is computed even past the last block (from stale, in-bounds LDS) and unused
     if (full_n) exp_qk(std::true_type{}, cur, nxt, kbuf(n + 1));
     else exp_qk(std::false_type{}, cur, nxt, kbuf(n + 1));
+    if (n == kTlBlock) { TS_TIMELINE_MARK_HERE(); }
     if (sv) {
       stage_issue<false>(vbuf(n + 2), vp, off_v);                                         // V_{n+2}
       off_v = stage_offsets(w.km, x0 + 3 * KB);
@@ -627,6 +633,7 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
     else pv_block32(vbuf(n), cur, l32, lg, o, [&](int i) { max_part(std::false_type{}, nxt, x1, i, m1); });
     mloc_n = max_done(full1, m1);
     full_n = full1;
+    if (n == kTlBlock) { TS_TIMELINE_MARK_HERE(); }
     // this iteration's staging (2 windows per staged block) may still be in flight
     if (sk && sv) __builtin_amdgcn_s_waitcnt(0x0F74);        // vmcnt(4)
     else if (sk || sv) __builtin_amdgcn_s_waitcnt(0x0F72);   // vmcnt(2)

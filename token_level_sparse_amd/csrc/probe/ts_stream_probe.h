@@ -1,5 +1,5 @@
-/* Streaming-bandwidth probe (libts_stream_probe.so): measurement infrastructure
- * for bench.py, not part of the TokenSelect method.
+/* Streaming-bandwidth and chunk-attention phase probes (libts_stream_probe.so):
+ * measurement infrastructure for bench.py, not part of the TokenSelect method.
  *
  * ts_stream_probe reads `bytes` bytes from device buffer `src` (16-byte aligned,
  * bytes a multiple of 16) with `grid` workgroups of 256 threads, each reading one
@@ -26,6 +26,19 @@ extern "C" {
 
 int ts_stream_probe(const void* src, size_t bytes, void* dst, int write, int grid, uint32_t* sink,
                     hipStream_t stream);
+
+/* Chunk-attention phase probe (phase_probe.hip): `grid` workgroups of 512 threads
+ * repeat `iters` times the instruction mix of one phase of the bf16 chunk attention's
+ * block loop (mode 0: the scores of the next block with this block's exp2; 1: the
+ * P V products; 2: the two alternating per SIMD; 3: mode 0 without the exp2; 4: mode 0
+ * without the matrix products) on LDS-resident data taken from `src` (device, 16-byte
+ * aligned, src_bytes >= 40960). Each wave writes its start and end wall clock
+ * (s_memrealtime, 100 MHz) to times[2 * (8 * workgroup + wave) + {0, 1}] (device,
+ * 16 * grid u64) and one float per thread to out (device, 512 * grid floats; values
+ * meaningless). Asynchronous on `stream`; returns 0, -1 on an invalid argument (nothing
+ * launched), or the hipError_t of the launch. The caller owns every buffer. */
+int ts_chunk_phase_probe(int mode, int iters, int grid, const void* src, size_t src_bytes, float* out,
+                         unsigned long long* times, hipStream_t stream);
 
 #ifdef __cplusplus
 }
