@@ -51,8 +51,8 @@ def test_stream_probe_library_exports_and_validates():
     if not os.path.exists(tb.PROBE_LIB):
         pytest.skip("probe library not built")
     hdr = open(os.path.join(ROOT, "token_level_sparse_amd", "csrc", "probe", "ts_stream_probe.h")).read()
-    names = set(re.findall(r"\b(ts_stream_probe\w*)\s*\(", hdr))
-    assert names == {"ts_stream_probe"}
+    names = set(re.findall(r"\b(ts_\w*probe)\s*\(", hdr))
+    assert names == {"ts_stream_probe", "ts_chunk_phase_probe"}
     plib = ctypes.CDLL(tb.PROBE_LIB)
     f = plib.ts_stream_probe
     f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
@@ -64,6 +64,17 @@ def test_stream_probe_library_exports_and_validates():
     assert f(ctypes.c_void_p(4104), 4096, FAKE, 0, 8, FAKE, None) == -1   # unaligned source
     assert f(FAKE, 4096, None, 1, 8, FAKE, None) == -1          # writes without a destination
     assert f(FAKE, 4096, FAKE, 0, 0, FAKE, None) == -1          # empty grid
+    g = plib.ts_chunk_phase_probe
+    g.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    g.restype = ctypes.c_int
+    assert g(5, 1, 1, FAKE, 40960, FAKE, FAKE, None) == -1       # no such mode
+    assert g(0, 0, 1, FAKE, 40960, FAKE, FAKE, None) == -1       # no iterations
+    assert g(0, 1, 0, FAKE, 40960, FAKE, FAKE, None) == -1       # empty grid
+    assert g(0, 1, 1, FAKE, 40944, FAKE, FAKE, None) == -1       # source too short
+    assert g(0, 1, 1, ctypes.c_void_p(4104), 40960, FAKE, FAKE, None) == -1   # unaligned source
+    assert g(0, 1, 1, FAKE, 40960, None, FAKE, None) == -1       # no output
+    assert g(0, 1, 1, FAKE, 40960, FAKE, None, None) == -1       # no times
 
 
 def test_attention_grid_beyond_int32_rejected(lib):
