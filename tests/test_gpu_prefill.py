@@ -75,6 +75,21 @@ def test_prefill_group7_bf16_small_budget():
     _run_all(cb, geo)
 
 
+@pytest.mark.parametrize("k", [8, 40, 100, 160, 260, 420, 700])
+def test_prefill_bf16_key_blocks_per_split(k):
+    # bf16 chunk attention stages 64-key blocks into three K and three V buffers, two
+    # blocks ahead; key lists of 72 ... 764 entries give one to three splits of 2, 3 or
+    # 4 blocks, most with a ragged last block, so the staging's prologue (fewer blocks
+    # than buffers) and its tail (no K, then no V left to stage) are taken; the G = 7
+    # test above has a single block, the 128K and 1024-query tests 8 to 16. All rows
+    # are checked against the oracle.
+    geo = wl.workload("prefill-tiny-f32", dtype="bf16", num_q_heads=16, num_kv_heads=4,
+                      seq_len=3040, chunk=40, top_k=k, n_local=24, seed=5900 + k)
+    gh.log(f"[prefill bf16 key blocks] P=3000 c=40 k={k} L=24 ({k + 64} list entries)")
+    cb = wl.make_chunk_batch(geo, DEV)
+    _run_all(cb, geo)
+
+
 def test_prefill_attention_on_oracle_topk():
     geo = wl.workload("prefill-tiny-f32", seq_len=5000, chunk=48, seed=5400)
     gh.log("[prefill attention on oracle TopK] f32")
