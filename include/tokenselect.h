@@ -227,7 +227,8 @@ ts_status tokenselect_decode_step_noalloc(const ts_shape* shape, const ts_select
    pointers, streams, ownership and errors apply. */
 
 /* Workspace bytes of the prefill entry points for chunks of up to max_chunk
-   tokens; 0 if the arguments are invalid. */
+   tokens (1 <= max_chunk <= shape->max_total_tokens: both are capacities, and a
+   chunk's tokens are among the batch's); 0 if the arguments are invalid. */
 size_t tokenselect_prefill_workspace_size(const ts_shape* shape, const ts_select* sel,
                                           int32_t max_chunk);
 
