@@ -196,7 +196,8 @@ def run_prefill(cb: wl.ChunkBatch, geo: wl.Geometry, top_k=None, n_local=None, s
     mc = cb.q_chunk.shape[1]
     lens = cb.seq_lens.cpu().tolist()
     past = [n - c for n, c in zip(lens, cb.chunk_lens.cpu().tolist())]
-    max_total = max(sum(lens), b)
+    # a capacity: at least the chunk capacity, which the ABI requires (max_chunk <= max_total_tokens)
+    max_total = max(sum(lens), b, mc)
     shape = ts.make_shape(H, geo.num_kv_heads, b, pb.block_table.shape[1], max_total, geo.torch_dtype)
     sel = select_params(geo, top_k, n_local, score_scale)
     k = sel.top_k
