@@ -218,23 +218,29 @@ __device__ __forceinline__ void stage_direct(char* kl, char* vl, const uint16_t*
       dma16(vp + off + 8 * v_pos(row, pos), vl + at);
   }
 }
-// The staging split in two: the key-list offsets of the wave's two 4-row windows (LDS
-// reads of the split's key table, issued one iteration ahead) and the loads themselves.
-struct StageOff { int64_t off[2]; };
+// The staging split in two: the key-list offsets of the wave's 4-row windows (LDS reads
+// of the split's key table, issued one iteration ahead) and the loads themselves, one
+// dma16 per window, so a staged block costs kStageWindows vector-memory operations per
+// wave (the explicit waits count them).
+constexpr int kStageWindows = 2;
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory operations
+// of the wave are outstanding; the export and LDS/scalar counters are left unconstrained.
+constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+struct StageOff { int64_t off[kStageWindows]; };
 __device__ __forceinline__ StageOff stage_offsets(const KeyMap& km, int x0) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   StageOff so;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) so.off[j] = km.row(x0 + 8 * wave + 4 * j + (lane >> 4));
+  for (int j = 0; j < kStageWindows; ++j) so.off[j] = km.row(x0 + 4 * kStageWindows * wave + 4 * j + (lane >> 4));
   return so;
 }
 template <bool kIsK>
 __device__ __forceinline__ void stage_issue(char* buf, const uint16_t* pool, const StageOff& so) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 8 * wave + 4 * j + (lane >> 4), pos = lane & 15;
-    dma16(pool + so.off[j] + 8 * (kIsK ? k_pos(row, pos) : v_pos(row, pos)), buf + (8 * wave + 4 * j) * Tile<true>::kRow);
+  for (int j = 0; j < kStageWindows; ++j) {
+    const int row0 = 4 * kStageWindows * wave + 4 * j, row = row0 + (lane >> 4), pos = lane & 15;
+    dma16(pool + so.off[j] + 8 * (kIsK ? k_pos(row, pos) : v_pos(row, pos)), buf + row0 * Tile<true>::kRow);
   }
 }
 // Every staged write of this thread has landed in LDS (the barrier that follows makes
@@ -461,7 +467,7 @@ __device__ __forceinline__ void softmax_step(float (&pv)[kN], float mloc, float&
 constexpr int kRows32 = kChunkRowsBf16;
 constexpr int kThreads32 = 512;
 static_assert(kThreads32 / 64 * 32 == kRows32, "32 rows per wave");
-static_assert(kThreads32 / 64 * 8 == Tile<true>::kKeys, "each wave stages 8 rows of a block");
+static_assert(kThreads32 / 64 * 4 * kStageWindows == Tile<true>::kKeys, "each wave stages 4 rows per window of a block");
 __global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void chunk_attn_bf16_kernel(ChunkParams p) {
   TS_TIMELINE_SCOPE(prefill, kTlChunkAttn);
@@ -634,10 +640,10 @@ void chunk_attn_bf16_kernel(ChunkParams p) {
     mloc_n = max_done(full1, m1);
     full_n = full1;
     if (n == kTlBlock) { TS_TIMELINE_MARK_HERE(); }
-    // this iteration's staging (2 windows per staged block) may still be in flight
-    if (sk && sv) __builtin_amdgcn_s_waitcnt(0x0F74);        // vmcnt(4)
-    else if (sk || sv) __builtin_amdgcn_s_waitcnt(0x0F72);   // vmcnt(2)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+    // this iteration's staging may still be in flight
+    if (sk && sv) __builtin_amdgcn_s_waitcnt(vmcnt_at_most(2 * kStageWindows));
+    else if (sk || sv) __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kStageWindows));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
     __syncthreads();
   };
   for (int n = 0; n < nb; n += 2) {
